@@ -1,0 +1,175 @@
+/*
+ * pins.c -- exhaustive checks of the CPU oracle's number-format primitives
+ * against independent brute-force definitions evaluated exactly in double.
+ *
+ * Nothing here includes or links the oracle: the test passes the oracle's
+ * primitive in as a function pointer, and this file decides what the right
+ * answer is from first principles (nearest representable value, ties to the
+ * even code / even mantissa).  Each function walks a range of binary32 bit
+ * patterns and returns the number of disagreements, storing the first
+ * offending pattern.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+typedef int (*e2m1_code_fn)(float);
+typedef uint8_t (*e4m3_encode_fn)(float);
+typedef uint16_t (*bf16_fn)(float);
+typedef int (*e8m0_fn)(float);
+
+static float from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* E2M1 magnitudes, listed as sign-less 1.m x 2^e values of a 2-bit-exponent,
+ * 1-bit-mantissa float with bias 1 (code 1 is the subnormal 0.5). */
+static double e2m1_grid(int q) {
+  int ex = q >> 1, man = q & 1;
+  return ex == 0 ? man * 0.5 : ldexp(1.0 + 0.5 * man, ex - 1);
+}
+
+/* Nearest grid value to a (exact in double), ties to the even code;
+ * values past the top saturate. */
+static int e2m1_nearest(const double* grid, double a) {
+  int best = 0;
+  double bestd = fabs(a - grid[0]);
+  for (int q = 1; q < 8; ++q) {
+    double d = fabs(a - grid[q]);
+    if (d < bestd || (d == bestd && (q % 2 == 0) && (best % 2 != 0))) {
+      best = q;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+/* The range is split into chunks walked by OpenMP threads; the count of
+ * disagreements and the lowest offending pattern do not depend on it. */
+#define CHUNK (1u << 20)
+
+int64_t pin_e2m1(e2m1_code_fn f, uint32_t lo, uint32_t hi, uint32_t* first) {
+  double grid[8];
+  for (int q = 0; q < 8; ++q) grid[q] = e2m1_grid(q);
+  int64_t bad = 0;
+  uint32_t first_bad = 0xFFFFFFFFu;
+  int64_t nchunks = ((int64_t)hi - lo) / CHUNK + 1;
+#pragma omp parallel for schedule(dynamic) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t c = 0; c < nchunks; ++c) {
+    uint64_t a0 = (uint64_t)lo + (uint64_t)c * CHUNK;
+    uint64_t a1 = a0 + CHUNK - 1 > hi ? hi : a0 + CHUNK - 1;
+    for (uint64_t u = a0; u <= a1; ++u) {
+      float a = from_bits((uint32_t)u);
+      if (f(a) != e2m1_nearest(grid, (double)a)) {
+        if ((uint32_t)u < first_bad) first_bad = (uint32_t)u;
+        ++bad;
+      }
+    }
+  }
+  if (bad) *first = first_bad;
+  return bad;
+}
+
+/* All 127 non-negative finite E4M3FN values in increasing order, built from
+ * the format's fields as 2^(E-7) * (1 + m/8) (normal) or 2^-6 * m/8
+ * (subnormal); byte pattern == index. */
+static double e4m3_table[127];
+static void build_e4m3_table(void) {
+  for (int byte = 0; byte < 127; ++byte) {
+    int E = byte >> 3, m = byte & 7;
+    e4m3_table[byte] = E == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, E - 7);
+  }
+}
+
+/* Walk the patterns in increasing order with a moving bracket
+ * table[j] <= a < table[j+1]; nearest with ties to the even byte,
+ * saturation above 448. */
+int64_t pin_e4m3(e4m3_encode_fn f, uint32_t lo, uint32_t hi, uint32_t* first) {
+  build_e4m3_table();
+  int64_t bad = 0;
+  uint32_t first_bad = 0xFFFFFFFFu;
+  int64_t nchunks = ((int64_t)hi - lo) / CHUNK + 1;
+#pragma omp parallel for schedule(dynamic) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t c = 0; c < nchunks; ++c) {
+    uint64_t a0 = (uint64_t)lo + (uint64_t)c * CHUNK;
+    uint64_t a1 = a0 + CHUNK - 1 > hi ? hi : a0 + CHUNK - 1;
+    int j = 0;
+    for (uint64_t u = a0; u <= a1; ++u) {
+      double a = (double)from_bits((uint32_t)u);
+      while (j < 126 && e4m3_table[j + 1] <= a) ++j;
+      int want;
+      if (j == 126) {
+        want = 126; /* at or past 448 */
+      } else {
+        double dl = a - e4m3_table[j], dh = e4m3_table[j + 1] - a;
+        if (dl < dh) want = j;
+        else if (dh < dl) want = j + 1;
+        else want = (j % 2 == 0) ? j : j + 1;
+      }
+      if (f((float)a) != want) {
+        if ((uint32_t)u < first_bad) first_bad = (uint32_t)u;
+        ++bad;
+      }
+    }
+  }
+  if (bad) *first = first_bad;
+  return bad;
+}
+
+/* Nearest BF16 to a finite float: the two BF16 neighbours are the pattern
+ * truncated to its top 16 bits and the next one up in magnitude; compare
+ * distances exactly in double, ties to the even pattern.  Overflow past
+ * the largest finite BF16 is decided the same way against 2^128 (the
+ * infinity pattern 0x7F80 is the "next" value). */
+int64_t pin_bf16(bf16_fn f, uint32_t lo, uint32_t hi, uint32_t* first) {
+  int64_t bad = 0;
+  uint32_t first_bad = 0xFFFFFFFFu;
+  int64_t nchunks = ((int64_t)hi - lo) / CHUNK + 1;
+#pragma omp parallel for schedule(dynamic) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t c = 0; c < nchunks; ++c) {
+    uint64_t a0 = (uint64_t)lo + (uint64_t)c * CHUNK;
+    uint64_t a1 = a0 + CHUNK - 1 > hi ? hi : a0 + CHUNK - 1;
+    for (uint64_t u = a0; u <= a1; ++u) {
+      uint32_t bits = (uint32_t)u;
+      if ((bits & 0x7F800000u) == 0x7F800000u) continue; /* Inf/NaN */
+      float x = from_bits(bits);
+      uint32_t t = bits & 0xFFFF0000u;
+      double lo_v = (double)from_bits(t);
+      uint32_t up = t + 0x10000u;
+      double hi_v = ((up & 0x7F800000u) == 0x7F800000u)
+                        ? copysign(ldexp(1.0, 128), lo_v)
+                        : (double)from_bits(up);
+      double dl = fabs((double)x - lo_v), dh = fabs(hi_v - (double)x);
+      uint16_t want;
+      if (dl < dh) want = (uint16_t)(t >> 16);
+      else if (dh < dl) want = (uint16_t)(up >> 16);
+      else want = ((t >> 16) & 1u) ? (uint16_t)(up >> 16) : (uint16_t)(t >> 16);
+      if (f(x) != want) {
+        if (bits < first_bad) first_bad = bits;
+        ++bad;
+      }
+    }
+  }
+  if (bad) *first = first_bad;
+  return bad;
+}
+
+/* E8M0 exponent k of a block max b > 0: k = floor(log2 b) - 2, so that
+ * 4 * 2^k <= b < 8 * 2^k when unclamped; checked as that inequality. */
+int64_t pin_e8m0(e8m0_fn f, uint32_t lo, uint32_t hi, uint32_t step,
+                 uint32_t* first) {
+  int64_t bad = 0;
+  for (uint64_t u = lo; u <= hi; u += step) {
+    float b = from_bits((uint32_t)u);
+    if (!(b > 0.0f) || isinf(b)) continue;
+    int k = f(b);
+    int ok;
+    double lo_b = ldexp(4.0, k), hi_b = ldexp(8.0, k);
+    if (k == -127) ok = (double)b < ldexp(8.0, -127);
+    else if (k == 127) ok = (double)b >= ldexp(4.0, 127);
+    else ok = lo_b <= (double)b && (double)b < hi_b;
+    if (!ok) {
+      if (!bad) *first = (uint32_t)u;
+      ++bad;
+    }
+  }
+  return bad;
+}
