@@ -1,0 +1,276 @@
+"""Throughput of the fused FP4 quantizer on one MI355X.
+
+Headline step: one nvfp4_quantize call (per-token NVFP4 with Four-Over-Six
+and the BF16 dequantized output) over the 8192 x 7168 BF16 MoE-activation
+workload (Student-t(3) values with a log-normal per-token gain), inputs
+resident in HBM.  value = algorithmic bytes per call / mean call time, in GB
+(10^9 B) per second.  Buffers rotate over several input/output sets (more
+than the 256 MB last-level cache) so repeated calls cannot be served from
+cache.  Calls are timed with HIP events on the stream the library launches
+on (torch's current stream).
+
+Also reported on the same JSON line: the roofline of the dominant kernel,
+a CPU baseline (the CPU oracle timed on this host), the other calls of the
+path (standalone dequant, expert-weight quantize, ragged routed quantize,
+MXFP4 Rollout-ResQ) and a device-copy ceiling.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp4_block_quantization_amd as fq  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "quantize+dequant GB/s and % of HBM peak, 8192×7168 BF16 per-token 4/6"
+
+
+def nvfp4_bytes(rows, hidden, dequant=True, groups=0):
+    """Algorithmic HBM bytes of one nvfp4_quantize call: read the BF16
+    input, write codes (1/2 B per element), E4M3 block scales (1/16 B per
+    element), FP32 token scales, and optionally the BF16 dequant."""
+    b = rows * hidden * 2 + rows * hidden // 2 + rows * hidden // 16 + rows * 4
+    if dequant:
+        b += rows * hidden * 2
+    if groups:
+        b += (groups + 1) * 8
+    return b
+
+
+def dequant_bytes(rows, hidden):
+    return rows * hidden // 2 + rows * hidden // 16 + rows * 4 + rows * hidden * 2
+
+
+def mx_bytes(rows, hidden):
+    """Read BF16; write primary codes (1/2 B/el) + E8M0 (1/32), residual kept
+    codes (1/4), 2:4 metadata (1/8) and residual E8M0 (1/32)."""
+    n = rows * hidden
+    return n * 2 + n // 2 + n // 32 + n // 4 + n // 8 + n // 32
+
+
+def time_calls(fn, sets, steps, warmup):
+    """Run fn(set) round-robin; return per-call durations (ms) from HIP
+    events recorded on the current stream around each call."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    wall0 = torch.cuda.Event(enable_timing=True)
+    wall1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(sets[i % len(sets)])
+        ends[i].record(stream)
+    wall1.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return per, wall0.elapsed_time(wall1)
+
+
+def rotating_nvfp4_sets(x, n, dequant=True):
+    rows, hidden = x.shape
+    sets = []
+    for i in range(n):
+        xi = x if i == 0 else x.clone()
+        out = (torch.empty((rows, hidden // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((rows, hidden // 16), dtype=torch.uint8, device=x.device),
+               torch.empty((rows,), dtype=torch.float32, device=x.device),
+               torch.empty_like(x) if dequant else None)
+        sets.append((xi, out))
+    return sets
+
+
+def cpu_baseline(x_bits, rows_sample, repeats=3):
+    """The CPU oracle as it stands (single-threaded C), over a bounded
+    sample of the headline workload's rows; median of `repeats`."""
+    import oracle
+    xs = np.ascontiguousarray(x_bits[:rows_sample])
+    oracle.nvfp4_quantize(xs[:8], True)  # load the library, warm caches
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.nvfp4_quantize(xs, True, dequant=True)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    hidden = xs.shape[1]
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": nvfp4_bytes(rows_sample, hidden) / t / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d of 8192 rows x %d, per-token NVFP4 4/6 + BF16 dequant, median of %d "
+                      "runs of %.2f s" % (rows_sample, hidden, repeats, t),
+            "elements_per_s": rows_sample * hidden / t, "cpu_model": cpu,
+            "host_threads_available": os.cpu_count()}
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_block_quantization_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel_key):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    valid only while the kernel sources are unchanged since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the quantizer is row-local and needs no "
+              "communication, so a multi-GPU figure is not produced (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    x_bits = workloads.rows("moe_act")
+    rows, hidden = x_bits.shape
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    print("[bench] generated moe_act %dx%d in %.1f s" % (rows, hidden, time.time() - t0),
+          file=sys.stderr, flush=True)
+
+    sets = rotating_nvfp4_sets(x, args.sets)
+    per, wall = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), sets, args.steps,
+                           args.warmup)
+    ms = float(per.mean())
+    nbytes = nvfp4_bytes(rows, hidden)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print("[bench] nvfp4_quantize moe_act: mean %.2f us (p10 %.2f p50 %.2f p90 %.2f), %.0f GB/s"
+          % (ms * 1e3, np.percentile(per, 10) * 1e3, np.median(per) * 1e3,
+             np.percentile(per, 90) * 1e3, gbs), file=sys.stderr, flush=True)
+
+    key = "nvfp4_quantize_rows<7,fos,dq> moe_act 8192x7168"
+    traffic = traffic_record(key)
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": nbytes,
+                "kernel": key, "launch_us_mean": round(ms * 1e3, 3),
+                "launch_us_p50": round(float(np.median(per)) * 1e3, 3)}
+    del sets
+    torch.cuda.empty_cache()
+
+    secondary = {}
+    if not args.no_secondary:
+        # device copy ceiling (a plain copy kernel of 2 x 256 MiB traffic)
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        dsts = [torch.empty_like(src) for _ in range(3)]
+        p, _ = time_calls(lambda d: d.copy_(src), dsts, 100, 10)
+        secondary["device_copy_GBps"] = round(2 * src.numel() / (p.mean() * 1e-3) / 1e9, 1)
+        del src, dsts
+
+        # standalone dequant on the headline shape
+        c, s_, ts, _ = fq.nvfp4_quantize(x, True, dequant=False)
+        dsets = [(c.clone(), s_.clone(), ts.clone(), torch.empty_like(x)) for _ in range(4)]
+        p, _ = time_calls(lambda d: fq.nvfp4_dequantize(d[0], d[1], d[2], out=d[3]), dsets, 200, 20)
+        b = dequant_bytes(rows, hidden)
+        secondary["nvfp4_dequantize moe_act 8192x7168"] = {
+            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+        del dsets, c, s_, ts
+        torch.cuda.empty_cache()
+
+        # MXFP4 Rollout-ResQ
+        xr = workloads.tensor("resq_act", dev)
+        msets = [xr] + [xr.clone() for _ in range(3)]
+        mouts = [fq.mxfp4_resq_quantize(m) for m in msets]
+        p, _ = time_calls(lambda i: fq.mxfp4_resq_quantize(msets[i], out=mouts[i]),
+                          list(range(4)), 200, 20)
+        b = mx_bytes(*xr.shape)
+        secondary["mxfp4_resq_quantize resq_act 8192x7168"] = {
+            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+        del msets, mouts, xr
+        torch.cuda.empty_cache()
+
+        # ragged routed, quantize only
+        xg = workloads.tensor("ragged_routed", dev)
+        offs = torch.from_numpy(workloads.group_offsets()).to(dev)
+        gsets = rotating_nvfp4_sets(xg, 2, dequant=False)
+        p, _ = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, offsets=offs, out=s[1]),
+                          gsets, 200, 20)
+        b = nvfp4_bytes(*xg.shape, dequant=False, groups=offs.numel() - 1)
+        secondary["nvfp4_quantize ragged_routed 65536x2048 (64 groups, no dequant)"] = {
+            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+        del gsets, xg
+        torch.cuda.empty_cache()
+
+        # expert weights, 32 x 2048 x 7168
+        xw = workloads.tensor("expert_weights", dev)
+        wsets = rotating_nvfp4_sets(xw, 1)
+        p, _ = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), wsets, 50, 5)
+        b = nvfp4_bytes(*xw.shape)
+        secondary["nvfp4_quantize expert_weights 65536x7168"] = {
+            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+        del wsets, xw
+        torch.cuda.empty_cache()
+        print("[bench] secondary: %s" % json.dumps(secondary), file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(x_bits, min(args.cpu_rows, rows))
+        print("[bench] cpu oracle: %.3f GB/s (%s)" % (cpu["value"], cpu["sample"]),
+              file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "moe_act: 8192x7168 BF16 MoE expert input activations, "
+                               "Student-t(3) x per-token LogNormal(0,0.5); per-token NVFP4 "
+                               "Four-Over-Six + BF16 dequant", "rows": rows, "hidden": hidden,
+                   "four_over_six": True, "dequant": True, "rotating_sets": args.sets},
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "elements_per_s": rows * hidden / (ms * 1e-3),
+        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

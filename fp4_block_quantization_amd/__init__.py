@@ -1,0 +1,151 @@
+"""MI355X (gfx950) fused FP4 block quantizer -- Python binding.
+
+Argument marshalling only: every step of the quantizer runs in the HIP
+kernels of libfp4q.so (C ABI in include/fp4q.h).  PyTorch supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+not built, or a tensor is not on a GPU, the call raises.
+
+Calls (same names as the C ABI):
+  nvfp4_quantize(x, four_over_six=True, offsets=None, dequant=True)
+      -> codes u8 [R, H/2], block_scales u8 [R, H/16] (E4M3FN bits),
+         token_scales f32 [R], dequant bf16 [R, H] or None
+  nvfp4_dequantize(codes, block_scales, token_scales) -> bf16 [R, H]
+  mxfp4_resq_quantize(x)
+      -> codes u8 [R, H/2], scales u8 [R, H/32], res_codes u8 [R, H/4],
+         res_meta u8 [R, H/8], res_scales u8 [R, H/32]
+"""
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+__all__ = ["lib", "nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
+           "Fp4qError", "LIB_PATH"]
+
+LIB_PATH = _build.LIB_PATH
+_lib = None
+
+
+class Fp4qError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded libfp4q.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Fp4qError(
+                "libfp4q.so is not built (%s); run __graft_entry__.build() or "
+                "python fp4_block_quantization_amd/_build.py" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.nvfp4_quantize.argtypes = [vp, i64, i64, vp, i64, ci, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize.restype = ci
+        L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+        L.nvfp4_dequantize.restype = ci
+        L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mxfp4_resq_quantize.restype = ci
+        L.fp4q_status_string.argtypes = [ci]
+        L.fp4q_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = lib().fp4q_status_string(status).decode()
+        raise Fp4qError("%s failed: %s (status %d)" % (what, msg, status))
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, name, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise Fp4qError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise Fp4qError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise Fp4qError("%s must be contiguous" % name)
+    return t
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def nvfp4_quantize(x, four_over_six=True, offsets=None, dequant=True, out=None):
+    """Per-token NVFP4 with Four-Over-Six of a BF16 [rows, hidden] tensor.
+
+    offsets: optional int64 GPU tensor [groups + 1] (ragged routed rows);
+    only rows [offsets[0], offsets[-1]) are written.  out: optional tuple
+    (codes, block_scales, token_scales, dequant-or-None) to write into."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise Fp4qError("x must be 2-D [rows, hidden]")
+    rows, hidden = x.shape
+    if out is None:
+        codes = torch.empty((rows, hidden // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, hidden // 16), dtype=torch.uint8, device=x.device)
+        ts = torch.empty((rows,), dtype=torch.float32, device=x.device)
+        dq = torch.empty_like(x) if dequant else None
+    else:
+        codes, scales, ts, dq = out
+        _dev(codes, "codes", torch.uint8)
+        _dev(scales, "block_scales", torch.uint8)
+        _dev(ts, "token_scales", torch.float32)
+        if dq is not None:
+            _dev(dq, "dequant", torch.bfloat16)
+        if (codes.numel() != rows * (hidden // 2) or scales.numel() != rows * (hidden // 16)
+                or ts.numel() != rows or (dq is not None and dq.numel() != rows * hidden)):
+            raise Fp4qError("output tensor sizes do not match x")
+    ng = 0
+    if offsets is not None:
+        _dev(offsets, "offsets", torch.int64)
+        ng = offsets.numel() - 1
+        if ng < 1:
+            raise Fp4qError("offsets needs at least two entries")
+    st = lib().nvfp4_quantize(_p(x), rows, hidden, _p(offsets), ng, int(bool(four_over_six)),
+                              _p(codes), _p(scales), _p(ts), _p(dq), _stream(x))
+    _check(st, "nvfp4_quantize")
+    return codes, scales, ts, dq
+
+
+def nvfp4_dequantize(codes, block_scales, token_scales, out=None):
+    _dev(codes, "codes", torch.uint8)
+    _dev(block_scales, "block_scales", torch.uint8)
+    _dev(token_scales, "token_scales", torch.float32)
+    rows = codes.shape[0]
+    hidden = codes.numel() // max(rows, 1) * 2
+    if out is None:
+        out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=codes.device)
+    _dev(out, "out", torch.bfloat16)
+    if (block_scales.numel() != rows * (hidden // 16) or token_scales.numel() != rows
+            or out.numel() != rows * hidden):
+        raise Fp4qError("tensor sizes do not match codes")
+    st = lib().nvfp4_dequantize(_p(codes), _p(block_scales), _p(token_scales), rows, hidden,
+                                _p(out), _stream(codes))
+    _check(st, "nvfp4_dequantize")
+    return out
+
+
+def mxfp4_resq_quantize(x, out=None):
+    """MXFP4 + Rollout-ResQ residual with 2:4 sparsity of a BF16 [rows, hidden]."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise Fp4qError("x must be 2-D [rows, hidden]")
+    rows, hidden = x.shape
+    if out is None:
+        kw = dict(dtype=torch.uint8, device=x.device)
+        out = (torch.empty((rows, hidden // 2), **kw), torch.empty((rows, hidden // 32), **kw),
+               torch.empty((rows, hidden // 4), **kw), torch.empty((rows, hidden // 8), **kw),
+               torch.empty((rows, hidden // 32), **kw))
+    for t, n in zip(out, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
+        _dev(t, n, torch.uint8)
+    st = lib().mxfp4_resq_quantize(_p(x), rows, hidden, *[_p(t) for t in out], _stream(x))
+    _check(st, "mxfp4_resq_quantize")
+    return out

@@ -1,0 +1,91 @@
+// fp4q_api.cpp -- the C ABI declared in include/fp4q.h: host-side argument
+// validation, then one kernel launch per call on the caller's stream.
+// Validation touches no HIP API, so a rejected call returns its status
+// even on a machine without a GPU.
+#include "fp4q.h"
+
+#include <hip/hip_runtime.h>
+
+#include "fp4q_launch.h"
+
+namespace {
+
+// Largest sizes the kernels index: row counts that keep the grid within
+// 2^31 workgroups, and row lengths whose block count fits an int.
+constexpr int64_t kMaxRows = (int64_t)1 << 32;
+constexpr int64_t kMaxHidden = (int64_t)1 << 30;
+constexpr int64_t kMaxElements = (int64_t)1 << 40;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+fp4q_status check_shape(int64_t rows, int64_t hidden, int64_t block) {
+  if (rows < 0 || hidden <= 0 || hidden % block != 0) return FP4Q_ERROR_INVALID_SHAPE;
+  if (rows > kMaxRows || hidden > kMaxHidden || rows * hidden > kMaxElements)
+    return FP4Q_ERROR_INVALID_SHAPE;
+  return FP4Q_SUCCESS;
+}
+
+fp4q_status launched(hipError_t e) { return e == hipSuccess ? FP4Q_SUCCESS : FP4Q_ERROR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+fp4q_status nvfp4_quantize(const void* x, int64_t rows, int64_t hidden,
+                           const int64_t* group_offsets, int64_t num_groups, int four_over_six,
+                           uint8_t* codes, uint8_t* block_scales, float* token_scales,
+                           void* dequant, void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 16);
+  if (st != FP4Q_SUCCESS) return st;
+  if (num_groups < 0 || (num_groups == 0 && group_offsets != nullptr))
+    return FP4Q_ERROR_INVALID_SHAPE;
+  if (num_groups > 0 && group_offsets == nullptr) return FP4Q_ERROR_NULL_POINTER;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!x || !codes || !block_scales || !token_scales) return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(token_scales, 4) ||
+      (dequant && !aligned(dequant, 16)) || (group_offsets && !aligned(group_offsets, 8)))
+    return FP4Q_ERROR_MISALIGNED;
+  fp4q::NvQuantArgs a{x,     rows,         hidden,       group_offsets, num_groups,
+                      four_over_six ? 1 : 0, codes, block_scales, token_scales, dequant};
+  return launched(fp4q::nvfp4_quantize_launch(a, (hipStream_t)stream));
+}
+
+fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales,
+                             const float* token_scales, int64_t rows, int64_t hidden, void* out,
+                             void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 16);
+  if (st != FP4Q_SUCCESS) return st;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!codes || !block_scales || !token_scales || !out) return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(codes, 8) || !aligned(token_scales, 4) || !aligned(out, 16))
+    return FP4Q_ERROR_MISALIGNED;
+  return launched(fp4q::nvfp4_dequantize_launch(codes, block_scales, token_scales, rows, hidden,
+                                                out, (hipStream_t)stream));
+}
+
+fp4q_status mxfp4_resq_quantize(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
+                                uint8_t* scales, uint8_t* res_codes, uint8_t* res_meta,
+                                uint8_t* res_scales, void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 32);
+  if (st != FP4Q_SUCCESS) return st;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!x || !codes || !scales || !res_codes || !res_meta || !res_scales)
+    return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(res_codes, 8) || !aligned(res_meta, 4))
+    return FP4Q_ERROR_MISALIGNED;
+  return launched(fp4q::mxfp4_resq_launch(x, rows, hidden, codes, scales, res_codes, res_meta,
+                                          res_scales, (hipStream_t)stream));
+}
+
+const char* fp4q_status_string(fp4q_status status) {
+  switch (status) {
+    case FP4Q_SUCCESS: return "success";
+    case FP4Q_ERROR_NULL_POINTER: return "a required pointer is NULL";
+    case FP4Q_ERROR_INVALID_SHAPE: return "invalid shape or group count";
+    case FP4Q_ERROR_MISALIGNED: return "a pointer lacks its required alignment";
+    case FP4Q_ERROR_LAUNCH: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// fp4q_device.h -- device-side number-format helpers for gfx950.
+//
+// Formats: E2M1 (TRACE page, Jargon: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6),
+// OCP E4M3FN block scales (NVFP4-RL blog, section 2: "FP8 E4M3"), E8M0 MX
+// scales and BF16 (HiFloat4 page, Rollout-ResQ section; NVFP4-RL blog,
+// section 3).  All rounding is to nearest with ties to even.  Built with
+// -ffp-contract=off, FP32 denormals preserved and correctly rounded FP32
+// division, so every float operation below is one IEEE binary32 operation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// FP32 -> BF16 bit pattern, round to nearest even.  Only finite values
+// reach it (candidates are products of finite scales).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+// E2M1 magnitude code of a >= 0 and its value: the grid below 1 has step
+// 0.5; from 1 up each binade holds two values (one fraction bit), so
+// rounding the binary32 significand to one fraction bit by an integer add
+// (ties to even; the carry steps the exponent) lands on the grid.  Codes
+// past 6 saturate.  a = NaN (only 0 * inf, from an infinite reciprocal of a
+// tiny decode step) gives code 0, like a zero input.
+__device__ __forceinline__ uint32_t e2m1_code_sw(float a, float& g) {
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t ur = u + 0x1FFFFFu + ((u >> 22) & 1u);
+  uint32_t code = min(ur >> 22, 259u) - 252u;  // 1.0 -> 2, 1.5 -> 3, ..., 6.0 -> 7
+  float val = (code == 7u) ? 6.0f : __uint_as_float(ur & 0xFFC00000u);
+  if (a < 1.0f) {  // 0.25 -> 0 and 0.75 -> 1.0 (the even codes)
+    code = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u);
+    val = 0.5f * (float)code;
+  }
+  if (u > 0x7F800000u) {  // NaN
+    code = 0u;
+    val = 0.0f;
+  }
+  g = val;
+  return code;
+}
+
+// OCP E4M3FN byte of t >= 0 (or NaN, treated as 0) and its exact value.
+// Bias 7, 3 fraction bits, smallest normal 2^-6 with step 2^-9 below it,
+// largest finite 448 (0x7E); larger values saturate.
+__device__ __forceinline__ uint32_t e4m3_encode(float t, float& val) {
+  if (!(t > 0.0f)) {
+    val = 0.0f;
+    return 0u;
+  }
+  if (t > 448.0f) {
+    val = 448.0f;
+    return 0x7Eu;
+  }
+  if (t < 0.015625f) {  // multiples of 2^-9; 8 * 2^-9 is the first normal (byte 0x08)
+    const float m = __builtin_rintf(t * 512.0f);
+    val = m * (1.0f / 512.0f);
+    return (uint32_t)m;
+  }
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t ur = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
+  val = __uint_as_float(ur);
+  return (ur >> 20) - 960u;  // ((binary32 exponent - 127 + 7) << 3) | fraction
+}
+
+// Value of an E4M3FN byte (sign honoured).
+__device__ __forceinline__ float e4m3_decode(uint32_t byte) {
+  const uint32_t mag = byte & 0x7Fu;
+  float v = (mag < 8u) ? (float)mag * (1.0f / 512.0f) : __uint_as_float((mag + 960u) << 20);
+  if (mag == 0x7Fu) v = __builtin_nanf("");
+  return (byte & 0x80u) ? -v : v;
+}
+
+// Value of E2M1 magnitude code q (0..7).
+__device__ __forceinline__ float e2m1_value(uint32_t q) {
+  return (q < 2u) ? 0.5f * (float)q
+                  : __uint_as_float((((q >> 1) + 126u) << 23) | ((q & 1u) << 22));
+}
+
+// MX shared exponent of a block whose max magnitude has binary32 pattern
+// bits (non-negative): floor(log2 b) - 2, clamped to [-127, 127]; zero and
+// tiny maxima give -127.  For b >= 2^-126, floor(log2 b) is the unbiased
+// exponent field; anything smaller clamps anyway.
+__device__ __forceinline__ int mx_exponent(uint32_t bits) {
+  return max((int)(bits >> 23) - 129, -127);
+}
+
+}  // namespace fp4q

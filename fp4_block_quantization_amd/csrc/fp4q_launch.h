@@ -1,0 +1,31 @@
+// fp4q_launch.h -- internal launchers behind the C ABI (include/fp4q.h).
+// Arguments reaching these have already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+struct NvQuantArgs {
+  const void* x;
+  int64_t rows;
+  int64_t hidden;
+  const int64_t* offsets;
+  int64_t num_groups;
+  int four_over_six;
+  uint8_t* codes;
+  uint8_t* block_scales;
+  float* token_scales;
+  void* dequant;
+};
+
+hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t stream);
+hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,
+                                   const float* token_scales, int64_t rows, int64_t hidden,
+                                   void* out, hipStream_t stream);
+hipError_t mxfp4_resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
+                             uint8_t* scales, uint8_t* res_codes, uint8_t* res_meta,
+                             uint8_t* res_scales, hipStream_t stream);
+
+}  // namespace fp4q

@@ -1,0 +1,153 @@
+/*
+ * fp4q.h -- C ABI of the MI355X (gfx950) fused FP4 block quantizer.
+ *
+ * Three operations, each one or more hand-written HIP kernels:
+ *
+ *   nvfp4_quantize      per-token NVFP4 with Four-Over-Six and the exact
+ *                       BF16 dequantized tensor
+ *   nvfp4_dequantize    BF16 dequantization of stored NVFP4 values
+ *   mxfp4_resq_quantize MXFP4 with a re-quantized, 2:4-sparsified residual
+ *                       (Rollout-ResQ)
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer on the current HIP device.  The
+ *     caller allocates and frees all memory; the library allocates nothing
+ *     and keeps no state between calls.
+ *   - Tensors are row-major and contiguous: [rows, hidden], hidden innermost.
+ *     BF16 is passed as 16-bit patterns (void*).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  Arguments are validated on the host before anything is
+ *     launched; a rejected call returns its status and writes nothing.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Outputs must not alias inputs or each other.
+ *   - Inputs must be finite.  NaN or infinity is outside the domain: the
+ *     kernels stay memory-safe but the output values are unspecified.
+ *   - Results depend only on the input values: they are bit-identical for
+ *     any stream, batch composition, row order or launch, and bit-identical
+ *     to the CPU reference.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4Q_SUCCESS = 0,
+  FP4Q_ERROR_NULL_POINTER = 1,  /* a required pointer is NULL                */
+  FP4Q_ERROR_INVALID_SHAPE = 2, /* rows < 0, hidden <= 0, hidden not a
+                                   multiple of the block size, num_groups < 0,
+                                   or a size too large to index              */
+  FP4Q_ERROR_MISALIGNED = 3,    /* a pointer lacks the alignment stated at
+                                   its argument                              */
+  FP4Q_ERROR_LAUNCH = 4         /* the HIP launch failed (no device, bad
+                                   stream, ...)                             */
+} fp4q_status;
+
+/*
+ * nvfp4_quantize -- per-token NVFP4 with Four-Over-Six.
+ *
+ * Definition: "humans& Open-Sources the First Stable 4-Bit RL Training
+ * Recipe at 1.73x Speedup" (alphasignal.ai), sections 1-3, and "NVFP4-RL"
+ * (jianyuh.github.io), section 2 (each token's FP32 scale over the hidden
+ * dimension, computed together with the FP8 E4M3 block scales in one
+ * kernel), section 3 (the dequantized value of the exact quantized tensor
+ * feeds the BF16 backward) and section 4 (Four-Over-Six candidate formula).
+ * Per row r with amax = max |x|:
+ *   s = amax / 1536 (four_over_six) or amax / 2688 (6 only), FP32;
+ *   per 16-element block with max b, per candidate k in {6, 4}:
+ *     e_k = E4M3_RNE(b / (k*s)), d_k = e_k*s, r_k = 1/d_k,
+ *     q_i = E2M1_RNE(|x_i| * r_k), c_i = +-((g(q_i) * e_k) * s),
+ *     err_k = sum_i (x_i - c_i)^2 in element order;
+ *   candidate 4 wins only if err_4 < err_6 (ties keep 6).
+ * Every step is one IEEE binary32 operation (no FMA contraction, division
+ * correctly rounded, subnormals kept).
+ *
+ *   x             BF16 [rows, hidden], 16-byte aligned.
+ *   rows          >= 0 (0: nothing is launched).
+ *   hidden        > 0, a multiple of 16.
+ *   group_offsets NULL, or int64 [num_groups + 1] on the device, 8-byte
+ *                 aligned, with 0 <= off[0] <= ... <= off[num_groups] <=
+ *                 rows (routed tokens grouped per expert).  Only rows
+ *                 [off[0], off[num_groups]) are read and written; the
+ *                 others keep their contents.  The offsets are not checked
+ *                 on the host (that would need a synchronisation); the
+ *                 kernel clamps the range to [0, rows), so wrong offsets
+ *                 cannot cause an out-of-bounds access.
+ *   num_groups    0 when group_offsets is NULL, else >= 1.
+ *   four_over_six 1: s = amax/1536 and the 4/6 choice per block;
+ *                 0: s = amax/2688 and the 6 candidate only.
+ *   codes         uint8 [rows, hidden/2], 8-byte aligned: E2M1 nibbles,
+ *                 sign in bit 3, element 2i in the low nibble of byte i.
+ *   block_scales  uint8 [rows, hidden/16]: OCP E4M3FN bit patterns.
+ *   token_scales  float [rows], 4-byte aligned: s.
+ *   dequant       BF16 [rows, hidden], 16-byte aligned, or NULL to skip:
+ *                 BF16_RNE(c_i) of the chosen candidate.
+ *   stream        hipStream_t or NULL.
+ */
+fp4q_status nvfp4_quantize(const void* x, int64_t rows, int64_t hidden,
+                           const int64_t* group_offsets, int64_t num_groups,
+                           int four_over_six, uint8_t* codes,
+                           uint8_t* block_scales, float* token_scales,
+                           void* dequant, void* stream);
+
+/*
+ * nvfp4_dequantize -- BF16 values of stored NVFP4 data.
+ *
+ * Definition: "NVFP4-RL" (jianyuh.github.io), section 3 (dequantized
+ * backward, y = x . DQ(Q(w))) and section 4 (candidate formula):
+ *   out_i = BF16_RNE(+-((g(code_i & 7) * e_block) * s_row)),
+ * the sign from bit 3 of the nibble.  Given the outputs of nvfp4_quantize
+ * it reproduces that call's dequant tensor bit for bit.
+ *
+ *   codes         uint8 [rows, hidden/2], 8-byte aligned.
+ *   block_scales  uint8 [rows, hidden/16].
+ *   token_scales  float [rows], 4-byte aligned.
+ *   rows          >= 0; hidden > 0, a multiple of 16.
+ *   out           BF16 [rows, hidden], 16-byte aligned.
+ */
+fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales,
+                             const float* token_scales, int64_t rows,
+                             int64_t hidden, void* out, void* stream);
+
+/*
+ * mxfp4_resq_quantize -- MXFP4 with a Rollout-ResQ residual.
+ *
+ * Definition: "HiFloat4 Format for End-To-End Reinforcement Learning
+ * Post-Training of Large Language Models" (agifrontier.github.io), section
+ * on Rollout-ResQ and hardware-aware sparsity: MXFP4 is E2M1 data under one
+ * E8M0 scale per 32 elements; the residual dX = X - Q(X) is quantized
+ * again and S_{2:4} keeps 2 of every 4 consecutive elements of Q(dX).  Per
+ * 32-element block with max b:
+ *   k = clamp(floor(log2 b) - 2, -127, 127) (b == 0: -127), E8M0 byte k+127;
+ *   q_i = E2M1_RNE(|x_i| * 2^-k); DQ_i = +-g(q_i) * 2^k (exact);
+ *   dX_i = x_i - DQ_i (exact in FP32); the residual gets its own k' and
+ *   codes q'_i by the same rule over all 32 residuals;
+ *   per group of 4 consecutive residual codes keep the two largest
+ *   magnitudes (ties to the lower index), indices i0 < i1.
+ *
+ *   x           BF16 [rows, hidden], 16-byte aligned; hidden a multiple of 32.
+ *   codes       uint8 [rows, hidden/2], 16-byte aligned: primary E2M1
+ *               nibbles, element 2i in the low nibble.
+ *   scales      uint8 [rows, hidden/32]: primary E8M0 (2^(byte-127)).
+ *   res_codes   uint8 [rows, hidden/4], 8-byte aligned: per group of 4, the
+ *               kept residual nibble at i0 (low) and at i1 (high).
+ *   res_meta    uint8 [rows, hidden/8], 4-byte aligned: per group the
+ *               nibble i0 | i1 << 2; group 2m in the low nibble of byte m.
+ *   res_scales  uint8 [rows, hidden/32]: residual E8M0.
+ */
+fp4q_status mxfp4_resq_quantize(const void* x, int64_t rows, int64_t hidden,
+                                uint8_t* codes, uint8_t* scales,
+                                uint8_t* res_codes, uint8_t* res_meta,
+                                uint8_t* res_scales, void* stream);
+
+/* Static description of a status (never NULL). */
+const char* fp4q_status_string(fp4q_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4Q_H */

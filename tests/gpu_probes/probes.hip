@@ -1,0 +1,121 @@
+// probes.hip -- exhaustive GPU evaluation of number-format conversions:
+// the gfx950 hardware conversion instructions and the library's own device
+// helpers (fp4q_device.h), over ranges of binary32 bit patterns.  The host
+// compares every result with the CPU oracle's primitives.
+//
+// Every kernel handles element i < n only and writes out[i]; the launcher
+// sizes the grid from n.  Input patterns are generated in-kernel from
+// (lo + index), so no input buffer exists.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4q_device.h"
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+namespace {
+
+__device__ __forceinline__ float pat(uint32_t lo, uint64_t k, uint32_t flip) {
+  return __uint_as_float((uint32_t)(lo + k) ^ flip);
+}
+
+// out[i] = byte holding the FP4 codes of patterns lo+2i (first operand) and
+// lo+2i+1 (second operand), hardware conversion with scale 1.0.
+__global__ void k_hw_fp4(uint32_t lo, uint32_t flip, uint64_t n, uint8_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float a = pat(lo, 2 * i, flip), b = pat(lo, 2 * i + 1, flip);
+  out[i] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+}
+
+// software E2M1 of |pattern| with the sign bit of the pattern, same layout
+__global__ void k_sw_fp4(uint32_t lo, uint32_t flip, uint64_t n, uint8_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t byte = 0;
+  for (int h = 0; h < 2; ++h) {
+    const float v = pat(lo, 2 * i + h, flip);
+    float g;
+    const uint32_t q = fp4q::e2m1_code_sw(fabsf(v), g);
+    byte |= (q | ((__float_as_uint(v) >> 31) << 3)) << (4 * h);
+  }
+  out[i] = (uint8_t)byte;
+}
+
+// out[i] = the two BF16 patterns of lo+2i (low half) and lo+2i+1 (high)
+__global__ void k_hw_bf16(uint32_t lo, uint64_t n, uint32_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float2v v = {pat(lo, 2 * i, 0u), pat(lo, 2 * i + 1, 0u)};
+  out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+__global__ void k_sw_bf16(uint32_t lo, uint64_t n, uint32_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = fp4q::pack_bf16x2(pat(lo, 2 * i, 0u), pat(lo, 2 * i + 1, 0u));
+}
+
+// out[i] = the two E4M3 bytes of lo+2i (low) and lo+2i+1 (high)
+__global__ void k_hw_fp8(uint32_t lo, uint64_t n, uint16_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = (uint16_t)__builtin_amdgcn_cvt_pk_fp8_f32(pat(lo, 2 * i, 0u), pat(lo, 2 * i + 1, 0u),
+                                                     0, false);
+}
+
+__global__ void k_sw_fp8(uint32_t lo, uint64_t n, uint16_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v;
+  const uint32_t a = fp4q::e4m3_encode(pat(lo, 2 * i, 0u), v);
+  const uint32_t b = fp4q::e4m3_encode(pat(lo, 2 * i + 1, 0u), v);
+  out[i] = (uint16_t)(a | (b << 8));
+}
+
+// decode tables: out has 512 floats for FP4 (byte b -> low, high nibble)
+// and 256 floats for FP8
+__global__ void k_decode_tables(float* fp4_hw, float* fp4_sw, float* fp8_hw, float* fp8_sw) {
+  const uint32_t b = threadIdx.x;  // 256 threads
+  const float2v d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b, 1.0f, 0);
+  fp4_hw[2 * b] = d.x;
+  fp4_hw[2 * b + 1] = d.y;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t nib = (b >> (4 * h)) & 15u;
+    const float g = fp4q::e2m1_value(nib & 7u);
+    fp4_sw[2 * b + h] = (nib & 8u) ? -g : g;
+  }
+  fp8_hw[b] = __builtin_amdgcn_cvt_f32_fp8(b, 0);
+  fp8_sw[b] = fp4q::e4m3_decode(b);
+}
+
+dim3 grid_for(uint64_t n) { return dim3((unsigned)((n + 255) / 256)); }
+
+}  // namespace
+
+extern "C" {
+
+// which: 0 hw fp4, 1 sw fp4, 2 hw bf16, 3 sw bf16, 4 hw fp8, 5 sw fp8
+int probe_launch(int which, uint32_t lo, uint32_t flip, uint64_t n, void* out, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (n == 0 || n > (1ull << 31)) return 2;
+  switch (which) {
+    case 0: hipLaunchKernelGGL(k_hw_fp4, grid_for(n), dim3(256), 0, st, lo, flip, n, (uint8_t*)out); break;
+    case 1: hipLaunchKernelGGL(k_sw_fp4, grid_for(n), dim3(256), 0, st, lo, flip, n, (uint8_t*)out); break;
+    case 2: hipLaunchKernelGGL(k_hw_bf16, grid_for(n), dim3(256), 0, st, lo, n, (uint32_t*)out); break;
+    case 3: hipLaunchKernelGGL(k_sw_bf16, grid_for(n), dim3(256), 0, st, lo, n, (uint32_t*)out); break;
+    case 4: hipLaunchKernelGGL(k_hw_fp8, grid_for(n), dim3(256), 0, st, lo, n, (uint16_t*)out); break;
+    case 5: hipLaunchKernelGGL(k_sw_fp8, grid_for(n), dim3(256), 0, st, lo, n, (uint16_t*)out); break;
+    default: return 2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int probe_decode_tables(void* fp4_hw, void* fp4_sw, void* fp8_hw, void* fp8_sw, void* stream) {
+  hipLaunchKernelGGL(k_decode_tables, dim3(1), dim3(256), 0, (hipStream_t)stream,
+                     (float*)fp4_hw, (float*)fp4_sw, (float*)fp8_hw, (float*)fp8_sw);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // extern "C"

@@ -173,3 +173,77 @@ int64_t pin_e8m0(e8m0_fn f, uint32_t lo, uint32_t hi, uint32_t step,
   }
   return bad;
 }
+
+/* ---- comparison of GPU conversion results with the oracle's primitives --
+ * Pairs: result i covers the binary32 patterns (lo + 2i) ^ flip (first /
+ * low part) and (lo + 2i + 1) ^ flip (second / high part).  NaN patterns
+ * are skipped.  Returns the number of mismatching results and the index of
+ * the first one. */
+
+static int is_nan_bits(uint32_t u) { return (u & 0x7FFFFFFFu) > 0x7F800000u; }
+
+int64_t cmp_fp4(e2m1_code_fn f, uint32_t lo, uint32_t flip, uint64_t n,
+                const uint8_t* got, uint64_t* first) {
+  int64_t bad = 0;
+  uint64_t first_bad = UINT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t i = 0; i < (int64_t)n; ++i) {
+    int ok = 1;
+    for (int h = 0; h < 2; ++h) {
+      uint32_t u = (uint32_t)(lo + 2 * (uint64_t)i + h) ^ flip;
+      if (is_nan_bits(u)) continue;
+      float v = from_bits(u);
+      int want = f(fabsf(v)) | ((u >> 31) << 3);
+      int have = (got[i] >> (4 * h)) & 15;
+      if (want != have) ok = 0;
+    }
+    if (!ok) {
+      ++bad;
+      if ((uint64_t)i < first_bad) first_bad = (uint64_t)i;
+    }
+  }
+  *first = first_bad;
+  return bad;
+}
+
+int64_t cmp_bf16(bf16_fn f, uint32_t lo, uint64_t n, const uint32_t* got,
+                 uint64_t* first) {
+  int64_t bad = 0;
+  uint64_t first_bad = UINT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t i = 0; i < (int64_t)n; ++i) {
+    int ok = 1;
+    for (int h = 0; h < 2; ++h) {
+      uint32_t u = (uint32_t)(lo + 2 * (uint64_t)i + h);
+      if (is_nan_bits(u)) continue;
+      if ((uint32_t)f(from_bits(u)) != ((got[i] >> (16 * h)) & 0xFFFFu)) ok = 0;
+    }
+    if (!ok) {
+      ++bad;
+      if ((uint64_t)i < first_bad) first_bad = (uint64_t)i;
+    }
+  }
+  *first = first_bad;
+  return bad;
+}
+
+int64_t cmp_fp8(e4m3_encode_fn f, uint32_t lo, uint64_t n, const uint16_t* got,
+                uint64_t* first) {
+  int64_t bad = 0;
+  uint64_t first_bad = UINT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t i = 0; i < (int64_t)n; ++i) {
+    int ok = 1;
+    for (int h = 0; h < 2; ++h) {
+      uint32_t u = (uint32_t)(lo + 2 * (uint64_t)i + h);
+      if (is_nan_bits(u)) continue;
+      if ((uint32_t)f(from_bits(u)) != ((uint32_t)(got[i] >> (8 * h)) & 0xFFu)) ok = 0;
+    }
+    if (!ok) {
+      ++bad;
+      if ((uint64_t)i < first_bad) first_bad = (uint64_t)i;
+    }
+  }
+  *first = first_bad;
+  return bad;
+}

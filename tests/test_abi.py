@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every call include/*.h declares, and
+rejects bad arguments on the host before any HIP call (so these run
+without a GPU; nothing here launches a kernel)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import fp4_block_quantization_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+SUCCESS, NULL, SHAPE, MISALIGNED, LAUNCH = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                            src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_call():
+    names = declared_functions()
+    assert {"nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
+            "fp4q_status_string"} <= set(names)
+    L = fq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = fq.lib()
+    for s in range(5):
+        assert L.fp4q_status_string(s)
+    assert L.fp4q_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+A16 = P(0x10000)  # aligned fake pointers: never dereferenced by a rejected call
+A8 = P(0x10008)
+ODD = P(0x10001)
+
+
+def nvq(x=A16, rows=4, hidden=64, offs=None, ng=0, fos=1, codes=A16, scales=A16, ts=A16,
+        dq=A16):
+    return fq.lib().nvfp4_quantize(x, rows, hidden, offs, ng, fos, codes, scales, ts, dq, None)
+
+
+def test_nvfp4_quantize_rejects():
+    assert nvq(hidden=24) == SHAPE
+    assert nvq(hidden=0) == SHAPE
+    assert nvq(rows=-1) == SHAPE
+    assert nvq(ng=-1) == SHAPE
+    assert nvq(ng=2) == NULL  # groups without offsets
+    assert nvq(offs=A8, ng=0) == SHAPE  # offsets without groups
+    assert nvq(x=None) == NULL
+    assert nvq(codes=None) == NULL
+    assert nvq(scales=None) == NULL
+    assert nvq(ts=None) == NULL
+    assert nvq(x=A8) == MISALIGNED
+    assert nvq(dq=A8) == MISALIGNED
+    assert nvq(codes=P(0x10004)) == MISALIGNED
+    assert nvq(ts=P(0x10002)) == MISALIGNED
+    assert nvq(offs=P(0x10004), ng=1) == MISALIGNED
+    assert nvq(rows=1 << 33) == SHAPE
+    # empty input: success, nothing launched, pointers may be NULL
+    assert nvq(rows=0, x=None, codes=None, scales=None, ts=None, dq=None) == SUCCESS
+
+
+def test_nvfp4_dequantize_rejects():
+    L = fq.lib()
+    assert L.nvfp4_dequantize(A16, A16, A16, 4, 40, A16, None) == SHAPE
+    assert L.nvfp4_dequantize(None, A16, A16, 4, 64, A16, None) == NULL
+    assert L.nvfp4_dequantize(A16, A16, A16, 4, 64, A8, None) == MISALIGNED
+    assert L.nvfp4_dequantize(None, None, None, 0, 64, None, None) == SUCCESS
+
+
+def test_mxfp4_resq_rejects():
+    L = fq.lib()
+    f = L.mxfp4_resq_quantize
+    assert f(A16, 4, 48, A16, A16, A16, A16, A16, None) == SHAPE  # not a multiple of 32
+    assert f(A16, 4, 64, A16, A16, None, A16, A16, None) == NULL
+    assert f(A16, 4, 64, A8, A16, A16, A16, A16, None) == MISALIGNED
+    assert f(A16, 4, 64, A16, A16, A16, P(0x10002), A16, None) == MISALIGNED
+    assert f(None, 0, 64, None, None, None, None, None, None) == SUCCESS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
+    with pytest.raises(fq.Fp4qError):
+        fq.mxfp4_resq_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))

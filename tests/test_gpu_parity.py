@@ -1,0 +1,229 @@
+"""GPU parity: the HIP kernels against the CPU oracle, element by element,
+bit-exact, through the C ABI (via the Python binding).
+
+Covers the five named workloads at their full sizes (the oracle runs over
+row chunks in threads), an edge suite over row lengths that span several
+tiles with ragged tails and the long-row path, the hand-worked golden
+blocks, ragged group ranges, the standalone dequantizer, determinism and
+argument errors."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_block_quantization_amd as fq
+import oracle
+import workloads
+from goldens import load
+from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_nvfp4, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fq.lib()
+
+
+def f32_to_bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def check_nvfp4(x_bits, fos, dequant=True, label=""):
+    x = to_dev(x_bits)
+    codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=fos, dequant=dequant)
+    torch.cuda.synchronize()
+    want = oracle_nvfp4(x_bits, fos, dequant=dequant)
+    assert_same(host(codes), want[0], label + " codes")
+    assert_same(host(scales), want[1], label + " block_scales")
+    assert_same(host(ts)[:, None], want[2][:, None], label + " token_scales")
+    if dequant:
+        assert_same(bits_of(dq), want[3], label + " dequant")
+    return codes, scales, ts, dq
+
+
+def check_mx(x_bits, label=""):
+    got = fq.mxfp4_resq_quantize(to_dev(x_bits))
+    torch.cuda.synchronize()
+    want = oracle_mx(x_bits)
+    for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
+        assert_same(host(g), w, label + " " + n)
+
+
+# ------------------------------------------------------------ edge suite --
+
+def edge_rows(H, seed):
+    """Rows that exercise the corner cases of the method."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    z = np.zeros(H, np.float32)
+    rows.append(z)                                         # zero row
+    rows.append(np.where(np.arange(H) % 2, -0.0, 0.0).astype(np.float32))  # +-0
+    one = z.copy(); one[rng.integers(H)] = -3.25; rows.append(one)         # single nonzero
+    rows.append(np.full(H, 1.7, np.float32))               # equal values
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5], np.float32)
+    for p in (-3, 0, 7):                                   # grid points and midpoints
+        r = rng.choice(grid, H) * rng.choice([-1, 1], H) * np.float32(2.0 ** p)
+        r[0] = 6 * 2.0 ** p
+        rows.append(r.astype(np.float32))
+    rows.append(rng.standard_normal(H).astype(np.float32))
+    rows.append(rng.standard_t(3, H).astype(np.float32) * 40)
+    r = rng.standard_normal(H).astype(np.float32); r[rng.integers(H, size=max(1, H // 100))] *= 50
+    rows.append(r)
+    for sc in (2.0 ** -126, 2.0 ** -133, 2.0 ** 64, 2.0 ** 100, 2.0 ** 120):
+        rows.append((rng.standard_normal(H) * sc).astype(np.float32))
+    bits = [f32_to_bf16_bits(r) for r in rows]
+    sub = rng.integers(1, 0x80, H).astype(np.uint16) | (rng.integers(0, 2, H).astype(np.uint16) << 15)
+    bits.append(sub)                                       # BF16 subnormals only
+    big = np.full(H, 0x7F7F, np.uint16); big[1::3] = 0x0001  # largest finite + tiny
+    bits.append(big)
+    mix = rng.integers(0, 0x7F80, H).astype(np.uint16)     # random finite patterns
+    mix |= (rng.integers(0, 2, H).astype(np.uint16) << 15)
+    bits.append(mix)
+    return np.stack(bits, 0)
+
+
+HIDDEN = [16, 32, 48, 1008, 1024, 1040, 2048, 7168, 8192, 8208, 16400]
+
+
+@pytest.mark.parametrize("fos", [True, False])
+@pytest.mark.parametrize("H", HIDDEN)
+def test_nvfp4_edge_suite(H, fos):
+    check_nvfp4(edge_rows(H, seed=H), fos, label="edge H=%d" % H)
+
+
+@pytest.mark.parametrize("H", [32, 64, 96, 2048, 7200])
+def test_mx_edge_suite(H):
+    check_mx(edge_rows(H, seed=H + 1), label="mx edge H=%d" % H)
+
+
+def test_golden_blocks_on_gpu():
+    for name, c in load("nvfp4_worked_blocks.txt").items():
+        x = to_dev(c["x"][None, :])
+        codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=bool(c["four_over_six"]))
+        torch.cuda.synchronize()
+        assert host(ts).view(np.uint32)[0] == c["token_scale_bits"], name
+        np.testing.assert_array_equal(host(scales)[0], c["scales"], err_msg=name)
+        np.testing.assert_array_equal(host(codes)[0], c["codes"], err_msg=name)
+        np.testing.assert_array_equal(bits_of(dq)[0], c["dequant"], err_msg=name)
+    c = load("mxfp4_resq_worked_block.txt")["MX_first_group"]
+    out = fq.mxfp4_resq_quantize(to_dev(c["x"][None, :]))
+    for t, k in zip(out, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
+        np.testing.assert_array_equal(host(t)[0], c[k], err_msg=k)
+
+
+# ------------------------------------------------------ named workloads --
+
+@pytest.mark.parametrize("fos", [True, False])
+def test_tiny_ref(fos):
+    check_nvfp4(workloads.rows("tiny_ref"), fos, label="tiny_ref")
+
+
+def test_moe_act_full_size():
+    check_nvfp4(workloads.rows("moe_act"), True, label="moe_act")
+
+
+def test_expert_weights_full_size():
+    check_nvfp4(workloads.rows("expert_weights"), True, label="expert_weights")
+
+
+def test_ragged_routed_full_size():
+    x_bits = workloads.rows("ragged_routed")
+    offs = workloads.group_offsets()
+    x = to_dev(x_bits)
+    codes, scales, ts, _ = fq.nvfp4_quantize(x, True, offsets=torch.from_numpy(offs).cuda(),
+                                             dequant=False)
+    torch.cuda.synchronize()
+    want = oracle_nvfp4(x_bits, True, dequant=False)
+    assert_same(host(codes), want[0], "ragged codes")
+    assert_same(host(scales), want[1], "ragged scales")
+    assert_same(host(ts)[:, None], want[2][:, None], "ragged token_scales")
+
+
+def test_ragged_subrange_leaves_other_rows():
+    x_bits = workloads.rows("ragged_routed", 0, 8192)
+    sub = workloads.group_offsets()[2:6].copy()  # groups 2..4 of the routed rows
+    x = to_dev(x_bits)
+    R, H = x_bits.shape
+    out = (torch.full((R, H // 2), 0xAB, dtype=torch.uint8, device="cuda"),
+           torch.full((R, H // 16), 0xCD, dtype=torch.uint8, device="cuda"),
+           torch.full((R,), -7.0, dtype=torch.float32, device="cuda"),
+           torch.full((R, H), 1.5, dtype=torch.bfloat16, device="cuda"))
+    fq.nvfp4_quantize(x, True, offsets=torch.from_numpy(sub).cuda(), out=out)
+    torch.cuda.synchronize()
+    want = oracle_nvfp4(x_bits, True)
+    lo, hi = int(sub[0]), int(sub[-1])
+    assert 0 < lo < hi < R
+    got = [host(out[0]), host(out[1]), host(out[2]), bits_of(out[3])]
+    fills = (0xAB, 0xCD, np.float32(-7.0), 0x3FC0)
+    for g, w, f, n in zip(got, want, fills, ("codes", "scales", "ts", "dq")):
+        w = w if w.ndim > 1 else w[:, None]
+        g = g if g.ndim > 1 else g[:, None]
+        assert_same(g[lo:hi], w[lo:hi], "subrange " + n)
+        assert (g[:lo] == f).all() and (g[hi:] == f).all(), n
+
+
+def test_resq_act_full_size():
+    check_mx(workloads.rows("resq_act"), label="resq_act")
+
+
+# -------------------------------------------------------------- dequant --
+
+def test_standalone_dequant_matches_fused():
+    for name in ("tiny_ref", "moe_act"):
+        codes, scales, ts, dq = fq.nvfp4_quantize(workloads.tensor(name, "cuda"), True)
+        out = fq.nvfp4_dequantize(codes, scales, ts)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), dq.view(torch.int16)), name
+
+
+def test_standalone_dequant_random_bytes():
+    rng = np.random.default_rng(99)
+    R, H = 512, 1040
+    codes = rng.integers(0, 256, (R, H // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (R, H // 16), dtype=np.uint8)
+    scales |= (rng.integers(0, 2, scales.shape, dtype=np.uint8) << 7)  # signed scale bytes
+    ts = (rng.standard_normal(R) * 2.0 ** rng.integers(-140, 60, R)).astype(np.float32)
+    out = fq.nvfp4_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                              torch.from_numpy(ts).cuda())
+    torch.cuda.synchronize()
+    assert_same(bits_of(out), oracle.nvfp4_dequantize(codes, scales, ts), "dequant")
+
+
+# ------------------------------------------- determinism and invariance --
+
+def test_determinism_streams_and_batch_invariance():
+    x_bits = workloads.rows("moe_act", 0, 512)
+    x = to_dev(x_bits)
+    ref = fq.nvfp4_quantize(x, True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        again = fq.nvfp4_quantize(x, True)
+    torch.cuda.synchronize()
+    def rowbytes(t):
+        return t.reshape(t.shape[0], -1).view(torch.uint8)
+
+    for a, b in zip(ref, again):
+        assert torch.equal(rowbytes(a), rowbytes(b))
+    perm = torch.randperm(512, generator=torch.Generator().manual_seed(1)).cuda()
+    pr = fq.nvfp4_quantize(x[perm].contiguous(), True)
+    one = fq.nvfp4_quantize(x[37:38].contiguous(), True)
+    torch.cuda.synchronize()
+    for a, b, c in zip(ref, pr, one):
+        a8, b8, c8 = rowbytes(a), rowbytes(b), rowbytes(c)
+        assert torch.equal(a8[perm], b8)
+        assert torch.equal(a8[37:38], c8)
+
+
+def test_empty_and_rejected_calls():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    codes, scales, ts, dq = fq.nvfp4_quantize(x)
+    assert codes.shape == (0, 32) and dq.shape == (0, 64)
+    fq.mxfp4_resq_quantize(x)
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_quantize(torch.zeros((4, 40), dtype=torch.bfloat16, device="cuda"))
+    flat = torch.zeros(16 * 5, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fq.Fp4qError):  # 2-byte offset: misaligned
+        fq.nvfp4_quantize(flat[1:1 + 64].view(4, 16))

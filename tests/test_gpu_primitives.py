@@ -1,0 +1,123 @@
+"""Exhaustive GPU parity of the number-format conversions the kernels use
+(fp4q_device.h), against the CPU oracle's pinned primitives.
+
+The probe kernels (tests/gpu_probes/probes.hip) evaluate a conversion on
+every binary32 pattern of a range; the host compares each result with the
+oracle."""
+import ctypes
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import fnptr
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROBES = os.path.join(ROOT, "tests", "_build", "libprobes.so")
+CHUNK = 1 << 26  # result pairs per launch
+
+HW_FP4, SW_FP4, HW_BF16, SW_BF16, HW_FP8, SW_FP8 = range(6)
+
+
+def bits(f):
+    return struct.unpack("<I", struct.pack("<f", f))[0]
+
+
+@pytest.fixture(scope="module")
+def probes():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(PROBES):
+        pytest.fail("probe library not built: run __graft_entry__.build()")
+    L = ctypes.CDLL(PROBES)
+    L.probe_launch.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    L.probe_launch.restype = ctypes.c_int
+    L.probe_decode_tables.argtypes = [ctypes.c_void_p] * 5
+    L.probe_decode_tables.restype = ctypes.c_int
+    return L
+
+
+def run(probes, which, lo, flip, n, dtype):
+    out = torch.empty(n, dtype=dtype, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert probes.probe_launch(which, lo, flip, n, ctypes.c_void_p(out.data_ptr()),
+                               ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def sweep(probes, pins, olib, which, cmp, fn_name, lo, hi, flip, dtype):
+    """Compare every pattern in [lo, hi] (hi - lo + 1 even)."""
+    total_bad = 0
+    start = lo
+    while start <= hi:
+        n = min(CHUNK, (hi - start + 1) // 2)
+        got = np.ascontiguousarray(run(probes, which, start, flip, n, dtype))
+        first = ctypes.c_uint64(0)
+        if cmp == "fp4":
+            bad = pins.cmp_fp4(fnptr(olib, fn_name), start, flip, n, got.ctypes.data, ctypes.byref(first))
+        else:
+            bad = getattr(pins, "cmp_" + cmp)(fnptr(olib, fn_name), start, n, got.ctypes.data,
+                                              ctypes.byref(first))
+        assert bad == 0, "%s: %d mismatches, first pair at pattern %#x" % (
+            cmp, bad, (start + 2 * first.value) ^ flip)
+        total_bad += bad
+        start += 2 * n
+    return total_bad
+
+
+@pytest.mark.parametrize("flip", [0, 0x80000000])
+def test_e2m1_device_helper_exhaustive(probes, pins, olib, flip):
+    # every FP32 magnitude in [0, 8] (and its negative), sign bit kept
+    sweep(probes, pins, olib, SW_FP4, "fp4", "oracle_e2m1_code", 0, bits(8.0) + 1, flip, torch.uint8)
+
+
+def test_e2m1_device_helper_saturation_and_nan(probes, pins, olib):
+    # (8, +inf]: strided windows up to the infinity pattern
+    for lo in range(bits(8.0) + 2, 0x7F800000, 0x00800000):
+        sweep(probes, pins, olib, SW_FP4, "fp4", "oracle_e2m1_code", lo, lo + (1 << 16) - 1, 0,
+              torch.uint8)
+    sweep(probes, pins, olib, SW_FP4, "fp4", "oracle_e2m1_code", 0x7F7FFFFE, 0x7F800000 - 1, 0,
+          torch.uint8)
+    # +inf saturates; NaN (0 * inf) gives code 0 like the oracle
+    got = run(probes, SW_FP4, 0x7F800000, 0, 1, torch.uint8)[0]
+    assert got & 15 == 7 and got >> 4 == 0
+
+
+def test_bf16_device_helper_exhaustive(probes, pins, olib):
+    # all 2^32 patterns (NaN inputs skipped)
+    sweep(probes, pins, olib, SW_BF16, "bf16", "oracle_bf16_rne", 0, 0xFFFFFFFF, 0, torch.int32)
+
+
+def test_e4m3_device_helper_exhaustive(probes, pins, olib):
+    sweep(probes, pins, olib, SW_FP8, "fp8", "oracle_e4m3_encode", 0, bits(1024.0) + 1, 0,
+          torch.int16)
+    for lo in range(bits(1024.0) + 2, 0x7F800000, 0x00400000):
+        sweep(probes, pins, olib, SW_FP8, "fp8", "oracle_e4m3_encode", lo, lo + 4095, 0,
+              torch.int16)
+
+
+def test_decode_tables(probes):
+    t = [torch.empty(n, dtype=torch.float32, device="cuda") for n in (512, 512, 256, 256)]
+    st = torch.cuda.current_stream().cuda_stream
+    assert probes.probe_decode_tables(*[ctypes.c_void_p(x.data_ptr()) for x in t],
+                                      ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    fp4_sw, fp8_sw = t[1].cpu().numpy(), t[3].cpu().numpy()
+    for b in range(256):
+        for h in range(2):
+            nib = (b >> (4 * h)) & 15
+            g = oracle.e2m1_value(nib & 7)
+            want = -g if nib & 8 else g
+            assert fp4_sw[2 * b + h] == want and np.signbit(fp4_sw[2 * b + h]) == bool(nib & 8)
+        want8 = oracle.e4m3_decode(b)
+        if want8 != want8:
+            assert fp8_sw[b] != fp8_sw[b]
+        else:
+            assert fp8_sw[b] == want8
