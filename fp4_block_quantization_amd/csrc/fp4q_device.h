@@ -13,6 +13,47 @@
 
 namespace fp4q {
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// ---- gfx950 conversion instructions -------------------------------------
+// Each was compared exhaustively on the GPU with the CPU reference's
+// definition over the inputs the kernels can feed it (see the GPU probe
+// tests): E2M1 encode of signed FP32 with unit scale (round to nearest
+// even, saturating, sign kept for zeros), E2M1 decode, E4M3FN encode on
+// [0, 448], E4M3FN decode and FP32 -> BF16 (round to nearest even).  NaN
+// must not reach the E2M1 encode (it yields 7, not 0).
+
+// Codes of a (low nibble) and b (high nibble) into byte SEL of acc.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_e2m1x2(uint32_t acc, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, SEL);
+}
+
+// Signed values of the two nibbles of byte SEL of src (low nibble in .x).
+template <int SEL>
+__device__ __forceinline__ float2v e2m1x2_values(uint32_t src) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, 1.0f, SEL);
+}
+
+// E4M3FN bytes of a (byte 0) and b (byte 1), both in [0, 448].
+__device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+template <int SEL>
+__device__ __forceinline__ float e4m3_value(uint32_t bytes) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)bytes, SEL);
+}
+
+// Two FP32 -> packed BF16 (a in the low half).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const float2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+// ---- portable definitions -------------------------------------------------
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

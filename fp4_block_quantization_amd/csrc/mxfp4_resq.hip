@@ -18,24 +18,33 @@ namespace fp4q {
 
 namespace {
 
-// MXFP4 of 32 FP32 values: nibbles (sign << 3 | code) and the exact
-// dequantized values +-g * 2^k.  Returns the E8M0 byte k + 127.
-__device__ __forceinline__ uint32_t mx_quantize32(const float (&v)[32], uint32_t (&nib)[32],
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// MXFP4 of 32 FP32 values: packed nibbles (element 2i in the low nibble of
+// byte i) and the exact dequantized values +-g * 2^k.  Returns the E8M0
+// byte k + 127.  x * 2^-k is exact (or far below the first code), so the
+// hardware E2M1 conversion of the scaled value is the reference rounding.
+__device__ __forceinline__ uint32_t mx_quantize32(const float (&v)[32], uint32_t (&cw)[4],
                                                   float (&deq)[32]) {
   uint32_t mbits = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) mbits = max(mbits, __float_as_uint(v[i]) & 0x7FFFFFFFu);
   const int k = mx_exponent(mbits);
   const float down = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k, k in [-127, 125]
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float g;
-    const uint32_t q = e2m1_code_sw(fabsf(v[i]) * down, g);
-    const uint32_t neg = __float_as_uint(v[i]) >> 31;
-    nib[i] = q | (neg << 3);
-    const float m = ldexpf(g, k);  // exact
-    deq[i] = neg ? -m : m;
-  }
+  static_for<0, 16>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    cw[p >> 2] = cvt_e2m1x2<p & 3>(p & 3 ? cw[p >> 2] : 0u, v[2 * p] * down,
+                                    v[2 * p + 1] * down);
+    const float2v g = e2m1x2_values<p & 3>(cw[p >> 2]);
+    deq[2 * p] = ldexpf(g.x, k);  // exact
+    deq[2 * p + 1] = ldexpf(g.y, k);
+  });
   return (uint32_t)(k + 127);
 }
 
@@ -58,39 +67,32 @@ __global__ __launch_bounds__(256) void mxfp4_resq_blocks(
     }
   }
 
-  uint32_t nib[32];
+  uint32_t cw[4];
   float deq[32];
-  scales[blk] = (uint8_t)mx_quantize32(v, nib, deq);
-  uint32_t cw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) cw[i >> 3] |= nib[i] << (4 * (i & 7));
+  scales[blk] = (uint8_t)mx_quantize32(v, cw, deq);
   codes[blk] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
 
   // residual, exact in FP32, quantized again over all 32 values
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = v[i] - deq[i];
-  res_scales[blk] = (uint8_t)mx_quantize32(v, nib, deq);
+  res_scales[blk] = (uint8_t)mx_quantize32(v, cw, deq);
 
   // S_{2:4}: per group of 4 keep the two largest magnitudes, ties to the
-  // lower index.  Key = magnitude * 4 + (3 - index) orders uniquely.
+  // lower index.  Key = magnitude * 4 + (3 - index) orders uniquely; the
+  // two largest of four keys come from a max/min network.
   uint32_t rc[2] = {0u, 0u}, meta = 0u;
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
+    const uint32_t word = cw[g >> 1] >> (16 * (g & 1));  // this group's 4 nibbles
     uint32_t key[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = ((nib[4 * g + i] & 7u) << 2) | (3u - i);
-    const uint32_t k1 = max(max(key[0], key[1]), max(key[2], key[3]));
-    uint32_t k2 = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) k2 = max(k2, key[i] == k1 ? 0u : key[i]);
+    for (int i = 0; i < 4; ++i) key[i] = (((word >> (4 * i)) & 7u) << 2) | (3u - i);
+    const uint32_t p = max(key[0], key[1]), q = min(key[0], key[1]);
+    const uint32_t r = max(key[2], key[3]), t = min(key[2], key[3]);
+    const uint32_t k1 = max(p, r), k2 = max(min(p, r), max(q, t));
     const uint32_t ia = 3u - (k1 & 3u), ib = 3u - (k2 & 3u);
     const uint32_t i0 = min(ia, ib), i1 = max(ia, ib);
-    uint32_t n0 = 0u, n1 = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      n0 = (i0 == (uint32_t)i) ? nib[4 * g + i] : n0;
-      n1 = (i1 == (uint32_t)i) ? nib[4 * g + i] : n1;
-    }
+    const uint32_t n0 = (word >> (4 * i0)) & 15u, n1 = (word >> (4 * i1)) & 15u;
     rc[g >> 2] |= (n0 | (n1 << 4)) << (8 * (g & 3));
     meta |= (i0 | (i1 << 2)) << (4 * g);
   }

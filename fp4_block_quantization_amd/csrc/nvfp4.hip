@@ -4,7 +4,7 @@
 // Method: "NVFP4-RL" (jianyuh.github.io), sections 2-4, and "humans&
 // Open-Sources the First Stable 4-Bit RL Training Recipe at 1.73x Speedup"
 // (alphasignal.ai), sections 1-3.  Each token row gets its own FP32 scale
-// from its amax over the hidden dimension; the E4M3 scale of every
+// s from its amax over the hidden dimension; the E4M3 scale of every
 // 16-element block is computed in the same kernel; per block the max is
 // mapped to 6 or to 4, whichever gives the lower squared error (ties keep
 // 6); the BF16 dequantized values of the chosen encoding are written in the
@@ -14,6 +14,14 @@
 // whole row stays in VGPRs between the amax reduction and the block pass
 // (CH chunks of 64 blocks = 1024 elements), so HBM sees every input byte
 // once; rows longer than 8 chunks take a second, L2-served read.
+//
+// Arithmetic per block and candidate k (all IEEE binary32, no contraction):
+//   t = b / fl(k s)   (IEEE division)      e = E4M3(min(t, 448))
+//   r = 1 / fl(e s)   (IEEE division, looked up in a per-row LDS table of
+//                      all 127 E4M3 values: the same bits, computed once
+//                      per row instead of once per block)
+//   v = x r, q = E2M1(v) with sign, c = fl(fl(+-g e) s), err += (x - c)^2
+// The E2M1/E4M3/BF16 conversions are the gfx950 conversion instructions.
 #include "fp4q_device.h"
 #include "fp4q_launch.h"
 
@@ -22,6 +30,14 @@ namespace fp4q {
 namespace {
 
 constexpr int kWaves = 4;  // wavefronts (rows) per workgroup
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Wave-wide max of a non-negative value held as its bit pattern.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -38,74 +54,110 @@ __device__ __forceinline__ uint32_t block_absmax_bits(const uint32_t (&w)[8]) {
   return m;
 }
 
+// Per-row reciprocal table: tab[byte] = 1 / fl(e(byte) * s) for every
+// E4M3 byte 0..127 (0 where the decode step is 0).  Each lane fills two
+// entries; only this wave reads them.
+__device__ __forceinline__ void fill_recip_table(float* tab, float s, int lane) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t byte = (uint32_t)lane + 64u * k;
+    const float d = e4m3_decode(byte) * s;
+    tab[byte] = (d != 0.0f) ? 1.0f / d : 0.0f;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 struct Candidate {
-  uint32_t code[2];  // 16 nibbles
-  uint32_t ebyte;
+  uint32_t code[2];  // 16 nibbles, element 2i in the low nibble of byte i
   float err;
-  uint32_t deq[8];  // 16 BF16 values
+  float c[16];  // signed FP32 candidate values
 };
 
-// One candidate of one block: the block max b is mapped to k via
-// ks = fl(k * s) (NVFP4-RL blog, section 4).
-template <bool DQ>
-__device__ __forceinline__ void candidate(const float (&xv)[16], float b, float ks, float s,
-                                          Candidate& c) {
-  float e;
-  c.ebyte = e4m3_encode(b / ks, e);
-  const float d = e * s;
-  const float r = (d != 0.0f) ? 1.0f / d : 0.0f;  // a zero step gives code 0 everywhere
-  float err = 0.0f;
-  uint32_t code[2] = {0u, 0u};
-  float cv[16];
+// One candidate: decode step with value e and reciprocal r under token
+// scale s.
+__device__ __forceinline__ void candidate(const float (&x)[16], float e, float r, float s,
+                                          Candidate& out) {
+  if (__builtin_expect(r <= 3.4028235e38f, 1)) {
+    uint32_t code[2] = {0u, 0u};
+    float err = 0.0f;
+    static_for<0, 8>([&](auto P) {
+      constexpr int p = decltype(P)::value;
+      const float v0 = x[2 * p] * r, v1 = x[2 * p + 1] * r;
+      code[p >> 2] = cvt_e2m1x2<p & 3>(code[p >> 2], v0, v1);
+      const float2v g = e2m1x2_values<p & 3>(code[p >> 2]);
+      const float ge0 = g.x * e, ge1 = g.y * e;  // exact: <= 6 significant bits
+      const float c0 = ge0 * s, c1 = ge1 * s;
+      const float d0 = x[2 * p] - c0, d1 = x[2 * p + 1] - c1;
+      const float q0 = d0 * d0, q1 = d1 * d1;
+      err = err + q0;
+      err = err + q1;
+      out.c[2 * p] = c0;
+      out.c[2 * p + 1] = c1;
+    });
+    out.code[0] = code[0];
+    out.code[1] = code[1];
+    out.err = err;
+  } else {
+    // r = +inf (a decode step below 2^-128): x * r is +-inf for nonzero x
+    // and NaN for zeros, which the portable rounding maps to code 0.
+    uint32_t code[2] = {0u, 0u};
+    float err = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float a = fabsf(xv[i]);
-    float g;
-    const uint32_t q = e2m1_code_sw(a * r, g);
-    const float ge = g * e;  // exact: at most 6 significant bits
-    float cand = ge * s;
-    const uint32_t neg = __float_as_uint(xv[i]) >> 31;
-    cand = neg ? -cand : cand;
-    const float delta = xv[i] - cand;
-    const float sq = delta * delta;
-    err = err + sq;
-    code[i >> 3] |= (q | (neg << 3)) << (4 * (i & 7));
-    cv[i] = cand;
-  }
-  c.code[0] = code[0];
-  c.code[1] = code[1];
-  c.err = err;
-  if (DQ) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) c.deq[k] = pack_bf16x2(cv[2 * k], cv[2 * k + 1]);
+    for (int i = 0; i < 16; ++i) {
+      float g;
+      const uint32_t q = e2m1_code_sw(fabsf(x[i]) * r, g);
+      const uint32_t neg = __float_as_uint(x[i]) >> 31;
+      const float ge = g * e;
+      float c = ge * s;
+      c = neg ? -c : c;
+      const float d = x[i] - c;
+      const float sq = d * d;
+      err = err + sq;
+      code[i >> 3] |= (q | (neg << 3)) << (4 * (i & 7));
+      out.c[i] = c;
+    }
+    out.code[0] = code[0];
+    out.code[1] = code[1];
+    out.err = err;
   }
 }
 
 template <bool FOS, bool DQ>
 __device__ __forceinline__ void quantize_block(const uint32_t (&w)[8], uint32_t bbits, float s,
-                                               float s6, float s4, int64_t blk,
-                                               uint2* __restrict__ codes,
+                                               float ks6, float ks4, const float* tab,
+                                               int64_t blk, uint2* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
                                                uint4* __restrict__ dq) {
-  float xv[16];
+  float x[16];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    xv[2 * k] = bf16_lo(w[k]);
-    xv[2 * k + 1] = bf16_hi(w[k]);
+    x[2 * k] = bf16_lo(w[k]);
+    x[2 * k + 1] = bf16_hi(w[k]);
   }
   const float b = __uint_as_float(bbits << 16);
+  // both candidate block scales in one conversion (byte 0: map to 6,
+  // byte 1: map to 4); E4M3 saturates at 448
+  const float t6 = fminf(b / ks6, 448.0f);
+  const float t4 = FOS ? fminf(b / ks4, 448.0f) : 0.0f;
+  const uint32_t eb = cvt_e4m3x2(t6, t4);
+
   Candidate c6;
-  candidate<DQ>(xv, b, s6, s, c6);
+  candidate(x, e4m3_value<0>(eb), tab[eb & 0xFFu], s, c6);
+  bool four = false;
+  Candidate c4;
   if (FOS) {
-    Candidate c4;
-    candidate<DQ>(xv, b, s4, s, c4);
-    if (c4.err < c6.err) c6 = c4;  // strictly lower error: 4 wins; ties keep 6
+    candidate(x, e4m3_value<1>(eb), tab[eb >> 8], s, c4);
+    four = c4.err < c6.err;  // strictly lower error: 4 wins; ties keep 6
   }
-  codes[blk] = make_uint2(c6.code[0], c6.code[1]);
-  scales[blk] = (uint8_t)c6.ebyte;
+  codes[blk] = four ? make_uint2(c4.code[0], c4.code[1]) : make_uint2(c6.code[0], c6.code[1]);
+  scales[blk] = (uint8_t)(four ? (eb >> 8) : (eb & 0xFFu));
   if (DQ) {
-    dq[2 * blk] = make_uint4(c6.deq[0], c6.deq[1], c6.deq[2], c6.deq[3]);
-    dq[2 * blk + 1] = make_uint4(c6.deq[4], c6.deq[5], c6.deq[6], c6.deq[7]);
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      o[k] = cvt_bf16x2(four ? c4.c[2 * k] : c6.c[2 * k], four ? c4.c[2 * k + 1] : c6.c[2 * k + 1]);
+    dq[2 * blk] = make_uint4(o[0], o[1], o[2], o[3]);
+    dq[2 * blk + 1] = make_uint4(o[4], o[5], o[6], o[7]);
   }
 }
 
@@ -119,14 +171,27 @@ __device__ __forceinline__ bool row_range(int64_t row, int64_t rows, const int64
   return row >= lo && row < hi;
 }
 
+// Token scale and the per-row constants: ks = fl(k s); a zero row uses 1
+// so that b / ks = 0 / 1 gives a zero block scale.
+template <bool FOS>
+__device__ __forceinline__ float token_scale(uint32_t amax_bits, float& ks6, float& ks4) {
+  const float amax = __uint_as_float(amax_bits << 16);
+  const float s = amax / (FOS ? 1536.0f : 2688.0f);
+  ks6 = (s != 0.0f) ? 6.0f * s : 1.0f;
+  ks4 = (s != 0.0f) ? 4.0f * s : 1.0f;
+  return s;
+}
+
 // Register-resident row: nblk <= 64 * CH.
 template <int CH, bool FOS, bool DQ>
 __global__ __launch_bounds__(64 * kWaves) void nvfp4_quantize_rows(
     const uint4* __restrict__ x, int64_t rows, int nblk, const int64_t* __restrict__ offs,
     int64_t ngroups, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tscale, uint4* __restrict__ dq) {
+  __shared__ float recip[kWaves][128];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
   if (!row_range(row, rows, offs, ngroups)) return;
 
   const int64_t base = row * nblk;  // first block of the row
@@ -150,15 +215,17 @@ __global__ __launch_bounds__(64 * kWaves) void nvfp4_quantize_rows(
     bmax[c] = block_absmax_bits(w[c]);
     lmax = max(lmax, bmax[c]);
   }
-  const float amax = __uint_as_float(wave_max_u32(lmax) << 16);
-  const float s = amax / (FOS ? 1536.0f : 2688.0f);
+  float ks6, ks4;
+  const float s = token_scale<FOS>(wave_max_u32(lmax), ks6, ks4);
   if (lane == 0) tscale[row] = s;
-  const float s6 = 6.0f * s, s4 = 4.0f * s;
+  fill_recip_table(recip[wave], s, lane);
 
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int j = c * 64 + lane;
-    if (j < nblk) quantize_block<FOS, DQ>(w[c], bmax[c], s, s6, s4, base + j, codes, scales, dq);
+    if (j < nblk)
+      quantize_block<FOS, DQ>(w[c], bmax[c], s, ks6, ks4, recip[wave], base + j, codes, scales,
+                              dq);
   }
 }
 
@@ -169,8 +236,10 @@ __global__ __launch_bounds__(64 * kWaves) void nvfp4_quantize_long_rows(
     const uint4* __restrict__ x, int64_t rows, int nblk, const int64_t* __restrict__ offs,
     int64_t ngroups, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tscale, uint4* __restrict__ dq) {
+  __shared__ float recip[kWaves][128];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
   if (!row_range(row, rows, offs, ngroups)) return;
   const int64_t base = row * nblk;
 
@@ -180,14 +249,15 @@ __global__ __launch_bounds__(64 * kWaves) void nvfp4_quantize_long_rows(
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
     lmax = max(lmax, block_absmax_bits(w));
   }
-  const float amax = __uint_as_float(wave_max_u32(lmax) << 16);
-  const float s = amax / (FOS ? 1536.0f : 2688.0f);
+  float ks6, ks4;
+  const float s = token_scale<FOS>(wave_max_u32(lmax), ks6, ks4);
   if (lane == 0) tscale[row] = s;
-  const float s6 = 6.0f * s, s4 = 4.0f * s;
+  fill_recip_table(recip[wave], s, lane);
   for (int j = lane; j < nblk; j += 64) {
     const uint4 a = x[2 * (base + j)], bq = x[2 * (base + j) + 1];
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-    quantize_block<FOS, DQ>(w, block_absmax_bits(w), s, s6, s4, base + j, codes, scales, dq);
+    quantize_block<FOS, DQ>(w, block_absmax_bits(w), s, ks6, ks4, recip[wave], base + j, codes,
+                            scales, dq);
   }
 }
 
@@ -201,19 +271,12 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_blocks(
   const float e = e4m3_decode(scales[blk]);
   const uint2 cw = codes[blk];
   uint32_t o[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t word = (k < 4) ? cw.x : cw.y;
-    float v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t nib = (word >> (8 * (k & 3) + 4 * h)) & 15u;
-      const float ge = e2m1_value(nib & 7u) * e;
-      const float c = ge * s;
-      v[h] = (nib & 8u) ? -c : c;
-    }
-    o[k] = pack_bf16x2(v[0], v[1]);
-  }
+  static_for<0, 8>([&](auto P) {
+    constexpr int k = decltype(P)::value;
+    const float2v g = e2m1x2_values<k & 3>(k < 4 ? cw.x : cw.y);
+    const float ge0 = g.x * e, ge1 = g.y * e;
+    o[k] = cvt_bf16x2(ge0 * s, ge1 * s);
+  });
   out[2 * blk] = make_uint4(o[0], o[1], o[2], o[3]);
   out[2 * blk + 1] = make_uint4(o[4], o[5], o[6], o[7]);
 }

@@ -1,5 +1,7 @@
 """Exhaustive GPU parity of the number-format conversions the kernels use
-(fp4q_device.h), against the CPU oracle's pinned primitives.
+(fp4q_device.h) -- the gfx950 conversion instructions on the fast path and
+the portable helpers on the rare paths -- against the CPU oracle's pinned
+primitives.
 
 The probe kernels (tests/gpu_probes/probes.hip) evaluate a conversion on
 every binary32 pattern of a range; the host compares each result with the
@@ -73,6 +75,33 @@ def sweep(probes, pins, olib, which, cmp, fn_name, lo, hi, flip, dtype):
 
 
 @pytest.mark.parametrize("flip", [0, 0x80000000])
+def test_e2m1_hw_conversion_exhaustive(probes, pins, olib, flip):
+    # every FP32 value in [-8, 8]: code with the sign bit kept (also for
+    # zeros and values that round to zero)
+    sweep(probes, pins, olib, HW_FP4, "fp4", "oracle_e2m1_code", 0, bits(8.0) + 1, flip, torch.uint8)
+
+
+def test_e2m1_hw_conversion_saturation(probes, pins, olib):
+    for flip in (0, 0x80000000):
+        for lo in range(bits(8.0) + 2, 0x7F800000, 0x00800000):
+            sweep(probes, pins, olib, HW_FP4, "fp4", "oracle_e2m1_code", lo, lo + (1 << 16) - 1,
+                  flip, torch.uint8)
+    # +-inf saturate (the kernels feed +-inf only through the portable path)
+    got = run(probes, HW_FP4, 0x7F7FFFFF, 0, 1, torch.uint8)[0]
+    assert got == 0x77
+
+
+def test_bf16_hw_conversion_exhaustive(probes, pins, olib):
+    sweep(probes, pins, olib, HW_BF16, "bf16", "oracle_bf16_rne", 0, 0xFFFFFFFF, 0, torch.int32)
+
+
+def test_e4m3_hw_conversion_0_to_448(probes, pins, olib):
+    # the kernels clamp the target scale to 448 before converting
+    sweep(probes, pins, olib, HW_FP8, "fp8", "oracle_e4m3_encode", 0, bits(448.0) + 1, 0,
+          torch.int16)
+
+
+@pytest.mark.parametrize("flip", [0, 0x80000000])
 def test_e2m1_device_helper_exhaustive(probes, pins, olib, flip):
     # every FP32 magnitude in [0, 8] (and its negative), sign bit kept
     sweep(probes, pins, olib, SW_FP4, "fp4", "oracle_e2m1_code", 0, bits(8.0) + 1, flip, torch.uint8)
@@ -109,15 +138,17 @@ def test_decode_tables(probes):
     assert probes.probe_decode_tables(*[ctypes.c_void_p(x.data_ptr()) for x in t],
                                       ctypes.c_void_p(st)) == 0
     torch.cuda.synchronize()
-    fp4_sw, fp8_sw = t[1].cpu().numpy(), t[3].cpu().numpy()
+    fp4_hw, fp4_sw, fp8_hw, fp8_sw = (x.cpu().numpy() for x in t)
     for b in range(256):
         for h in range(2):
             nib = (b >> (4 * h)) & 15
             g = oracle.e2m1_value(nib & 7)
             want = -g if nib & 8 else g
-            assert fp4_sw[2 * b + h] == want and np.signbit(fp4_sw[2 * b + h]) == bool(nib & 8)
+            for tab in (fp4_hw, fp4_sw):
+                assert tab[2 * b + h] == want and np.signbit(tab[2 * b + h]) == bool(nib & 8)
         want8 = oracle.e4m3_decode(b)
-        if want8 != want8:
-            assert fp8_sw[b] != fp8_sw[b]
-        else:
-            assert fp8_sw[b] == want8
+        for tab in (fp8_hw, fp8_sw):
+            if want8 != want8:
+                assert tab[b] != tab[b]
+            else:
+                assert tab[b] == want8
