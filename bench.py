@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--parts", default="copy,dequant,resq,ragged,weights",
+                    help="secondary measurements to run (comma list)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     args = ap.parse_args()
 
@@ -197,14 +199,16 @@ def main():
     torch.cuda.empty_cache()
 
     secondary = {}
-    if not args.no_secondary:
-        # device copy ceiling (a plain copy kernel of 2 x 256 MiB traffic)
+    parts = set() if args.no_secondary else set(args.parts.split(","))
+    if "copy" in parts:
+        # device copy ceiling (a plain copy kernel of 2 x 256 MiB traffic);
+        # also the calibration kernel for the HBM byte counters
         src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
         dsts = [torch.empty_like(src) for _ in range(3)]
         p, _ = time_calls(lambda d: d.copy_(src), dsts, 100, 10)
         secondary["device_copy_GBps"] = round(2 * src.numel() / (p.mean() * 1e-3) / 1e9, 1)
         del src, dsts
-
+    if "dequant" in parts:
         # standalone dequant on the headline shape
         c, s_, ts, _ = fq.nvfp4_quantize(x, True, dequant=False)
         dsets = [(c.clone(), s_.clone(), ts.clone(), torch.empty_like(x)) for _ in range(4)]
@@ -214,7 +218,7 @@ def main():
             "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
         del dsets, c, s_, ts
         torch.cuda.empty_cache()
-
+    if "resq" in parts:
         # MXFP4 Rollout-ResQ
         xr = workloads.tensor("resq_act", dev)
         msets = [xr] + [xr.clone() for _ in range(3)]
@@ -226,7 +230,7 @@ def main():
             "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
         del msets, mouts, xr
         torch.cuda.empty_cache()
-
+    if "ragged" in parts:
         # ragged routed, quantize only
         xg = workloads.tensor("ragged_routed", dev)
         offs = torch.from_numpy(workloads.group_offsets()).to(dev)
@@ -238,7 +242,7 @@ def main():
             "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
         del gsets, xg
         torch.cuda.empty_cache()
-
+    if "weights" in parts:
         # expert weights, 32 x 2048 x 7168
         xw = workloads.tensor("expert_weights", dev)
         wsets = rotating_nvfp4_sets(xw, 1)
@@ -248,6 +252,7 @@ def main():
             "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
         del wsets, xw
         torch.cuda.empty_cache()
+    if secondary:
         print("[bench] secondary: %s" % json.dumps(secondary), file=sys.stderr, flush=True)
 
     cpu = None

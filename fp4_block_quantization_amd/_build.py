@@ -31,26 +31,29 @@ HIP_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libfp4q.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out_path: str = None) -> str:
+    """Compile every source and link libfp4q.so (or out_path, with
+    extra_flags such as -D launch knobs); returns the library path."""
+    out_path = out_path or LIB_PATH
+    obj_dir = os.path.join(os.path.dirname(out_path), "obj_" + os.path.basename(out_path))
+    os.makedirs(obj_dir, exist_ok=True)
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC, *HIP_FLAGS, *lang, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        cmd = [HIPCC, *HIP_FLAGS, *extra_flags, *lang, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
                "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    tmp = out_path + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

@@ -15,6 +15,7 @@ namespace fp4q {
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // ---- gfx950 conversion instructions -------------------------------------
 // Each was compared exhaustively on the GPU with the CPU reference's
@@ -34,6 +35,12 @@ __device__ __forceinline__ uint32_t cvt_e2m1x2(uint32_t acc, float a, float b) {
 template <int SEL>
 __device__ __forceinline__ float2v e2m1x2_values(uint32_t src) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, 1.0f, SEL);
+}
+
+// The same values as FP16 (exact: E2M1 values are FP16 numbers).
+template <int SEL>
+__device__ __forceinline__ half2v e2m1x2_values_f16(uint32_t src) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, 1.0f, SEL);
 }
 
 // E4M3FN bytes of a (byte 0) and b (byte 1), both in [0, 448].

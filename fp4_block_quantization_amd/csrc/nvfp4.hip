@@ -10,18 +10,28 @@
 // 6); the BF16 dequantized values of the chosen encoding are written in the
 // same pass for the dequantized backward.
 //
-// Mapping (K1): one wavefront per row, one lane per 16-element block.  The
-// whole row stays in VGPRs between the amax reduction and the block pass
-// (CH chunks of 64 blocks = 1024 elements), so HBM sees every input byte
-// once; rows longer than 8 chunks take a second, L2-served read.
+// Mapping (K1): one lane per 16-element block; a wavefront covers a chunk
+// of 64 blocks (1024 elements) of one row and a workgroup covers whole rows
+// (up to 16 chunks), combining the row amax through LDS.  Each lane keeps
+// its block in VGPRs between the amax and the block pass, so HBM sees every
+// input byte once; rows longer than 16 chunks take a second, L2-served read.
 //
-// Arithmetic per block and candidate k (all IEEE binary32, no contraction):
-//   t = b / fl(k s)   (IEEE division)      e = E4M3(min(t, 448))
-//   r = 1 / fl(e s)   (IEEE division, looked up in a per-row LDS table of
-//                      all 127 E4M3 values: the same bits, computed once
-//                      per row instead of once per block)
-//   v = x r, q = E2M1(v) with sign, c = fl(fl(+-g e) s), err += (x - c)^2
-// The E2M1/E4M3/BF16 conversions are the gfx950 conversion instructions.
+// Arithmetic per block and candidate k (each an IEEE binary32 operation, no
+// contraction), with the exact equivalences the kernel relies on:
+//   t = fl(b / fl(k s)); e = E4M3(t).  The kernel forms t' = b * (1/fl(k s))
+//     (within 2^-22 of t) and converts t' (1 -+ 2^-18); when both bounds
+//     give the same E4M3 byte, so does t (rounding is monotone); otherwise
+//     it divides.
+//   r = fl(1 / fl(e s)), looked up in a per-row LDS table of all E4M3 bytes
+//     (the same IEEE division, done once per row instead of per block).
+//   v = fl(x r); q = E2M1(v) with the sign of x.
+//   c = fl(fl(g e) s): g e is exact in FP16 (<= 6 significant bits, between
+//     2^-10 and 2688), so the kernel multiplies in packed FP16 and rounds
+//     ge * s once with v_fma_mix_f32 (addend -0, which leaves every product
+//     unchanged, zeros included).
+//   err = sum over the block, in element order, of fl(fl(x - c)^2).
+// The E2M1, E4M3 and BF16 conversions are the gfx950 conversion
+// instructions, checked exhaustively against the definitions by the tests.
 #include "fp4q_device.h"
 #include "fp4q_launch.h"
 
@@ -29,7 +39,48 @@ namespace fp4q {
 
 namespace {
 
-constexpr int kWaves = 4;  // wavefronts (rows) per workgroup
+// Build-time knob: FP4Q_NV_NT_STORES = 1 writes the outputs with
+// non-temporal stores (they are not re-read by this kernel).
+#ifndef FP4Q_NV_NT_STORES
+#define FP4Q_NV_NT_STORES 1
+#endif
+// Build-time knob: FP4Q_NV_PERSIST = 1 sizes the split grid to the device
+// (workgroups loop over row groups); 0 launches one workgroup per group.
+#ifndef FP4Q_NV_PERSIST
+#define FP4Q_NV_PERSIST 0
+#endif
+// Build-time knob: FP4Q_NV_CONTIG = 1 makes every load and dequant store
+// instruction of a wave cover 1 KiB contiguously (16 bytes per lane); the
+// half-blocks are exchanged between neighbouring lanes with DPP.
+#ifndef FP4Q_NV_CONTIG
+#define FP4Q_NV_CONTIG 0
+#endif
+
+constexpr int kMaxWgWaves = 16;  // rows of up to 16 chunks use the split kernel
+constexpr int kLongWaves = 4;    // rows per workgroup of the long-row kernel
+constexpr int kMaxWavesPerSimd = 8;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_out(uint4* p, uint4 v) {
+  if (FP4Q_NV_NT_STORES)
+    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, (u32x4*)p);
+  else
+    *p = v;
+}
+__device__ __forceinline__ void store_out(uint2* p, uint2 v) {
+  if (FP4Q_NV_NT_STORES)
+    __builtin_nontemporal_store((u32x2){v.x, v.y}, (u32x2*)p);
+  else
+    *p = v;
+}
+__device__ __forceinline__ void store_out(uint8_t* p, uint8_t v) {
+  if (FP4Q_NV_NT_STORES)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -39,125 +90,237 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Wave-wide max of a non-negative value held as its bit pattern.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Wave-wide max of a non-negative value (DPP row shifts, then the row
+// broadcasts; lane 63 ends with the max of all 64 lanes).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
-  return v;
+  v = max(v, dpp<0x111, 0xF>(v));  // row_shr:1
+  v = max(v, dpp<0x112, 0xF>(v));  // row_shr:2
+  v = max(v, dpp<0x114, 0xF>(v));  // row_shr:4
+  v = max(v, dpp<0x118, 0xF>(v));  // row_shr:8
+  v = max(v, dpp<0x142, 0xA>(v));  // row_bcast:15
+  v = max(v, dpp<0x143, 0xC>(v));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Max |x| over one block of 16 BF16 values, as a BF16 magnitude pattern.
-__device__ __forceinline__ uint32_t block_absmax_bits(const uint32_t (&w)[8]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
-  return m;
-}
-
-// Per-row reciprocal table: tab[byte] = 1 / fl(e(byte) * s) for every
-// E4M3 byte 0..127 (0 where the decode step is 0).  Each lane fills two
-// entries; only this wave reads them.
-__device__ __forceinline__ void fill_recip_table(float* tab, float s, int lane) {
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t byte = (uint32_t)lane + 64u * k;
-    const float d = e4m3_decode(byte) * s;
-    tab[byte] = (d != 0.0f) ? 1.0f / d : 0.0f;
-  }
-  __builtin_amdgcn_wave_barrier();
-}
-
-struct Candidate {
-  uint32_t code[2];  // 16 nibbles, element 2i in the low nibble of byte i
-  float err;
-  float c[16];  // signed FP32 candidate values
-};
-
-// One candidate: decode step with value e and reciprocal r under token
-// scale s.
-__device__ __forceinline__ void candidate(const float (&x)[16], float e, float r, float s,
-                                          Candidate& out) {
-  if (__builtin_expect(r <= 3.4028235e38f, 1)) {
-    uint32_t code[2] = {0u, 0u};
-    float err = 0.0f;
-    static_for<0, 8>([&](auto P) {
-      constexpr int p = decltype(P)::value;
-      const float v0 = x[2 * p] * r, v1 = x[2 * p + 1] * r;
-      code[p >> 2] = cvt_e2m1x2<p & 3>(code[p >> 2], v0, v1);
-      const float2v g = e2m1x2_values<p & 3>(code[p >> 2]);
-      const float ge0 = g.x * e, ge1 = g.y * e;  // exact: <= 6 significant bits
-      const float c0 = ge0 * s, c1 = ge1 * s;
-      const float d0 = x[2 * p] - c0, d1 = x[2 * p + 1] - c1;
-      const float q0 = d0 * d0, q1 = d1 * d1;
-      err = err + q0;
-      err = err + q1;
-      out.c[2 * p] = c0;
-      out.c[2 * p + 1] = c1;
-    });
-    out.code[0] = code[0];
-    out.code[1] = code[1];
-    out.err = err;
-  } else {
-    // r = +inf (a decode step below 2^-128): x * r is +-inf for nonzero x
-    // and NaN for zeros, which the portable rounding maps to code 0.
-    uint32_t code[2] = {0u, 0u};
-    float err = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float g;
-      const uint32_t q = e2m1_code_sw(fabsf(x[i]) * r, g);
-      const uint32_t neg = __float_as_uint(x[i]) >> 31;
-      const float ge = g * e;
-      float c = ge * s;
-      c = neg ? -c : c;
-      const float d = x[i] - c;
-      const float sq = d * d;
-      err = err + sq;
-      code[i >> 3] |= (q | (neg << 3)) << (4 * (i & 7));
-      out.c[i] = c;
-    }
-    out.code[0] = code[0];
-    out.code[1] = code[1];
-    out.err = err;
-  }
-}
-
-template <bool FOS, bool DQ>
-__device__ __forceinline__ void quantize_block(const uint32_t (&w)[8], uint32_t bbits, float s,
-                                               float ks6, float ks4, const float* tab,
-                                               int64_t blk, uint2* __restrict__ codes,
-                                               uint8_t* __restrict__ scales,
-                                               uint4* __restrict__ dq) {
-  float x[16];
+__device__ __forceinline__ void unpack16(const uint32_t (&w)[8], float (&x)[16]) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     x[2 * k] = bf16_lo(w[k]);
     x[2 * k + 1] = bf16_hi(w[k]);
   }
-  const float b = __uint_as_float(bbits << 16);
-  // both candidate block scales in one conversion (byte 0: map to 6,
-  // byte 1: map to 4); E4M3 saturates at 448
-  const float t6 = fminf(b / ks6, 448.0f);
-  const float t4 = FOS ? fminf(b / ks4, 448.0f) : 0.0f;
-  const uint32_t eb = cvt_e4m3x2(t6, t4);
+}
 
-  Candidate c6;
-  candidate(x, e4m3_value<0>(eb), tab[eb & 0xFFu], s, c6);
-  bool four = false;
-  Candidate c4;
-  if (FOS) {
-    candidate(x, e4m3_value<1>(eb), tab[eb >> 8], s, c4);
-    four = c4.err < c6.err;  // strictly lower error: 4 wins; ties keep 6
-  }
-  codes[blk] = four ? make_uint2(c4.code[0], c4.code[1]) : make_uint2(c6.code[0], c6.code[1]);
-  scales[blk] = (uint8_t)(four ? (eb >> 8) : (eb & 0xFFu));
-  if (DQ) {
-    uint32_t o[8];
+// Max |x| of a block as the bit pattern of a non-negative float: a packed
+// 16-bit max over the sign-cleared BF16 patterns (for non-negative values
+// the integer order is the value order).
+__device__ __forceinline__ uint32_t block_absmax_bits(const uint32_t (&w)[8]) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      o[k] = cvt_bf16x2(four ? c4.c[2 * k] : c6.c[2 * k], four ? c4.c[2 * k + 1] : c6.c[2 * k + 1]);
-    dq[2 * blk] = make_uint4(o[0], o[1], o[2], o[3]);
-    dq[2 * blk + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+  for (int k = 0; k < 8; ++k) m[k] = __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int n = 4; n >= 1; n >>= 1)
+#pragma unroll
+    for (int k = 0; k < n; ++k) m[k] = __builtin_elementwise_max(m[k], m[k + n]);
+  return (uint32_t)max(m[0].x, m[0].y) << 16;
+}
+
+// Per-row constants.
+struct RowScale {
+  float s;           // token scale, stored
+  float ks6, ks4;    // fl(6 s), fl(4 s); 1 for a zero row (so b / ks = 0)
+  float rks6, rks4;  // approximate reciprocals for the bracketed block scale
+  bool fast;         // every decode step e s is 0 or >= 2^-127
+};
+
+template <bool FOS>
+__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
+  RowScale r;
+  r.s = __uint_as_float(amax_bits) / (FOS ? 1536.0f : 2688.0f);
+  r.ks6 = (r.s != 0.0f) ? 6.0f * r.s : 1.0f;
+  r.ks4 = (r.s != 0.0f) ? 4.0f * r.s : 1.0f;
+  r.rks6 = __builtin_amdgcn_rcpf(r.ks6);
+  r.rks4 = __builtin_amdgcn_rcpf(r.ks4);
+  // s >= 2^-118: ks >= 2^-116 so 1/ks is normal, and the smallest decode
+  // step 2^-9 s >= 2^-127 has a finite reciprocal.
+  r.fast = r.s >= 0x1p-118f || r.s == 0.0f;
+  return r;
+}
+
+// tab[byte] = 1 / fl(e(byte) s) for the E4M3 bytes this lane covers.
+__device__ __forceinline__ void fill_recip(float* tab, float s, int first, int step) {
+  for (int byte = first; byte < 128; byte += step) {
+    const float d = e4m3_value<0>((uint32_t)byte) * s;
+    tab[byte] = (d != 0.0f) ? 1.0f / d : 0.0f;
+  }
+}
+
+struct Candidate {
+  uint32_t code[2];  // 16 nibbles, element 2i in the low nibble of byte i
+  float err;
+  uint32_t deq[8];   // the candidate values rounded to BF16, two per word
+};
+
+// One candidate on the fast path: decode step e, finite reciprocal r.
+template <bool DQ>
+__device__ __forceinline__ void candidate(const float (&x)[16], float e, float r, float s,
+                                          float neg_zero, Candidate& out) {
+  uint32_t code[2] = {0u, 0u};
+  float err = 0.0f;
+  const _Float16 eh = (_Float16)e;  // exact: E4M3 values are FP16 numbers
+  const half2v e2 = {eh, eh};
+  static_for<0, 8>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    const float v0 = x[2 * p] * r, v1 = x[2 * p + 1] * r;
+    code[p >> 2] = cvt_e2m1x2<p & 3>(code[p >> 2], v0, v1);
+    const half2v ge = e2m1x2_values_f16<p & 3>(code[p >> 2]) * e2;  // exact
+    const float c0 = __builtin_fmaf((float)ge.x, s, neg_zero);     // fl(ge s)
+    const float c1 = __builtin_fmaf((float)ge.y, s, neg_zero);
+    const float d0 = x[2 * p] - c0, d1 = x[2 * p + 1] - c1;
+    const float q0 = d0 * d0, q1 = d1 * d1;
+    err = err + q0;
+    err = err + q1;
+    if (DQ) {
+      uint32_t pair = cvt_bf16x2(c0, c1);
+      asm volatile("" : "+v"(pair));  // keep the BF16 pair: select words, not floats
+      out.deq[p] = pair;
+    }
+  });
+  out.code[0] = code[0];
+  out.code[1] = code[1];
+  out.err = err;
+}
+
+// One element of a candidate by the portable definition: |x| r may be
+// +inf (code 7) or NaN (0 * inf, code 0).  Returns the nibble and the FP32
+// candidate value.
+__device__ __forceinline__ uint32_t element_portable(float x, float e, float r, float s,
+                                                     float& c) {
+  const uint32_t neg = __float_as_uint(x) >> 31;
+  float g;
+  const uint32_t q = e2m1_code_sw(fabsf(x) * r, g);
+  const float ge = g * e;
+  c = ge * s;
+  c = neg ? -c : c;
+  return q | (neg << 3);
+}
+
+// Rows with s < 2^-118 (row amax below about 2^-107): decode steps may be
+// subnormal and their reciprocals infinite, so the block follows the
+// definition step by step -- exact division for the block scale, portable
+// rounding -- in loops that re-read the block from memory.  Nothing here
+// stays live across the hot path, so it costs the common case no registers.
+template <bool FOS, bool DQ>
+__device__ __attribute__((noinline)) void tiny_row_block(const uint16_t* __restrict__ xb,
+                                                         float b, const float* tab, float s,
+                                                         uint8_t* __restrict__ code_bytes,
+                                                         uint8_t* __restrict__ scale,
+                                                         uint16_t* __restrict__ dqb) {
+  float best_err = 0.0f, best_e = 0.0f, best_r = 0.0f;
+  uint32_t best_byte = 0u;
+#pragma unroll 1
+  for (int k = 0; k < (FOS ? 2 : 1); ++k) {
+    float e = 0.0f;
+    uint32_t byte = 0u;
+    if (b != 0.0f) byte = e4m3_encode(b / ((k == 0 ? 6.0f : 4.0f) * s), e);
+    const float r = tab[byte];
+    float err = 0.0f;
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      const float xi = __uint_as_float((uint32_t)xb[i] << 16);
+      float c;
+      element_portable(xi, e, r, s, c);
+      const float d = xi - c;
+      const float sq = d * d;
+      err = err + sq;
+    }
+    if (k == 0 || err < best_err) {  // strictly lower error: 4 wins
+      best_err = err;
+      best_e = e;
+      best_r = r;
+      best_byte = byte;
+    }
+  }
+  *scale = (uint8_t)best_byte;
+#pragma unroll 1
+  for (int i = 0; i < 16; i += 2) {
+    float c0, c1;
+    const uint32_t n0 =
+        element_portable(__uint_as_float((uint32_t)xb[i] << 16), best_e, best_r, s, c0);
+    const uint32_t n1 =
+        element_portable(__uint_as_float((uint32_t)xb[i + 1] << 16), best_e, best_r, s, c1);
+    code_bytes[i / 2] = (uint8_t)(n0 | (n1 << 4));
+    if (DQ) {
+      const uint32_t pair = cvt_bf16x2(c0, c1);
+      dqb[i] = (uint16_t)pair;
+      dqb[i + 1] = (uint16_t)(pair >> 16);
+    }
+  }
+}
+
+// Outputs of one block on the fast path.
+struct BlockOut {
+  uint32_t code0, code1, ebyte;
+  uint32_t deq[8];
+};
+
+template <bool FOS, bool DQ>
+__device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32_t bbits,
+                                                    const RowScale& rs, const float* tab,
+                                                    float neg_zero, BlockOut& out) {
+  const float b = __uint_as_float(bbits);
+  // bracketed block scales for both candidates (byte 0: map to 6, byte 1:
+  // map to 4)
+  const float t6 = b * rs.rks6, t4 = FOS ? b * rs.rks4 : 0.0f;
+  const uint32_t lo = cvt_e4m3x2(t6 * (1.0f - 0x1p-18f), t4 * (1.0f - 0x1p-18f));
+  uint32_t eb = cvt_e4m3x2(t6 * (1.0f + 0x1p-18f), t4 * (1.0f + 0x1p-18f));
+  if (__builtin_expect(lo != eb, 0))
+    eb = cvt_e4m3x2(fminf(b / rs.ks6, 448.0f), FOS ? fminf(b / rs.ks4, 448.0f) : 0.0f);
+  Candidate c6;
+  candidate<DQ>(x, e4m3_value<0>(eb), tab[eb & 0xFFu], rs.s, neg_zero, c6);
+  out.code0 = c6.code[0];
+  out.code1 = c6.code[1];
+  out.ebyte = eb & 0xFFu;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out.deq[k] = c6.deq[k];
+  if (FOS) {
+    Candidate c4;
+    candidate<DQ>(x, e4m3_value<1>(eb), tab[eb >> 8], rs.s, neg_zero, c4);
+    const bool four = c4.err < c6.err;  // strictly lower error: 4 wins; ties keep 6
+    out.code0 = four ? c4.code[0] : out.code0;
+    out.code1 = four ? c4.code[1] : out.code1;
+    out.ebyte = four ? (eb >> 8) : out.ebyte;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out.deq[k] = four ? c4.deq[k] : out.deq[k];
+  }
+}
+
+// One block, written directly (one lane, 32 contiguous dequant bytes).
+template <bool FOS, bool DQ>
+__device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bbits,
+                                               const RowScale& rs, const float* tab,
+                                               float neg_zero, const uint4* __restrict__ xin,
+                                               int64_t blk, uint2* __restrict__ codes,
+                                               uint8_t* __restrict__ scales,
+                                               uint4* __restrict__ dq) {
+  if (__builtin_expect(!rs.fast, 0)) {
+    tiny_row_block<FOS, DQ>((const uint16_t*)(xin + 2 * blk), __uint_as_float(bbits), tab, rs.s,
+                            (uint8_t*)(codes + blk), scales + blk,
+                            DQ ? (uint16_t*)(dq + 2 * blk) : nullptr);
+    return;
+  }
+  BlockOut o;
+  quantize_block_fast<FOS, DQ>(x, bbits, rs, tab, neg_zero, o);
+  store_out(&codes[blk], make_uint2(o.code0, o.code1));
+  store_out(&scales[blk], (uint8_t)o.ebyte);
+  if (DQ) {
+    store_out(&dq[2 * blk], make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]));
+    store_out(&dq[2 * blk + 1], make_uint4(o.deq[4], o.deq[5], o.deq[6], o.deq[7]));
   }
 }
 
@@ -171,104 +334,195 @@ __device__ __forceinline__ bool row_range(int64_t row, int64_t rows, const int64
   return row >= lo && row < hi;
 }
 
-// Token scale and the per-row constants: ks = fl(k s); a zero row uses 1
-// so that b / ks = 0 / 1 gives a zero block scale.
-template <bool FOS>
-__device__ __forceinline__ float token_scale(uint32_t amax_bits, float& ks6, float& ks4) {
-  const float amax = __uint_as_float(amax_bits << 16);
-  const float s = amax / (FOS ? 1536.0f : 2688.0f);
-  ks6 = (s != 0.0f) ? 6.0f * s : 1.0f;
-  ks4 = (s != 0.0f) ? 4.0f * s : 1.0f;
-  return s;
+__device__ __forceinline__ void load_block(const uint4* __restrict__ x, int64_t blk,
+                                           uint32_t (&w)[8]) {
+  const uint4 a = x[2 * blk], b = x[2 * blk + 1];
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
-// Register-resident row: nblk <= 64 * CH.
-template <int CH, bool FOS, bool DQ>
-__global__ __launch_bounds__(64 * kWaves) void nvfp4_quantize_rows(
-    const uint4* __restrict__ x, int64_t rows, int nblk, const int64_t* __restrict__ offs,
-    int64_t ngroups, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ tscale, uint4* __restrict__ dq) {
-  __shared__ float recip[kWaves][128];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  if (!row_range(row, rows, offs, ngroups)) return;
-
-  const int64_t base = row * nblk;  // first block of the row
-  uint32_t w[CH][8];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int j = c * 64 + lane;
-    uint4 a = make_uint4(0, 0, 0, 0), bq = a;
-    if (j < nblk) {
-      a = x[2 * (base + j)];
-      bq = x[2 * (base + j) + 1];
-    }
-    w[c][0] = a.x; w[c][1] = a.y; w[c][2] = a.z; w[c][3] = a.w;
-    w[c][4] = bq.x; w[c][5] = bq.y; w[c][6] = bq.z; w[c][7] = bq.w;
-  }
-
-  uint32_t bmax[CH];
-  uint32_t lmax = 0;
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    bmax[c] = block_absmax_bits(w[c]);
-    lmax = max(lmax, bmax[c]);
-  }
-  float ks6, ks4;
-  const float s = token_scale<FOS>(wave_max_u32(lmax), ks6, ks4);
-  if (lane == 0) tscale[row] = s;
-  fill_recip_table(recip[wave], s, lane);
-
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int j = c * 64 + lane;
-    if (j < nblk)
-      quantize_block<FOS, DQ>(w[c], bmax[c], s, ks6, ks4, recip[wave], base + j, codes, scales,
-                              dq);
-  }
+// Neighbour-lane exchange: lane 2m receives lane 2m+1's value and vice
+// versa (DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ uint32_t swap_pairs(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
 
-// Any row length: a first pass for the amax, a second pass (served mostly
-// by L2) for the blocks.
+// Split rows: a workgroup holds R rows x W wavefronts; wave c of a row owns
+// chunk c (64 blocks) of it, one block per lane.  The row amax is combined
+// across the W waves through LDS; waves 0 and 1 of the row derive the row
+// constants and fill the reciprocal table, which the others read back.
+//
+// The grid is persistent: workgroup g handles row groups g, g + G, g + 2G,
+// ... of the active row range, and every wave issues the loads of its next
+// row group before it works on the current one, so each wave keeps a load
+// in flight through the amax exchange and the block arithmetic.
+//
+// Block of a lane: with FP4Q_NV_CONTIG the wave loads the chunk as two
+// contiguous 1 KiB halves (16 bytes per lane); lane 2m then owns block m
+// and lane 2m+1 block 32+m after a neighbour exchange of half-blocks, and
+// the dequant leaves the same way.  Otherwise lane l owns block l and reads
+// and writes its 32 bytes directly.
+struct ChunkData {
+  uint4 a, b;
+};
+
+__device__ __forceinline__ ChunkData load_chunk(const uint4* __restrict__ x, int64_t cbase,
+                                                int valid, int lane) {
+  ChunkData d;
+  d.a = make_uint4(0, 0, 0, 0);
+  d.b = d.a;
+  if (FP4Q_NV_CONTIG) {
+    if ((lane >> 1) < valid) d.a = x[2 * cbase + lane];
+    if (32 + (lane >> 1) < valid) d.b = x[2 * cbase + 64 + lane];
+  } else if (lane < valid) {
+    d.a = x[2 * (cbase + lane)];
+    d.b = x[2 * (cbase + lane) + 1];
+  }
+  return d;
+}
+
 template <bool FOS, bool DQ>
-__global__ __launch_bounds__(64 * kWaves) void nvfp4_quantize_long_rows(
+__global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
+    const uint4* __restrict__ x, int64_t rows, int nblk, int W, int R,
+    const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
+    float neg_zero) {
+  __shared__ uint32_t wave_max[kMaxWgWaves];
+  __shared__ float recip[kMaxWgWaves][128];
+  __shared__ RowScale rowinfo[kMaxWgWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
+  const bool odd = lane & 1;
+  const int j = FP4Q_NV_CONTIG ? (odd ? 32 + (lane >> 1) : (lane >> 1)) : lane;
+
+  int64_t lo = 0, hi = rows;  // active row range (ragged groups)
+  if (offs != nullptr) {
+    lo = max(offs[0], (int64_t)0);
+    hi = min(offs[ngroups], rows);
+  }
+  const int64_t step = (int64_t)gridDim.x * R;
+  int64_t row = lo + (int64_t)blockIdx.x * R + rw;
+  // rows handled by this workgroup (the same count for all of its waves)
+  int64_t first = lo + (int64_t)blockIdx.x * R;
+
+  auto chunk_valid = [&](int64_t r) -> int {
+    return r < hi ? min(64, nblk - chunk * 64) : 0;
+  };
+  ChunkData next = load_chunk(x, row * nblk + chunk * 64, chunk_valid(row), lane);
+
+  for (; first < hi; first += step, row += step) {
+    const int valid = chunk_valid(row);
+    const int64_t cbase = row * nblk + chunk * 64;
+    const ChunkData cur = next;
+    next = load_chunk(x, (row + step) * nblk + chunk * 64, chunk_valid(row + step), lane);
+
+    uint32_t w[8];
+    if (FP4Q_NV_CONTIG) {
+      const uint32_t A[4] = {cur.a.x, cur.a.y, cur.a.z, cur.a.w};
+      const uint32_t B[4] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t recv = swap_pairs(odd ? A[k] : B[k]);
+        w[k] = odd ? recv : A[k];
+        w[4 + k] = odd ? B[k] : recv;
+      }
+    } else {
+      w[0] = cur.a.x; w[1] = cur.a.y; w[2] = cur.a.z; w[3] = cur.a.w;
+      w[4] = cur.b.x; w[5] = cur.b.y; w[6] = cur.b.z; w[7] = cur.b.w;
+    }
+    const uint32_t bmax = block_absmax_bits(w);
+    const uint32_t m = wave_max_u32(bmax);
+    if (lane == 0) wave_max[wave] = m;
+    __syncthreads();
+    if (chunk < 2) {
+      uint32_t amax_bits = 0;
+      for (int c = 0; c < W; ++c) amax_bits = max(amax_bits, wave_max[rw * W + c]);
+      const RowScale rs = row_scale<FOS>(amax_bits);
+      if (chunk == 0 && lane == 0) {
+        rowinfo[rw] = rs;
+        if (row < hi) tscale[row] = rs.s;
+      }
+      fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
+    }
+    __syncthreads();
+    const RowScale rs = rowinfo[rw];
+    float xv[16];
+    unpack16(w, xv);
+    const bool has = j < valid;
+    const int64_t blk = cbase + j;
+    if (!FP4Q_NV_CONTIG || __builtin_expect(!rs.fast, 0)) {
+      if (has)
+        quantize_block<FOS, DQ>(xv, bmax, rs, recip[rw], neg_zero, x, blk, codes, scales, dq);
+      continue;
+    }
+    BlockOut o;
+    quantize_block_fast<FOS, DQ>(xv, bmax, rs, recip[rw], neg_zero, o);
+    if (has) {
+      store_out(&codes[blk], make_uint2(o.code0, o.code1));
+      store_out(&scales[blk], (uint8_t)o.ebyte);
+    }
+    if (DQ) {
+      // back to contiguous halves: lane 2m stores the first halves, lane
+      // 2m+1 the second halves, of blocks m (first KiB) and 32+m (second)
+      uint32_t h1[4], h2[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t recv = swap_pairs(odd ? o.deq[k] : o.deq[4 + k]);
+        h1[k] = odd ? recv : o.deq[k];
+        h2[k] = odd ? o.deq[4 + k] : recv;
+      }
+      if ((lane >> 1) < valid)
+        store_out(&dq[2 * cbase + lane], make_uint4(h1[0], h1[1], h1[2], h1[3]));
+      if (32 + (lane >> 1) < valid)
+        store_out(&dq[2 * cbase + 64 + lane], make_uint4(h2[0], h2[1], h2[2], h2[3]));
+    }
+  }
+}
+
+// Any row length: one wavefront per row; a first pass for the amax, a
+// second pass (served mostly by L2) for the blocks.
+template <bool FOS, bool DQ>
+__global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     const uint4* __restrict__ x, int64_t rows, int nblk, const int64_t* __restrict__ offs,
     int64_t ngroups, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ tscale, uint4* __restrict__ dq) {
-  __shared__ float recip[kWaves][128];
+    float* __restrict__ tscale, uint4* __restrict__ dq, float neg_zero) {
+  __shared__ float recip[kLongWaves][128];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  if (!row_range(row, rows, offs, ngroups)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * kLongWaves + wave;
+  if (row >= rows || !row_range(row, rows, offs, ngroups)) return;
   const int64_t base = row * nblk;
 
   uint32_t lmax = 0;
   for (int j = lane; j < nblk; j += 64) {
-    const uint4 a = x[2 * (base + j)], bq = x[2 * (base + j) + 1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+    uint32_t w[8];
+    load_block(x, base + j, w);
     lmax = max(lmax, block_absmax_bits(w));
   }
-  float ks6, ks4;
-  const float s = token_scale<FOS>(wave_max_u32(lmax), ks6, ks4);
-  if (lane == 0) tscale[row] = s;
-  fill_recip_table(recip[wave], s, lane);
+  const RowScale rs = row_scale<FOS>(wave_max_u32(lmax));
+  if (lane == 0) tscale[row] = rs.s;
+  fill_recip(recip[wave], rs.s, lane, 64);
+  __builtin_amdgcn_wave_barrier();
   for (int j = lane; j < nblk; j += 64) {
-    const uint4 a = x[2 * (base + j)], bq = x[2 * (base + j) + 1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-    quantize_block<FOS, DQ>(w, block_absmax_bits(w), s, ks6, ks4, recip[wave], base + j, codes,
-                            scales, dq);
+    uint32_t w[8];
+    float xv[16];
+    load_block(x, base + j, w);
+    unpack16(w, xv);
+    quantize_block<FOS, DQ>(xv, block_absmax_bits(w), rs, recip[wave], neg_zero, x, base + j,
+                            codes, scales, dq);
   }
 }
 
-// K2: one lane per 16-element block.
+// K2: one lane per 16-element block, the candidate formula on the stored
+// values.
 __global__ __launch_bounds__(256) void nvfp4_dequantize_blocks(
     const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tscale, int64_t nblocks, int nblk, uint4* __restrict__ out) {
   const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (blk >= nblocks) return;
   const float s = tscale[blk / nblk];
-  const float e = e4m3_decode(scales[blk]);
+  const float e = e4m3_value<0>(scales[blk]);
   const uint2 cw = codes[blk];
   uint32_t o[8];
   static_for<0, 8>([&](auto P) {
@@ -281,35 +535,46 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_blocks(
   out[2 * blk + 1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Workgroups that fit on the device at once for the split kernel, capped
+// by the work available.
+int64_t persistent_groups(int waves_per_group, int64_t row_groups) {
+  static int cu_count[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cu_count[dev] = n;
+  }
+  const int per_cu = max(1, (4 * kMaxWavesPerSimd) / waves_per_group);
+  const int64_t cap = (int64_t)cu_count[dev] * per_cu;
+  return row_groups < cap ? row_groups : cap;
+}
+
 template <bool FOS, bool DQ>
 hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const int nblk = (int)(a.hidden / 16);
-  const dim3 grid((unsigned)((a.rows + kWaves - 1) / kWaves)), block(64 * kWaves);
   const uint4* x = (const uint4*)a.x;
   uint2* codes = (uint2*)a.codes;
   uint4* dq = (uint4*)a.dequant;
-  const int ch = (nblk + 63) / 64;
-#define FP4Q_ROWS(CHN)                                                                       \
-  case CHN:                                                                                   \
-    hipLaunchKernelGGL((nvfp4_quantize_rows<CHN, FOS, DQ>), grid, block, 0, st, x, a.rows,  \
-                       nblk, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, \
-                       dq);                                                                   \
-    break;
-  switch (ch) {
-    FP4Q_ROWS(1)
-    FP4Q_ROWS(2)
-    FP4Q_ROWS(3)
-    FP4Q_ROWS(4)
-    FP4Q_ROWS(5)
-    FP4Q_ROWS(6)
-    FP4Q_ROWS(7)
-    FP4Q_ROWS(8)
-    default:
-      hipLaunchKernelGGL((nvfp4_quantize_long_rows<FOS, DQ>), grid, block, 0, st, x, a.rows,
-                         nblk, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales,
-                         dq);
+  const float neg_zero = -0.0f;
+  const int W = (nblk + 63) / 64;  // waves per row
+  if (W <= kMaxWgWaves) {
+    const int R = W >= 8 ? 1 : 8 / W;  // rows per workgroup
+    const int64_t row_groups = (a.rows + R - 1) / R;
+    const int64_t groups = FP4Q_NV_PERSIST ? persistent_groups(W * R, row_groups) : row_groups;
+    const dim3 grid((unsigned)groups), block(64 * W * R);
+    hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ>), grid, block, 0, st, x, a.rows, nblk, W,
+                       R, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
+                       neg_zero);
+  } else {
+    const dim3 grid((unsigned)((a.rows + kLongWaves - 1) / kLongWaves)), block(64 * kLongWaves);
+    hipLaunchKernelGGL((nvfp4_quantize_long_rows<FOS, DQ>), grid, block, 0, st, x, a.rows, nblk,
+                       a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
+                       neg_zero);
   }
-#undef FP4Q_ROWS
   return hipGetLastError();
 }
 
