@@ -44,21 +44,20 @@ namespace {
 #ifndef FP4Q_NV_NT_STORES
 #define FP4Q_NV_NT_STORES 1
 #endif
-// Build-time knob: FP4Q_NV_PERSIST = 1 sizes the split grid to the device
-// (workgroups loop over row groups); 0 launches one workgroup per group.
-#ifndef FP4Q_NV_PERSIST
-#define FP4Q_NV_PERSIST 0
+
+// Build-time knob: FP4Q_NV_LDS_DQ = 1 stages each wave's dequant chunk
+// through LDS so that every dequant store instruction writes 1 KiB
+// contiguously (16 bytes per lane); 0 stores each lane's 32 bytes directly.
+#ifndef FP4Q_NV_LDS_DQ
+#define FP4Q_NV_LDS_DQ 1
 #endif
-// Build-time knob: FP4Q_NV_CONTIG = 1 makes every load and dequant store
-// instruction of a wave cover 1 KiB contiguously (16 bytes per lane); the
-// half-blocks are exchanged between neighbouring lanes with DPP.
-#ifndef FP4Q_NV_CONTIG
-#define FP4Q_NV_CONTIG 0
+// Build-time knob: blocks per lane in the split kernel (1 or 2).
+#ifndef FP4Q_NV_NB
+#define FP4Q_NV_NB 2
 #endif
 
-constexpr int kMaxWgWaves = 16;  // rows of up to 16 chunks use the split kernel
+constexpr int kMaxWgWaves = 16;  // rows of up to 16 waves use the split kernel
 constexpr int kLongWaves = 4;    // rows per workgroup of the long-row kernel
-constexpr int kMaxWavesPerSimd = 8;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -307,7 +306,8 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
                                                float neg_zero, const uint4* __restrict__ xin,
                                                int64_t blk, uint2* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
-                                               uint4* __restrict__ dq) {
+                                               uint4* __restrict__ dq,
+                                               uint4* stage = nullptr) {
   if (__builtin_expect(!rs.fast, 0)) {
     tiny_row_block<FOS, DQ>((const uint16_t*)(xin + 2 * blk), __uint_as_float(bbits), tab, rs.s,
                             (uint8_t*)(codes + blk), scales + blk,
@@ -319,8 +319,13 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
   store_out(&codes[blk], make_uint2(o.code0, o.code1));
   store_out(&scales[blk], (uint8_t)o.ebyte);
   if (DQ) {
-    store_out(&dq[2 * blk], make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]));
-    store_out(&dq[2 * blk + 1], make_uint4(o.deq[4], o.deq[5], o.deq[6], o.deq[7]));
+    if (stage != nullptr) {  // the caller writes the chunk out contiguously
+      stage[0] = make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]);
+      stage[1] = make_uint4(o.deq[4], o.deq[5], o.deq[6], o.deq[7]);
+    } else {
+      store_out(&dq[2 * blk], make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]));
+      store_out(&dq[2 * blk + 1], make_uint4(o.deq[4], o.deq[5], o.deq[6], o.deq[7]));
+    }
   }
 }
 
@@ -341,47 +346,14 @@ __device__ __forceinline__ void load_block(const uint4* __restrict__ x, int64_t 
   w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
-// Neighbour-lane exchange: lane 2m receives lane 2m+1's value and vice
-// versa (DPP quad_perm [1,0,3,2]).
-__device__ __forceinline__ uint32_t swap_pairs(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-}
-
 // Split rows: a workgroup holds R rows x W wavefronts; wave c of a row owns
-// chunk c (64 blocks) of it, one block per lane.  The row amax is combined
-// across the W waves through LDS; waves 0 and 1 of the row derive the row
-// constants and fill the reciprocal table, which the others read back.
-//
-// The grid is persistent: workgroup g handles row groups g, g + G, g + 2G,
-// ... of the active row range, and every wave issues the loads of its next
-// row group before it works on the current one, so each wave keeps a load
-// in flight through the amax exchange and the block arithmetic.
-//
-// Block of a lane: with FP4Q_NV_CONTIG the wave loads the chunk as two
-// contiguous 1 KiB halves (16 bytes per lane); lane 2m then owns block m
-// and lane 2m+1 block 32+m after a neighbour exchange of half-blocks, and
-// the dequant leaves the same way.  Otherwise lane l owns block l and reads
-// and writes its 32 bytes directly.
-struct ChunkData {
-  uint4 a, b;
-};
-
-__device__ __forceinline__ ChunkData load_chunk(const uint4* __restrict__ x, int64_t cbase,
-                                                int valid, int lane) {
-  ChunkData d;
-  d.a = make_uint4(0, 0, 0, 0);
-  d.b = d.a;
-  if (FP4Q_NV_CONTIG) {
-    if ((lane >> 1) < valid) d.a = x[2 * cbase + lane];
-    if (32 + (lane >> 1) < valid) d.b = x[2 * cbase + 64 + lane];
-  } else if (lane < valid) {
-    d.a = x[2 * (cbase + lane)];
-    d.b = x[2 * (cbase + lane) + 1];
-  }
-  return d;
-}
-
-template <bool FOS, bool DQ>
+// chunk c of it -- 64 * NB consecutive blocks, lane l taking blocks l and
+// l + 64 (NB = 2) -- so each lane quantizes NB blocks per pass.  The row
+// amax is combined across the W waves through LDS; waves 0 and 1 of the row
+// derive the row constants and fill the reciprocal table, which the others
+// read back.  Row and chunk are wave-uniform, so all addressing is scalar
+// base + 32-bit lane offset.
+template <bool FOS, bool DQ, int NB>
 __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     const uint4* __restrict__ x, int64_t rows, int nblk, int W, int R,
     const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
@@ -390,93 +362,67 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   __shared__ uint32_t wave_max[kMaxWgWaves];
   __shared__ float recip[kMaxWgWaves][128];
   __shared__ RowScale rowinfo[kMaxWgWaves];
+  // dequant staging: per wave, 64 blocks x 32 bytes
+  __shared__ uint4 dq_stage[FP4Q_NV_LDS_DQ && DQ && NB == 1 ? kMaxWgWaves : 1][128];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
-  const bool odd = lane & 1;
-  const int j = FP4Q_NV_CONTIG ? (odd ? 32 + (lane >> 1) : (lane >> 1)) : lane;
+  const int64_t row = (int64_t)blockIdx.x * R + rw;
+  const bool active = row < rows && row_range(row, rows, offs, ngroups);
+  // blocks of this wave's chunk that exist (0 for an inactive row)
+  const int valid = active ? min(64 * NB, nblk - chunk * 64 * NB) : 0;
+  const int64_t cbase = row * nblk + (int64_t)chunk * 64 * NB;  // uniform
+  const uint4* xc = x + 2 * cbase;
 
-  int64_t lo = 0, hi = rows;  // active row range (ragged groups)
-  if (offs != nullptr) {
-    lo = max(offs[0], (int64_t)0);
-    hi = min(offs[ngroups], rows);
-  }
-  const int64_t step = (int64_t)gridDim.x * R;
-  int64_t row = lo + (int64_t)blockIdx.x * R + rw;
-  // rows handled by this workgroup (the same count for all of its waves)
-  int64_t first = lo + (int64_t)blockIdx.x * R;
-
-  auto chunk_valid = [&](int64_t r) -> int {
-    return r < hi ? min(64, nblk - chunk * 64) : 0;
-  };
-  ChunkData next = load_chunk(x, row * nblk + chunk * 64, chunk_valid(row), lane);
-
-  for (; first < hi; first += step, row += step) {
-    const int valid = chunk_valid(row);
-    const int64_t cbase = row * nblk + chunk * 64;
-    const ChunkData cur = next;
-    next = load_chunk(x, (row + step) * nblk + chunk * 64, chunk_valid(row + step), lane);
-
-    uint32_t w[8];
-    if (FP4Q_NV_CONTIG) {
-      const uint32_t A[4] = {cur.a.x, cur.a.y, cur.a.z, cur.a.w};
-      const uint32_t B[4] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w};
+  uint32_t w[NB][8];
+  uint32_t bmax[NB];
+  uint32_t lmax = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t recv = swap_pairs(odd ? A[k] : B[k]);
-        w[k] = odd ? recv : A[k];
-        w[4 + k] = odd ? B[k] : recv;
-      }
+  for (int n = 0; n < NB; ++n) {
+    const int j = lane + 64 * n;
+    if (64 * n < valid) {  // wave-uniform: the block slot exists for some lane
+      const int jj = min(j, valid - 1);  // in-bounds for every lane
+      load_block(xc, jj, w[n]);
+      bmax[n] = j < valid ? block_absmax_bits(w[n]) : 0u;
     } else {
-      w[0] = cur.a.x; w[1] = cur.a.y; w[2] = cur.a.z; w[3] = cur.a.w;
-      w[4] = cur.b.x; w[5] = cur.b.y; w[6] = cur.b.z; w[7] = cur.b.w;
-    }
-    const uint32_t bmax = block_absmax_bits(w);
-    const uint32_t m = wave_max_u32(bmax);
-    if (lane == 0) wave_max[wave] = m;
-    __syncthreads();
-    if (chunk < 2) {
-      uint32_t amax_bits = 0;
-      for (int c = 0; c < W; ++c) amax_bits = max(amax_bits, wave_max[rw * W + c]);
-      const RowScale rs = row_scale<FOS>(amax_bits);
-      if (chunk == 0 && lane == 0) {
-        rowinfo[rw] = rs;
-        if (row < hi) tscale[row] = rs.s;
-      }
-      fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
-    }
-    __syncthreads();
-    const RowScale rs = rowinfo[rw];
-    float xv[16];
-    unpack16(w, xv);
-    const bool has = j < valid;
-    const int64_t blk = cbase + j;
-    if (!FP4Q_NV_CONTIG || __builtin_expect(!rs.fast, 0)) {
-      if (has)
-        quantize_block<FOS, DQ>(xv, bmax, rs, recip[rw], neg_zero, x, blk, codes, scales, dq);
-      continue;
-    }
-    BlockOut o;
-    quantize_block_fast<FOS, DQ>(xv, bmax, rs, recip[rw], neg_zero, o);
-    if (has) {
-      store_out(&codes[blk], make_uint2(o.code0, o.code1));
-      store_out(&scales[blk], (uint8_t)o.ebyte);
-    }
-    if (DQ) {
-      // back to contiguous halves: lane 2m stores the first halves, lane
-      // 2m+1 the second halves, of blocks m (first KiB) and 32+m (second)
-      uint32_t h1[4], h2[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t recv = swap_pairs(odd ? o.deq[k] : o.deq[4 + k]);
-        h1[k] = odd ? recv : o.deq[k];
-        h2[k] = odd ? o.deq[4 + k] : recv;
-      }
-      if ((lane >> 1) < valid)
-        store_out(&dq[2 * cbase + lane], make_uint4(h1[0], h1[1], h1[2], h1[3]));
-      if (32 + (lane >> 1) < valid)
-        store_out(&dq[2 * cbase + 64 + lane], make_uint4(h2[0], h2[1], h2[2], h2[3]));
+      for (int k = 0; k < 8; ++k) w[n][k] = 0u;
+      bmax[n] = 0u;
     }
+    lmax = max(lmax, bmax[n]);
+  }
+  const uint32_t m = wave_max_u32(lmax);
+  if (lane == 0) wave_max[wave] = m;
+  __syncthreads();
+  if (chunk < 2) {
+    uint32_t amax_bits = 0;
+    for (int c = 0; c < W; ++c) amax_bits = max(amax_bits, wave_max[rw * W + c]);
+    const RowScale rs = row_scale<FOS>(amax_bits);
+    if (chunk == 0 && lane == 0) {
+      rowinfo[rw] = rs;
+      if (active) tscale[row] = rs.s;
+    }
+    fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
+  }
+  __syncthreads();
+  const RowScale rs = rowinfo[rw];
+  constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ && NB == 1;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int j = lane + 64 * n;
+    if (64 * n < valid && j < valid) {
+      float xv[16];
+      unpack16(w[n], xv);
+      quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, cbase + j, codes, scales,
+                              dq, kStage && rs.fast ? &dq_stage[wave][2 * lane] : nullptr);
+    }
+  }
+  if (kStage && rs.fast && valid > 0) {
+    // the wave's dequant chunk leaves as two contiguous KiB
+    __builtin_amdgcn_wave_barrier();
+    uint4* dqc = dq + 2 * cbase;
+    if (lane < 2 * valid) store_out(&dqc[lane], dq_stage[wave][lane]);
+    if (64 + lane < 2 * valid) store_out(&dqc[64 + lane], dq_stage[wave][64 + lane]);
   }
 }
 
@@ -535,24 +481,6 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_blocks(
   out[2 * blk + 1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// Workgroups that fit on the device at once for the split kernel, capped
-// by the work available.
-int64_t persistent_groups(int waves_per_group, int64_t row_groups) {
-  static int cu_count[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cu_count[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cu_count[dev] = n;
-  }
-  const int per_cu = max(1, (4 * kMaxWavesPerSimd) / waves_per_group);
-  const int64_t cap = (int64_t)cu_count[dev] * per_cu;
-  return row_groups < cap ? row_groups : cap;
-}
-
 template <bool FOS, bool DQ>
 hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const int nblk = (int)(a.hidden / 16);
@@ -560,14 +488,13 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   uint2* codes = (uint2*)a.codes;
   uint4* dq = (uint4*)a.dequant;
   const float neg_zero = -0.0f;
-  const int W = (nblk + 63) / 64;  // waves per row
+  constexpr int NB = FP4Q_NV_NB;             // blocks per lane
+  const int W = (nblk + 64 * NB - 1) / (64 * NB);  // waves per row
   if (W <= kMaxWgWaves) {
     const int R = W >= 8 ? 1 : 8 / W;  // rows per workgroup
-    const int64_t row_groups = (a.rows + R - 1) / R;
-    const int64_t groups = FP4Q_NV_PERSIST ? persistent_groups(W * R, row_groups) : row_groups;
-    const dim3 grid((unsigned)groups), block(64 * W * R);
-    hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ>), grid, block, 0, st, x, a.rows, nblk, W,
-                       R, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
+    const dim3 grid((unsigned)((a.rows + R - 1) / R)), block(64 * W * R);
+    hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, 0, st, x, a.rows, nblk,
+                       W, R, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
                        neg_zero);
   } else {
     const dim3 grid((unsigned)((a.rows + kLongWaves - 1) / kLongWaves)), block(64 * kLongWaves);

@@ -85,7 +85,7 @@ def edge_rows(H, seed):
     return np.stack(bits, 0)
 
 
-HIDDEN = [16, 32, 48, 1008, 1024, 1040, 2048, 7168, 8192, 8208, 16400]
+HIDDEN = [16, 32, 48, 1008, 1024, 1040, 2048, 2064, 7168, 8192, 8208, 16400, 32784]
 
 
 @pytest.mark.parametrize("fos", [True, False])
