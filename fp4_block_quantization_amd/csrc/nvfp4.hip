@@ -51,6 +51,17 @@ namespace {
 #ifndef FP4Q_NV_LDS_DQ
 #define FP4Q_NV_LDS_DQ 1
 #endif
+// Build-time knob: wavefronts per workgroup the split kernel aims for
+// (whole rows per workgroup).
+#ifndef FP4Q_NV_WG_WAVES
+#define FP4Q_NV_WG_WAVES 4
+#endif
+// Build-time knob: FP4Q_NV_GRID_PER_CU > 0 launches at most that many
+// workgroups per compute unit, each looping over row groups; 0 launches one
+// workgroup per row group.
+#ifndef FP4Q_NV_GRID_PER_CU
+#define FP4Q_NV_GRID_PER_CU 0
+#endif
 // Build-time knob: blocks per lane in the split kernel (1 or 2).
 #ifndef FP4Q_NV_NB
 #define FP4Q_NV_NB 2
@@ -135,6 +146,7 @@ struct RowScale {
   float ks6, ks4;    // fl(6 s), fl(4 s); 1 for a zero row (so b / ks = 0)
   float rks6, rks4;  // approximate reciprocals for the bracketed block scale
   bool fast;         // every decode step e s is 0 or >= 2^-127
+  bool certify;      // 2^-50 <= s <= 2^40: the error enclosure applies
 };
 
 template <bool FOS>
@@ -148,6 +160,7 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
   // s >= 2^-118: ks >= 2^-116 so 1/ks is normal, and the smallest decode
   // step 2^-9 s >= 2^-127 has a finite reciprocal.
   r.fast = r.s >= 0x1p-118f || r.s == 0.0f;
+  r.certify = r.s >= 0x1p-50f && r.s <= 0x1p40f;
   return r;
 }
 
@@ -159,40 +172,85 @@ __device__ __forceinline__ void fill_recip(float* tab, float s, int first, int s
   }
 }
 
-struct Candidate {
-  uint32_t code[2];  // 16 nibbles, element 2i in the low nibble of byte i
-  float err;
-  uint32_t deq[8];   // the candidate values rounded to BF16, two per word
-};
-
-// One candidate on the fast path: decode step e, finite reciprocal r.
-template <bool DQ>
-__device__ __forceinline__ void candidate(const float (&x)[16], float e, float r, float s,
-                                          float neg_zero, Candidate& out) {
-  uint32_t code[2] = {0u, 0u};
-  float err = 0.0f;
-  const _Float16 eh = (_Float16)e;  // exact: E4M3 values are FP16 numbers
-  const half2v e2 = {eh, eh};
+// Codes of one candidate, and (APPROX) A = sum over the block of
+// (v - g)^2 in FP32 with fused multiply-adds: the candidate's error in units
+// of its decode step, used by the certified comparison below.
+template <bool APPROX>
+__device__ __forceinline__ void encode_candidate(const float (&x)[16], float r,
+                                                 uint32_t (&code)[2], float& A) {
+  code[0] = code[1] = 0u;
+  A = 0.0f;
   static_for<0, 8>([&](auto P) {
     constexpr int p = decltype(P)::value;
     const float v0 = x[2 * p] * r, v1 = x[2 * p + 1] * r;
     code[p >> 2] = cvt_e2m1x2<p & 3>(code[p >> 2], v0, v1);
-    const half2v ge = e2m1x2_values_f16<p & 3>(code[p >> 2]) * e2;  // exact
-    const float c0 = __builtin_fmaf((float)ge.x, s, neg_zero);     // fl(ge s)
+    if (APPROX) {
+      const float2v g = e2m1x2_values<p & 3>(code[p >> 2]);
+      const float a0 = v0 - g.x, a1 = v1 - g.y;  // exact (Sterbenz; g = 0 gives v)
+      A = __builtin_fmaf(a0, a0, A);
+      A = __builtin_fmaf(a1, a1, A);
+    }
+  });
+  // computed here, while v is live, not sunk into the branch that reads it
+  if (APPROX) asm volatile("" : "+v"(A));
+}
+
+// The candidate's squared error by the definition: c = fl(fl(g e) s),
+// err = sum in element order of fl(fl(x - c)^2).  g e is exact in FP16
+// (<= 6 significant bits, between 2^-10 and 2688); v_fma_mix_f32 with the
+// addend -0 rounds ge * s once and leaves every product unchanged.
+__device__ __forceinline__ float exact_error(const float (&x)[16], const uint32_t (&code)[2],
+                                             float e, float s, float neg_zero) {
+  const _Float16 eh = (_Float16)e;  // exact: E4M3 values are FP16 numbers
+  const half2v e2 = {eh, eh};
+  float err = 0.0f;
+  static_for<0, 8>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    const half2v ge = e2m1x2_values_f16<p & 3>(code[p >> 2]) * e2;
+    const float c0 = __builtin_fmaf((float)ge.x, s, neg_zero);
     const float c1 = __builtin_fmaf((float)ge.y, s, neg_zero);
     const float d0 = x[2 * p] - c0, d1 = x[2 * p + 1] - c1;
     const float q0 = d0 * d0, q1 = d1 * d1;
     err = err + q0;
     err = err + q1;
-    if (DQ) {
-      uint32_t pair = cvt_bf16x2(c0, c1);
-      asm volatile("" : "+v"(pair));  // keep the BF16 pair: select words, not floats
-      out.deq[p] = pair;
-    }
   });
-  out.code[0] = code[0];
-  out.code[1] = code[1];
-  out.err = err;
+  return err;
+}
+
+// The chosen candidate's values c = fl(fl(g e) s) rounded to BF16.
+__device__ __forceinline__ void dequant_block(const uint32_t (&code)[2], float e, float s,
+                                              float neg_zero, uint32_t (&deq)[8]) {
+  const _Float16 eh = (_Float16)e;
+  const half2v e2 = {eh, eh};
+  static_for<0, 8>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    const half2v ge = e2m1x2_values_f16<p & 3>(code[p >> 2]) * e2;
+    deq[p] = cvt_bf16x2(__builtin_fmaf((float)ge.x, s, neg_zero),
+                        __builtin_fmaf((float)ge.y, s, neg_zero));
+  });
+}
+
+// Certified enclosure [lo, hi] of a candidate's FP32 error err (as the
+// definition computes it) from A and the decode step D = fl(e s), for rows
+// with 2^-50 <= s <= 2^40 and e != 0.  With u = 2^-24: v = x r and the
+// candidate value c carry relative rounding errors, so each x - c differs
+// from D (v - g) by at most D 2.01u (|v| + |g|) <= D 32.2u (|v| < 10,
+// |g| <= 6); summed over 16 elements, |sum (x-c)^2 - D^2 S| <= D^2 (258u
+// sqrt(S) + 0.001u) with S the exact sum of (v - g)^2, and A = S (1 +- 16.1u).
+// The FP32 error is sum (x-c)^2 (1 +- 18.1u), plus at most 2^-145 from
+// underflow.  Every coefficient below carries a factor of two or more over
+// these (which also covers the rounding of this arithmetic), and the range of
+// s keeps D^2 normal and every error finite.
+struct ErrBounds {
+  float lo, hi;
+};
+__device__ __forceinline__ ErrBounds err_bounds(float A, float D) {
+  constexpr float u = 0x1p-24f;
+  const float D2 = D * D;
+  const float t = __builtin_fmaf(520.0f * u, __builtin_amdgcn_sqrtf(A), 40.0f * u);
+  const float hi = __builtin_fmaf(A, 1.0f + 80.0f * u, t);
+  const float lo = __builtin_fmaf(A, 1.0f - 80.0f * u, -t);
+  return {__builtin_fmaf(D2, lo, -0x1p-136f), __builtin_fmaf(D2, hi, 0x1p-136f)};
 }
 
 // One element of a candidate by the portable definition: |x| r may be
@@ -280,23 +338,36 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
   uint32_t eb = cvt_e4m3x2(t6 * (1.0f + 0x1p-18f), t4 * (1.0f + 0x1p-18f));
   if (__builtin_expect(lo != eb, 0))
     eb = cvt_e4m3x2(fminf(b / rs.ks6, 448.0f), FOS ? fminf(b / rs.ks4, 448.0f) : 0.0f);
-  Candidate c6;
-  candidate<DQ>(x, e4m3_value<0>(eb), tab[eb & 0xFFu], rs.s, neg_zero, c6);
-  out.code0 = c6.code[0];
-  out.code1 = c6.code[1];
-  out.ebyte = eb & 0xFFu;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) out.deq[k] = c6.deq[k];
+  const float e6 = e4m3_value<0>(eb);
+  uint32_t code[2];
+  float A6;
+  encode_candidate<FOS>(x, tab[eb & 0xFFu], code, A6);
+  float e = e6;
+  uint32_t ebyte = eb & 0xFFu;
   if (FOS) {
-    Candidate c4;
-    candidate<DQ>(x, e4m3_value<1>(eb), tab[eb >> 8], rs.s, neg_zero, c4);
-    const bool four = c4.err < c6.err;  // strictly lower error: 4 wins; ties keep 6
-    out.code0 = four ? c4.code[0] : out.code0;
-    out.code1 = four ? c4.code[1] : out.code1;
-    out.ebyte = four ? (eb >> 8) : out.ebyte;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out.deq[k] = four ? c4.deq[k] : out.deq[k];
+    const float e4 = e4m3_value<1>(eb);
+    uint32_t code4[2];
+    float A4;
+    encode_candidate<true>(x, tab[eb >> 8], code4, A4);
+    // 4 wins only with a strictly lower error; both scales zero: the same
+    // error, keep 6
+    bool four = false, decided = eb == 0u;
+    if (rs.certify && e4 != 0.0f && e6 != 0.0f) {
+      const ErrBounds b6 = err_bounds(A6, e6 * rs.s), b4 = err_bounds(A4, e4 * rs.s);
+      four = b4.hi < b6.lo;
+      decided = four || b4.lo >= b6.hi;
+    }
+    if (__builtin_expect(!decided, 0))
+      four = exact_error(x, code4, e4, rs.s, neg_zero) < exact_error(x, code, e6, rs.s, neg_zero);
+    code[0] = four ? code4[0] : code[0];
+    code[1] = four ? code4[1] : code[1];
+    e = four ? e4 : e;
+    ebyte = four ? (eb >> 8) : ebyte;
   }
+  out.code0 = code[0];
+  out.code1 = code[1];
+  out.ebyte = ebyte;
+  if (DQ) dequant_block(code, e, rs.s, neg_zero, out.deq);
 }
 
 // One block, written directly (one lane, 32 contiguous dequant bytes).
@@ -353,76 +424,128 @@ __device__ __forceinline__ void load_block(const uint4* __restrict__ x, int64_t 
 // derive the row constants and fill the reciprocal table, which the others
 // read back.  Row and chunk are wave-uniform, so all addressing is scalar
 // base + 32-bit lane offset.
+// Rows of group g this wave works on: row, the blocks of its chunk that
+// exist (0 for a row outside the range or past the end), their first index.
+struct ChunkRef {
+  int64_t row, cbase;
+  int valid;
+  bool active;
+};
+template <int NB>
+__device__ __forceinline__ ChunkRef chunk_ref(int64_t g, int rw, int chunk, int R, int nblk,
+                                              int64_t rows, const int64_t* offs,
+                                              int64_t ngroups) {
+  ChunkRef c;
+  c.row = g * R + rw;
+  c.active = c.row < rows && row_range(c.row, rows, offs, ngroups);
+  c.valid = c.active ? min(64 * NB, nblk - chunk * 64 * NB) : 0;
+  c.cbase = c.row * nblk + (int64_t)chunk * 64 * NB;
+  return c;
+}
+
+template <int NB>
+__device__ __forceinline__ void load_chunk(const uint4* __restrict__ x, const ChunkRef& c,
+                                           int lane, uint32_t (&w)[NB][8]) {
+  const uint4* xc = x + 2 * c.cbase;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    if (64 * n < c.valid) {  // wave-uniform: the block slot exists for some lane
+      load_block(xc, min(lane + 64 * n, c.valid - 1), w[n]);  // in bounds for every lane
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[n][k] = 0u;
+    }
+  }
+}
+
 template <bool FOS, bool DQ, int NB>
 __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
-    const uint4* __restrict__ x, int64_t rows, int nblk, int W, int R,
+    const uint4* __restrict__ x, int64_t rows, int nblk, int W, int R, int64_t ngrp,
     const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
     float neg_zero) {
   __shared__ uint32_t wave_max[kMaxWgWaves];
-  __shared__ float recip[kMaxWgWaves][128];
   __shared__ RowScale rowinfo[kMaxWgWaves];
-  // dequant staging: per wave, 64 blocks x 32 bytes
-  __shared__ uint4 dq_stage[FP4Q_NV_LDS_DQ && DQ && NB == 1 ? kMaxWgWaves : 1][128];
+  // dynamic LDS: the reciprocal table of each row (R x 128 floats), then,
+  // with staged dequant stores, 2 KiB per wave (64 blocks x 32 bytes, reused
+  // for each group of 64 blocks)
+  extern __shared__ uint4 dyn_lds[];
+  float(*recip)[128] = (float(*)[128])dyn_lds;
+  uint4(*dq_stage)[128] = (uint4(*)[128])(dyn_lds + 32 * R);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
-  const int64_t row = (int64_t)blockIdx.x * R + rw;
-  const bool active = row < rows && row_range(row, rows, offs, ngroups);
-  // blocks of this wave's chunk that exist (0 for an inactive row)
-  const int valid = active ? min(64 * NB, nblk - chunk * 64 * NB) : 0;
-  const int64_t cbase = row * nblk + (int64_t)chunk * 64 * NB;  // uniform
-  const uint4* xc = x + 2 * cbase;
 
+  // Row groups g = blockIdx.x, + gridDim.x, ...: the next group's chunk is
+  // loaded while this one is processed.
+  int64_t g = blockIdx.x;
+  ChunkRef c = chunk_ref<NB>(g, rw, chunk, R, nblk, rows, offs, ngroups);
   uint32_t w[NB][8];
-  uint32_t bmax[NB];
-  uint32_t lmax = 0;
+  load_chunk<NB>(x, c, lane, w);
+  constexpr bool kPersist = FP4Q_NV_GRID_PER_CU > 0;
+  for (;;) {  // gridDim.x <= ngrp: every workgroup has a first group
+    uint32_t bmax[NB];
+    uint32_t lmax = 0;
 #pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    const int j = lane + 64 * n;
-    if (64 * n < valid) {  // wave-uniform: the block slot exists for some lane
-      const int jj = min(j, valid - 1);  // in-bounds for every lane
-      load_block(xc, jj, w[n]);
-      bmax[n] = j < valid ? block_absmax_bits(w[n]) : 0u;
-    } else {
+    for (int n = 0; n < NB; ++n) {
+      bmax[n] = lane + 64 * n < c.valid ? block_absmax_bits(w[n]) : 0u;
+      lmax = max(lmax, bmax[n]);
+    }
+    ChunkRef cn;
+    uint32_t wn[NB][8];
+    if (kPersist) {
+      cn = chunk_ref<NB>(g + gridDim.x, rw, chunk, R, nblk, rows, offs, ngroups);
+      load_chunk<NB>(x, cn, lane, wn);
+    }
+
+    const uint32_t m = wave_max_u32(lmax);
+    if (lane == 0) wave_max[wave] = m;
+    __syncthreads();
+    if (chunk < 2) {
+      uint32_t amax_bits = 0;
+      for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+      const RowScale rs = row_scale<FOS>(amax_bits);
+      if (chunk == 0 && lane == 0) {
+        rowinfo[rw] = rs;
+        if (c.active) tscale[c.row] = rs.s;
+      }
+      fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
+    }
+    __syncthreads();
+    const RowScale rs = rowinfo[rw];
+    constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ;
+    const bool stage = kStage && rs.fast;  // wave-uniform
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w[n][k] = 0u;
-      bmax[n] = 0u;
+    for (int n = 0; n < NB; ++n) {
+      const int j = lane + 64 * n;
+      if (64 * n < c.valid && j < c.valid) {
+        float xv[16];
+        unpack16(w[n], xv);
+        quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, c.cbase + j, codes,
+                                scales, dq, stage ? &dq_stage[wave][2 * lane] : nullptr);
+      }
+      if (stage && 64 * n < c.valid) {
+        // the 64 blocks' dequant values leave as two contiguous KiB
+        const int nv2 = 2 * min(64, c.valid - 64 * n);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint4* dqc = dq + 2 * (c.cbase + 64 * n);
+        if (lane < nv2) store_out(&dqc[lane], dq_stage[wave][lane]);
+        if (64 + lane < nv2) store_out(&dqc[64 + lane], dq_stage[wave][64 + lane]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
     }
-    lmax = max(lmax, bmax[n]);
-  }
-  const uint32_t m = wave_max_u32(lmax);
-  if (lane == 0) wave_max[wave] = m;
-  __syncthreads();
-  if (chunk < 2) {
-    uint32_t amax_bits = 0;
-    for (int c = 0; c < W; ++c) amax_bits = max(amax_bits, wave_max[rw * W + c]);
-    const RowScale rs = row_scale<FOS>(amax_bits);
-    if (chunk == 0 && lane == 0) {
-      rowinfo[rw] = rs;
-      if (active) tscale[row] = rs.s;
-    }
-    fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
-  }
-  __syncthreads();
-  const RowScale rs = rowinfo[rw];
-  constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ && NB == 1;
+    if (!kPersist) break;
+    g += gridDim.x;
+    if (g >= ngrp) break;
+    c = cn;
 #pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    const int j = lane + 64 * n;
-    if (64 * n < valid && j < valid) {
-      float xv[16];
-      unpack16(w[n], xv);
-      quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, cbase + j, codes, scales,
-                              dq, kStage && rs.fast ? &dq_stage[wave][2 * lane] : nullptr);
-    }
-  }
-  if (kStage && rs.fast && valid > 0) {
-    // the wave's dequant chunk leaves as two contiguous KiB
-    __builtin_amdgcn_wave_barrier();
-    uint4* dqc = dq + 2 * cbase;
-    if (lane < 2 * valid) store_out(&dqc[lane], dq_stage[wave][lane]);
-    if (64 + lane < 2 * valid) store_out(&dqc[64 + lane], dq_stage[wave][64 + lane]);
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[n][k] = wn[n][k];
   }
 }
 
@@ -491,10 +614,21 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   constexpr int NB = FP4Q_NV_NB;             // blocks per lane
   const int W = (nblk + 64 * NB - 1) / (64 * NB);  // waves per row
   if (W <= kMaxWgWaves) {
-    const int R = W >= 8 ? 1 : 8 / W;  // rows per workgroup
-    const dim3 grid((unsigned)((a.rows + R - 1) / R)), block(64 * W * R);
-    hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, 0, st, x, a.rows, nblk,
-                       W, R, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
+    const int R = W >= FP4Q_NV_WG_WAVES ? 1 : FP4Q_NV_WG_WAVES / W;  // rows per workgroup
+    const int64_t ngrp = (a.rows + R - 1) / R;
+    int64_t nwg = ngrp;
+    if (FP4Q_NV_GRID_PER_CU > 0) {
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) == hipSuccess &&
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+          cus > 0)
+        nwg = (int64_t)cus * FP4Q_NV_GRID_PER_CU < ngrp ? (int64_t)cus * FP4Q_NV_GRID_PER_CU : ngrp;
+    }
+    const dim3 grid((unsigned)nwg), block(64 * W * R);
+    const size_t lds = (size_t)R * 128 * sizeof(float) +
+                       (FP4Q_NV_LDS_DQ && DQ ? (size_t)W * R * 128 * sizeof(uint4) : 0);
+    hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, lds, st, x, a.rows, nblk,
+                       W, R, ngrp, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
                        neg_zero);
   } else {
     const dim3 grid((unsigned)((a.rows + kLongWaves - 1) / kLongWaves)), block(64 * kLongWaves);
