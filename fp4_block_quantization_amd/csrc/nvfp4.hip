@@ -62,6 +62,12 @@ namespace {
 #ifndef FP4Q_NV_GRID_PER_CU
 #define FP4Q_NV_GRID_PER_CU 0
 #endif
+// Build-time knob: FP4Q_NV_LDS_LOAD = 1 copies each wave's input chunk
+// into LDS with 16-byte-per-lane contiguous loads (global_load_lds) and
+// reads the lane's blocks from there.
+#ifndef FP4Q_NV_LDS_LOAD
+#define FP4Q_NV_LDS_LOAD 0
+#endif
 // Build-time knob: blocks per lane in the split kernel (1 or 2).
 #ifndef FP4Q_NV_NB
 #define FP4Q_NV_NB 2
@@ -178,17 +184,27 @@ __device__ __forceinline__ void fill_recip(float* tab, float s, int first, int s
 template <bool APPROX>
 __device__ __forceinline__ void encode_candidate(const float (&x)[16], float r,
                                                  uint32_t (&code)[2], float& A) {
-  code[0] = code[1] = 0u;
   A = 0.0f;
-  static_for<0, 8>([&](auto P) {
-    constexpr int p = decltype(P)::value;
-    const float v0 = x[2 * p] * r, v1 = x[2 * p + 1] * r;
-    code[p >> 2] = cvt_e2m1x2<p & 3>(code[p >> 2], v0, v1);
+  static_for<0, 2>([&](auto H) {
+    constexpr int h = decltype(H)::value;
+    float v[8];
+    uint32_t word = 0u;
+    static_for<0, 4>([&](auto P) {
+      constexpr int p = decltype(P)::value;
+      v[2 * p] = x[8 * h + 2 * p] * r;
+      v[2 * p + 1] = x[8 * h + 2 * p + 1] * r;
+      word = cvt_e2m1x2<p>(word, v[2 * p], v[2 * p + 1]);
+    });
+    code[h] = word;
     if (APPROX) {
-      const float2v g = e2m1x2_values<p & 3>(code[p >> 2]);
-      const float a0 = v0 - g.x, a1 = v1 - g.y;  // exact (Sterbenz; g = 0 gives v)
-      A = __builtin_fmaf(a0, a0, A);
-      A = __builtin_fmaf(a1, a1, A);
+      // decoded from the finished word: each byte is final once written
+      static_for<0, 4>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        const float2v g = e2m1x2_values<p>(word);
+        const float a0 = v[2 * p] - g.x, a1 = v[2 * p + 1] - g.y;  // exact (Sterbenz; g = 0 gives v)
+        A = __builtin_fmaf(a0, a0, A);
+        A = __builtin_fmaf(a1, a1, A);
+      });
     }
   });
   // computed here, while v is live, not sunk into the branch that reads it
@@ -458,6 +474,38 @@ __device__ __forceinline__ void load_chunk(const uint4* __restrict__ x, const Ch
   }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The same chunk through LDS: every lane copies 16 consecutive bytes per
+// instruction straight into the wave's LDS tile (1 KiB contiguous per
+// instruction), then reads its own blocks back.  Lanes whose half-block
+// lies past the chunk's end copy nothing.
+template <int NB>
+__device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, const ChunkRef& c,
+                                               int lane, uint4* tile, uint32_t (&w)[NB][8]) {
+  const uint4* xc = x + 2 * c.cbase;
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = 128 * n + 64 * k + lane;  // 16-byte unit of the chunk
+      if (64 * n < c.valid && (q >> 1) < c.valid)
+        __builtin_amdgcn_global_load_lds(xc + q, (lds_void*)(tile + 128 * n + 64 * k), 16, 0, 0);
+    }
+  __builtin_amdgcn_s_waitcnt(0);  // the copies have landed in LDS
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    if (64 * n < c.valid) {
+      const uint4 a = tile[128 * n + 2 * lane], b = tile[128 * n + 2 * lane + 1];
+      w[n][0] = a.x; w[n][1] = a.y; w[n][2] = a.z; w[n][3] = a.w;
+      w[n][4] = b.x; w[n][5] = b.y; w[n][6] = b.z; w[n][7] = b.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[n][k] = 0u;
+    }
+  }
+}
+
 template <bool FOS, bool DQ, int NB>
 __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     const uint4* __restrict__ x, int64_t rows, int nblk, int W, int R, int64_t ngrp,
@@ -471,7 +519,11 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // for each group of 64 blocks)
   extern __shared__ uint4 dyn_lds[];
   float(*recip)[128] = (float(*)[128])dyn_lds;
-  uint4(*dq_stage)[128] = (uint4(*)[128])(dyn_lds + 32 * R);
+  constexpr bool kLdsLoad = FP4Q_NV_LDS_LOAD && FP4Q_NV_GRID_PER_CU == 0;
+  // per wave: the input tile (NB x 2 KiB) when loading through LDS, whose
+  // half n, once read, stages the dequant values of block group n; else
+  // 2 KiB of staging
+  uint4* wave_lds = dyn_lds + 32 * R + (kLdsLoad ? 128 * NB : 128) * (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
@@ -481,7 +533,10 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   int64_t g = blockIdx.x;
   ChunkRef c = chunk_ref<NB>(g, rw, chunk, R, nblk, rows, offs, ngroups);
   uint32_t w[NB][8];
-  load_chunk<NB>(x, c, lane, w);
+  if (kLdsLoad)
+    load_chunk_lds<NB>(x, c, lane, wave_lds, w);
+  else
+    load_chunk<NB>(x, c, lane, w);
   constexpr bool kPersist = FP4Q_NV_GRID_PER_CU > 0;
   for (;;) {  // gridDim.x <= ngrp: every workgroup has a first group
     uint32_t bmax[NB];
@@ -518,11 +573,12 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int j = lane + 64 * n;
+      uint4* dq_stage_n = wave_lds + (kLdsLoad ? 128 * n : 0);
       if (64 * n < c.valid && j < c.valid) {
         float xv[16];
         unpack16(w[n], xv);
         quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, c.cbase + j, codes,
-                                scales, dq, stage ? &dq_stage[wave][2 * lane] : nullptr);
+                                scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr);
       }
       if (stage && 64 * n < c.valid) {
         // the 64 blocks' dequant values leave as two contiguous KiB
@@ -531,8 +587,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         uint4* dqc = dq + 2 * (c.cbase + 64 * n);
-        if (lane < nv2) store_out(&dqc[lane], dq_stage[wave][lane]);
-        if (64 + lane < nv2) store_out(&dqc[64 + lane], dq_stage[wave][64 + lane]);
+        if (lane < nv2) store_out(&dqc[lane], dq_stage_n[lane]);
+        if (64 + lane < nv2) store_out(&dqc[64 + lane], dq_stage_n[64 + lane]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -625,8 +681,10 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
         nwg = (int64_t)cus * FP4Q_NV_GRID_PER_CU < ngrp ? (int64_t)cus * FP4Q_NV_GRID_PER_CU : ngrp;
     }
     const dim3 grid((unsigned)nwg), block(64 * W * R);
+    const bool lds_load = FP4Q_NV_LDS_LOAD && FP4Q_NV_GRID_PER_CU == 0;
     const size_t lds = (size_t)R * 128 * sizeof(float) +
-                       (FP4Q_NV_LDS_DQ && DQ ? (size_t)W * R * 128 * sizeof(uint4) : 0);
+                       (lds_load ? (size_t)W * R * NB * 128 * sizeof(uint4)
+                                 : FP4Q_NV_LDS_DQ && DQ ? (size_t)W * R * 128 * sizeof(uint4) : 0);
     hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, lds, st, x, a.rows, nblk,
                        W, R, ngrp, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
                        neg_zero);
