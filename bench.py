@@ -6,8 +6,9 @@ workload (Student-t(3) values with a log-normal per-token gain), inputs
 resident in HBM.  value = algorithmic bytes per call / mean call time, in GB
 (10^9 B) per second.  Buffers rotate over several input/output sets (more
 than the 256 MB last-level cache) so repeated calls cannot be served from
-cache.  Calls are timed with HIP events on the stream the library launches
-on (torch's current stream).
+cache.  The timed calls run back to back between two HIP events on the
+stream the library launches on (torch's current stream); a second pass with
+events around every call gives the per-call spread.
 
 Also reported on the same JSON line: the roofline of the dominant kernel,
 a CPU baseline (the CPU oracle timed on this host), the other calls of the
@@ -59,27 +60,33 @@ def mx_bytes(rows, hidden):
     return n * 2 + n // 2 + n // 32 + n // 4 + n // 8 + n // 32
 
 
-def time_calls(fn, sets, steps, warmup):
-    """Run fn(set) round-robin; return per-call durations (ms) from HIP
-    events recorded on the current stream around each call."""
+def time_calls(fn, sets, steps, warmup, per_call=False):
+    """Run fn(set) round-robin.  Returns (mean ms per call over `steps`
+    back-to-back calls bracketed by two HIP events on the current stream,
+    per-call ms from a second pass with events around every call or None)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     wall0 = torch.cuda.Event(enable_timing=True)
     wall1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0.record(stream)
     for i in range(steps):
-        starts[i].record(stream)
         fn(sets[i % len(sets)])
-        ends[i].record(stream)
     wall1.record(stream)
     torch.cuda.synchronize()
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    return per, wall0.elapsed_time(wall1)
+    mean = wall0.elapsed_time(wall1) / steps
+    per = None
+    if per_call:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            starts[i].record(stream)
+            fn(sets[i % len(sets)])
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return mean, per
 
 
 def rotating_nvfp4_sets(x, n, dequant=True):
@@ -146,11 +153,143 @@ def traffic_record(kernel_key):
     return rec.get("bytes_per_launch")
 
 
+# Kernels of the bench run, named by what each dispatch computes.  The
+# split kernel serves both full-width workloads; its smaller grid is the
+# 8192-row headline call.
+HEADLINE_KEY = "nvfp4_quantize_split<fos,dq> moe_act 8192x7168"
+
+
+def _dispatch_label(name, grid, split_grids):
+    if "nvfp4_quantize_split<true, true" in name:
+        return HEADLINE_KEY if grid == min(split_grids) else \
+            "nvfp4_quantize_split<fos,dq> expert_weights 65536x7168"
+    if "nvfp4_quantize_split<true, false" in name:
+        return "nvfp4_quantize_split<fos> ragged_routed 65536x2048"
+    if "nvfp4_dequantize_blocks" in name:
+        return "nvfp4_dequantize_blocks moe_act 8192x7168"
+    if "mxfp4_resq" in name:
+        return "mxfp4_resq_quantize resq_act 8192x7168"
+    if "copyBuffer" in name:
+        return "copyBuffer 256 MiB (device copy, counter calibration)"
+    return None
+
+
+def _read_dispatches(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    for r in rows:  # the trace names it Grid_Size_X, the counter table Grid_Size
+        r["Grid_Size"] = r.get("Grid_Size") or r.get("Grid_Size_X")
+    split_grids = {int(r["Grid_Size"]) for r in rows
+                   if "nvfp4_quantize_split<true, true" in r["Kernel_Name"]}
+    return rows, split_grids
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
+    """Turn the rocprofv3 CSV output of the three profiling runs of this
+    script (kernel trace, FETCH_SIZE, WRITE_SIZE) into the text summaries
+    under profiles/ and the per-launch traffic table the bench reads."""
+    import glob
+    cmd_trace = ("rocprofv3 --kernel-trace --stats -f csv -d %s -o run -- python bench.py "
+                 "--no-cpu" % trace_dir)
+    cmd_pmc = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python bench.py --steps 20 "
+               "--warmup 2 --sets 2 --no-cpu")
+    # kernel durations per (kernel, workload)
+    trace = glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0]
+    rows, split_grids = _read_dispatches(trace)
+    dur = {}
+    for r in rows:
+        lab = _dispatch_label(r["Kernel_Name"], int(r["Grid_Size"]), split_grids)
+        if lab:
+            dur.setdefault(lab, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    stats = glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0]
+    import csv
+    srows = list(csv.DictReader(open(stats)))
+    lines = ["# Kernel durations, bench.py default run (moe_act 8192x7168 headline + secondary "
+             "calls)", "", "Command (repo root, MI355X):", "", "    " + cmd_trace, "",
+             "Per kernel and workload, from the kernel trace (us):", "",
+             "| kernel / workload | dispatches | mean | p50 | min | max |", "|---|---|---|---|---|---|"]
+    for lab, d in sorted(dur.items()):
+        a = np.array(d)
+        lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
+            lab, a.size, a.mean(), np.median(a), a.min(), a.max()))
+    lines += ["", "rocprofv3 --stats summary (all kernels of the run):", "",
+              "| kernel | calls | total ns | average ns | % |", "|---|---|---|---|---|"]
+    for r in srows[:12]:
+        lines.append("| %s | %s | %s | %s | %s |" % (r["Name"][:90], r["Calls"],
+                                                    r["TotalDurationNs"], r["AverageNs"],
+                                                    r["Percentage"]))
+    os.makedirs(out_dir, exist_ok=True)
+    open(os.path.join(out_dir, "kernel_trace_bench_default.md"), "w").write("\n".join(lines) + "\n")
+
+    # HBM bytes per dispatch, calibrated on the 256 MiB device copy
+    def counter(dir_, cname):
+        path = glob.glob(os.path.join(dir_, "*counter_collection.csv"))[0]
+        rows, grids = _read_dispatches(path)
+        per = {}
+        for r in rows:
+            if r["Counter_Name"] != cname:
+                continue
+            lab = _dispatch_label(r["Kernel_Name"], int(r["Grid_Size"]), grids)
+            if lab:
+                per.setdefault(lab, []).append(float(r["Counter_Value"]))
+        return {k: float(np.median(v)) for k, v in per.items()}
+    fetch = counter(fetch_dir, "FETCH_SIZE")
+    write = counter(write_dir, "WRITE_SIZE")
+    copy_key = "copyBuffer 256 MiB (device copy, counter calibration)"
+    copy_bytes = float(1 << 28)
+    f_scale = copy_bytes / (fetch[copy_key] * 1024.0)
+    w_scale = copy_bytes / (write[copy_key] * 1024.0)
+    algo = {HEADLINE_KEY: (8192 * 7168 * 2, nvfp4_bytes(8192, 7168) - 8192 * 7168 * 2),
+            "nvfp4_quantize_split<fos,dq> expert_weights 65536x7168":
+                (65536 * 7168 * 2, nvfp4_bytes(65536, 7168) - 65536 * 7168 * 2),
+            "nvfp4_quantize_split<fos> ragged_routed 65536x2048":
+                (65536 * 2048 * 2 + 65 * 8, nvfp4_bytes(65536, 2048, dequant=False)
+                 - 65536 * 2048 * 2),
+            "nvfp4_dequantize_blocks moe_act 8192x7168":
+                (8192 * 7168 // 2 + 8192 * 7168 // 16 + 8192 * 4, 8192 * 7168 * 2),
+            "mxfp4_resq_quantize resq_act 8192x7168":
+                (8192 * 7168 * 2, mx_bytes(8192, 7168) - 8192 * 7168 * 2),
+            copy_key: (copy_bytes, copy_bytes)}
+    digest = source_digest()
+    table = {}
+    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands (repo root, MI355X), one counter per run:", "",
+             "    " + cmd_pmc.format(c="FETCH_SIZE", d=fetch_dir),
+             "    " + cmd_pmc.format(c="WRITE_SIZE", d=write_dir), "",
+             "Both counters are in KiB per dispatch.  Calibration on the runtime's device copy "
+             "of 256 MiB (268435456 B read, 268435456 B written): FETCH_SIZE reads %.0f KiB "
+             "(scale x%.4f), WRITE_SIZE reads %.0f KiB (scale x%.4f).  Median over dispatches; "
+             "kernel sources digest %s." % (fetch[copy_key], f_scale, write[copy_key], w_scale,
+                                            digest), "",
+             "| kernel / workload | read B (scaled) | algorithmic read B | ratio | write B (scaled) "
+             "| algorithmic write B | ratio |", "|---|---|---|---|---|---|---|"]
+    for lab in sorted(fetch):
+        if lab not in write or lab not in algo:
+            continue
+        rd, wr = fetch[lab] * 1024.0 * f_scale, write[lab] * 1024.0 * w_scale
+        ar, aw = algo[lab]
+        lines.append("| %s | %.0f | %.0f | %.3f | %.0f | %.0f | %.3f |" % (
+            lab, rd, ar, rd / ar, wr, aw, wr / aw))
+        table[lab] = {"bytes_per_launch": round(rd + wr), "read_bytes": round(rd),
+                      "write_bytes": round(wr), "source_digest": digest,
+                      "fetch_scale": f_scale, "write_scale": w_scale}
+    open(os.path.join(out_dir, "hbm_traffic_bench.md"), "w").write("\n".join(lines) + "\n")
+    json.dump(table, open(os.path.join(out_dir, "traffic.json"), "w"), indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
+        # python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR
+        summarize_profiles(*sys.argv[2:5], os.path.join(ROOT, "profiles"))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    # the default warmup (~50 ms of calls) lets the GPU clocks settle: the
+    # first tens of milliseconds of back-to-back calls run several % slower
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-secondary", action="store_true")
@@ -179,22 +318,22 @@ def main():
           file=sys.stderr, flush=True)
 
     sets = rotating_nvfp4_sets(x, args.sets)
-    per, wall = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), sets, args.steps,
-                           args.warmup)
-    ms = float(per.mean())
+    ms, per = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), sets, args.steps,
+                         args.warmup, per_call=True)
     nbytes = nvfp4_bytes(rows, hidden)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    print("[bench] nvfp4_quantize moe_act: mean %.2f us (p10 %.2f p50 %.2f p90 %.2f), %.0f GB/s"
-          % (ms * 1e3, np.percentile(per, 10) * 1e3, np.median(per) * 1e3,
-             np.percentile(per, 90) * 1e3, gbs), file=sys.stderr, flush=True)
+    print("[bench] nvfp4_quantize moe_act: %.2f us per call back to back, %.0f GB/s; per-call "
+          "events p10 %.2f p50 %.2f p90 %.2f us" % (
+              ms * 1e3, gbs, np.percentile(per, 10) * 1e3, np.median(per) * 1e3,
+              np.percentile(per, 90) * 1e3), file=sys.stderr, flush=True)
 
-    key = "nvfp4_quantize_rows<7,fos,dq> moe_act 8192x7168"
+    key = HEADLINE_KEY
     traffic = traffic_record(key)
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": nbytes,
                 "kernel": key, "launch_us_mean": round(ms * 1e3, 3),
-                "launch_us_p50": round(float(np.median(per)) * 1e3, 3)}
+                "launch_us_p50_per_call_events": round(float(np.median(per)) * 1e3, 3)}
     del sets
     torch.cuda.empty_cache()
 
@@ -206,7 +345,7 @@ def main():
         src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
         dsts = [torch.empty_like(src) for _ in range(3)]
         p, _ = time_calls(lambda d: d.copy_(src), dsts, 100, 10)
-        secondary["device_copy_GBps"] = round(2 * src.numel() / (p.mean() * 1e-3) / 1e9, 1)
+        secondary["device_copy_GBps"] = round(2 * src.numel() / (p * 1e-3) / 1e9, 1)
         del src, dsts
     if "dequant" in parts:
         # standalone dequant on the headline shape
@@ -215,7 +354,7 @@ def main():
         p, _ = time_calls(lambda d: fq.nvfp4_dequantize(d[0], d[1], d[2], out=d[3]), dsets, 200, 20)
         b = dequant_bytes(rows, hidden)
         secondary["nvfp4_dequantize moe_act 8192x7168"] = {
-            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
         del dsets, c, s_, ts
         torch.cuda.empty_cache()
     if "resq" in parts:
@@ -227,7 +366,7 @@ def main():
                           list(range(4)), 200, 20)
         b = mx_bytes(*xr.shape)
         secondary["mxfp4_resq_quantize resq_act 8192x7168"] = {
-            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
         del msets, mouts, xr
         torch.cuda.empty_cache()
     if "ragged" in parts:
@@ -239,7 +378,7 @@ def main():
                           gsets, 200, 20)
         b = nvfp4_bytes(*xg.shape, dequant=False, groups=offs.numel() - 1)
         secondary["nvfp4_quantize ragged_routed 65536x2048 (64 groups, no dequant)"] = {
-            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
         del gsets, xg
         torch.cuda.empty_cache()
     if "weights" in parts:
@@ -249,7 +388,7 @@ def main():
         p, _ = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), wsets, 50, 5)
         b = nvfp4_bytes(*xw.shape)
         secondary["nvfp4_quantize expert_weights 65536x7168"] = {
-            "us": round(p.mean() * 1e3, 2), "GBps": round(b / (p.mean() * 1e-3) / 1e9, 1)}
+            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
         del wsets, xw
         torch.cuda.empty_cache()
     if secondary:
@@ -263,7 +402,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps, 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "moe_act: 8192x7168 BF16 MoE expert input activations, "
