@@ -37,6 +37,14 @@ __device__ __forceinline__ float2v e2m1x2_values(uint32_t src) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, 1.0f, SEL);
 }
 
+// The two E2M1 values of byte SEL times 2^k, exact, where scale2k is the
+// FP32 pattern (k + 127) << 23 (k = -127 gives the all-zero pattern: the
+// conversion reads the scale's exponent field as an E8M0 byte).
+template <int SEL>
+__device__ __forceinline__ float2v e2m1x2_values_scaled(uint32_t src, float scale2k) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, scale2k, SEL);
+}
+
 // The same values as FP16 (exact: E2M1 values are FP16 numbers).
 template <int SEL>
 __device__ __forceinline__ half2v e2m1x2_values_f16(uint32_t src) {

@@ -5,6 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Work-items per kernel launch at most; larger calls are split into several
+// launches over consecutive rows (or blocks).  The dispatch packet counts
+// work-items in 32 bits.
+#ifndef FP4Q_MAX_LAUNCH_ITEMS
+#define FP4Q_MAX_LAUNCH_ITEMS ((int64_t)1 << 31)
+#endif
+
 namespace fp4q {
 
 struct NvQuantArgs {

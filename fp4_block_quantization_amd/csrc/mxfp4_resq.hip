@@ -10,7 +10,7 @@
 // Q(X), Q(dX)'s scale and its 2:4-compressed codes in one pass; the
 // residual itself never leaves registers.
 //
-// Mapping: one lane per 32-element block; no cross-lane work.
+// Mapping: one lane per 8 elements, a quad of lanes per 32-element block.
 #include "fp4q_device.h"
 #include "fp4q_launch.h"
 
@@ -26,78 +26,171 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// MXFP4 of 32 FP32 values: packed nibbles (element 2i in the low nibble of
-// byte i) and the exact dequantized values +-g * 2^k.  Returns the E8M0
-// byte k + 127.  x * 2^-k is exact (or far below the first code), so the
-// hardware E2M1 conversion of the scaled value is the reference rounding.
-__device__ __forceinline__ uint32_t mx_quantize32(const float (&v)[32], uint32_t (&cw)[4],
-                                                  float (&deq)[32]) {
-  uint32_t mbits = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) mbits = max(mbits, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-  const int k = mx_exponent(mbits);
-  const float down = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k, k in [-127, 125]
-  static_for<0, 16>([&](auto P) {
-    constexpr int p = decltype(P)::value;
-    cw[p >> 2] = cvt_e2m1x2<p & 3>(p & 3 ? cw[p >> 2] : 0u, v[2 * p] * down,
-                                    v[2 * p + 1] * down);
-    const float2v g = e2m1x2_values<p & 3>(cw[p >> 2]);
-    deq[2 * p] = ldexpf(g.x, k);  // exact
-    deq[2 * p + 1] = ldexpf(g.y, k);
-  });
-  return (uint32_t)(k + 127);
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
-__global__ __launch_bounds__(256) void mxfp4_resq_blocks(
-    const uint4* __restrict__ x, int64_t nblocks, uint4* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint2* __restrict__ res_codes, uint32_t* __restrict__ res_meta,
-    uint8_t* __restrict__ res_scales) {
-  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blk >= nblocks) return;
+// Max over the four lanes of a quad (the four lanes of one 32-element
+// block): quad_perm [1,0,3,2], then [2,3,0,1].
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, dpp_mov<0xB1>(v));
+  v = max(v, dpp_mov<0x4E>(v));
+  return v;
+}
 
-  float v[32];
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// S_{2:4} choice for every group of four magnitude codes m0..m3 (3 bits
+// each, index = m0 | m1 << 3 | m2 << 6 | m3 << 9): the two largest
+// magnitudes, ties to the lower index; kept indices i0 < i1.  Entry bits
+// 0-3: 4 i0, bits 4-7: 4 i1 (nibble offsets), bit 8: 0, bits 9-12:
+// i0 | i1 << 2.
+struct alignas(16) SelTable {
+  uint16_t e[4096];
+};
+constexpr SelTable make_sel_table() {
+  SelTable t{};
+  for (int idx = 0; idx < 4096; ++idx) {
+    int key[4] = {};
+    for (int i = 0; i < 4; ++i) key[i] = ((idx >> (3 * i)) & 7) * 4 + (3 - i);
+    int first = 0;
+    for (int i = 1; i < 4; ++i)
+      if (key[i] > key[first]) first = i;
+    int second = first == 0 ? 1 : 0;
+    for (int i = 0; i < 4; ++i)
+      if (i != first && key[i] > key[second]) second = i;
+    const int i0 = first < second ? first : second, i1 = first < second ? second : first;
+    t.e[idx] = (uint16_t)((4 * i0) | ((4 * i1) << 4) | ((i0 | (i1 << 2)) << 9));
+  }
+  return t;
+}
+__device__ constexpr SelTable kSelTable = make_sel_table();
+
+// S_{2:4} of one code word holding two groups of four nibbles (group 0 in
+// the low 16 bits), through the table in LDS.  Returns the kept codes, two
+// per group (lower index in the low nibble), and sets meta to i0 | i1 << 2
+// per group (group 0 in the low nibble).
+__device__ __forceinline__ uint32_t select_2of4(uint32_t rw, const uint16_t* tab,
+                                                uint32_t& meta) {
+  // gather the 3-bit magnitudes of each group into 12 bits, both groups at
+  // once (group 0 in bits 0-11, group 1 in bits 16-27)
+  const uint32_t t = (rw & 0x07070707u) | ((rw >> 1) & 0x38383838u);
+  const uint32_t idx = (t & 0x003F003Fu) | ((t >> 2) & 0x0FC00FC0u);
+  const uint32_t e0 = tab[idx & 0xFFFu], e1 = tab[idx >> 16];
+  const uint32_t hi = rw >> 16;
+  // the field offset uses the low 5 bits of its operand: e holds 4 i0 in
+  // bits 0-3 with bit 4 (bit 0 of 4 i1) zero, and e >> 4 holds 4 i1 with
+  // bit 4 (entry bit 8) zero
+  const uint32_t n00 = __builtin_amdgcn_ubfe(rw, e0, 4);
+  const uint32_t n01 = __builtin_amdgcn_ubfe(rw, e0 >> 4, 4);
+  const uint32_t n10 = __builtin_amdgcn_ubfe(hi, e1, 4);
+  const uint32_t n11 = __builtin_amdgcn_ubfe(hi, e1 >> 4, 4);
+  meta = (e0 >> 9) | ((e1 >> 5) & 0xF0u);
+  return n00 | (n01 << 4) | (n10 << 8) | (n11 << 12);
+}
+
+// Units of 8 elements (16 input bytes): a wavefront owns 64 * NU
+// consecutive units and lane l takes units l, l + 64, ... of them, so every
+// load instruction reads 1 KiB contiguously.  The four lanes of a quad hold
+// one 32-element block per unit slot and share its scale through DPP.
+#ifndef FP4Q_MX_UNITS
+#define FP4Q_MX_UNITS 2
+#endif
+constexpr int kUnitsPerLane = FP4Q_MX_UNITS;
+
+__device__ __forceinline__ void resq_unit(const uint4 a, const uint16_t* tab, uint32_t& cw,
+                                          uint32_t& rc, uint32_t& meta, int& k, int& kr) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  // primary scale: packed 16-bit max of the sign-cleared BF16 patterns
+  const u16x2 mw = __builtin_elementwise_max(
+      __builtin_elementwise_max(as_u16x2(w[0] & 0x7FFF7FFFu), as_u16x2(w[1] & 0x7FFF7FFFu)),
+      __builtin_elementwise_max(as_u16x2(w[2] & 0x7FFF7FFFu), as_u16x2(w[3] & 0x7FFF7FFFu)));
+  const uint32_t mbits = quad_max((uint32_t)max(mw.x, mw.y) << 16);
+  k = mx_exponent(mbits);  // [-127, 125]
+  const float down = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k
+  const float up = __uint_as_float((uint32_t)(127 + k) << 23);    // 2^k as a scale operand
+
+  // primary codes; x * 2^-k is exact (or far below the first code)
+  float v[8];
+  cw = 0u;
+  static_for<0, 4>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    v[2 * p] = bf16_lo(w[p]);
+    v[2 * p + 1] = bf16_hi(w[p]);
+    cw = cvt_e2m1x2<p>(cw, v[2 * p] * down, v[2 * p + 1] * down);
+  });
+
+  // residual x - (+-g 2^k), exact in FP32
+  float rmax = 0.0f;
+  static_for<0, 4>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    const float2v g = e2m1x2_values_scaled<p>(cw, up);
+    v[2 * p] = v[2 * p] - g.x;
+    v[2 * p + 1] = v[2 * p + 1] - g.y;
+    rmax = fmaxf(fmaxf(rmax, fabsf(v[2 * p])), fabsf(v[2 * p + 1]));
+  });
+  kr = mx_exponent(quad_max(__float_as_uint(rmax)));
+  const float rdown = __uint_as_float((uint32_t)(127 - kr) << 23);
+  uint32_t rw = 0u;
+  static_for<0, 4>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    rw = cvt_e2m1x2<p>(rw, v[2 * p] * rdown, v[2 * p + 1] * rdown);
+  });
+  rc = select_2of4(rw, tab, meta);
+}
+
+__global__ __launch_bounds__(256) void mxfp4_resq_units(
+    const uint4* __restrict__ x, int64_t u0, int64_t u_end, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint16_t* __restrict__ res_codes,
+    uint8_t* __restrict__ res_meta, uint8_t* __restrict__ res_scales) {
+  // the 2:4 table (8 KiB) into LDS
+  __shared__ uint4 tab_lds[512];
+  const uint4* tab_src = reinterpret_cast<const uint4*>(kSelTable.e);
+  tab_lds[threadIdx.x] = tab_src[threadIdx.x];
+  tab_lds[threadIdx.x + 256] = tab_src[threadIdx.x + 256];
+  __syncthreads();
+  const uint16_t* tab = reinterpret_cast<const uint16_t*>(tab_lds);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // first unit of this wave (uniform); u0 and u_end are multiples of 4, so
+  // quads are whole
+  const int64_t ub = u0 + ((int64_t)blockIdx.x * 4 + wave) * 64 * kUnitsPerLane;
+  const int64_t left = u_end - ub;  // units of this wave that exist (may be <= 0)
+  if (left <= 0) return;
+  const int nv = left < 64 * kUnitsPerLane ? (int)left : 64 * kUnitsPerLane;
+  const uint4* xw = x + ub;  // wave-uniform bases, 32-bit lane offsets
+  uint32_t* cw_out = codes + ub;
+  uint16_t* rc_out = res_codes + ub;
+  uint8_t* meta_out = res_meta + ub;
+  uint8_t* sc_out = scales + (ub >> 2);
+  uint8_t* rs_out = res_scales + (ub >> 2);
+  uint4 a[kUnitsPerLane];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint4 a = x[4 * blk + p];
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  for (int n = 0; n < kUnitsPerLane; ++n)
+    if (64 * n < nv) a[n] = xw[min(lane + 64 * n, nv - 1)];  // in bounds for every lane
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[8 * p + 2 * k] = bf16_lo(w[k]);
-      v[8 * p + 2 * k + 1] = bf16_hi(w[k]);
+  for (int n = 0; n < kUnitsPerLane; ++n) {
+    const int j = lane + 64 * n;
+    if (64 * n < nv) {  // wave-uniform
+      uint32_t cw, rc, meta;
+      int k, kr;
+      resq_unit(a[n], tab, cw, rc, meta, k, kr);
+      if (j < nv) {
+        cw_out[j] = cw;
+        rc_out[j] = (uint16_t)rc;
+        meta_out[j] = (uint8_t)meta;
+        if ((lane & 3) == 0) {
+          sc_out[j >> 2] = (uint8_t)(k + 127);
+          rs_out[j >> 2] = (uint8_t)(kr + 127);
+        }
+      }
     }
   }
-
-  uint32_t cw[4];
-  float deq[32];
-  scales[blk] = (uint8_t)mx_quantize32(v, cw, deq);
-  codes[blk] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-
-  // residual, exact in FP32, quantized again over all 32 values
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = v[i] - deq[i];
-  res_scales[blk] = (uint8_t)mx_quantize32(v, cw, deq);
-
-  // S_{2:4}: per group of 4 keep the two largest magnitudes, ties to the
-  // lower index.  Key = magnitude * 4 + (3 - index) orders uniquely; the
-  // two largest of four keys come from a max/min network.
-  uint32_t rc[2] = {0u, 0u}, meta = 0u;
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const uint32_t word = cw[g >> 1] >> (16 * (g & 1));  // this group's 4 nibbles
-    uint32_t key[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = (((word >> (4 * i)) & 7u) << 2) | (3u - i);
-    const uint32_t p = max(key[0], key[1]), q = min(key[0], key[1]);
-    const uint32_t r = max(key[2], key[3]), t = min(key[2], key[3]);
-    const uint32_t k1 = max(p, r), k2 = max(min(p, r), max(q, t));
-    const uint32_t ia = 3u - (k1 & 3u), ib = 3u - (k2 & 3u);
-    const uint32_t i0 = min(ia, ib), i1 = max(ia, ib);
-    const uint32_t n0 = (word >> (4 * i0)) & 15u, n1 = (word >> (4 * i1)) & 15u;
-    rc[g >> 2] |= (n0 | (n1 << 4)) << (8 * (g & 3));
-    meta |= (i0 | (i1 << 2)) << (4 * g);
-  }
-  res_codes[blk] = make_uint2(rc[0], rc[1]);
-  res_meta[blk] = meta;
 }
 
 }  // namespace
@@ -105,10 +198,15 @@ __global__ __launch_bounds__(256) void mxfp4_resq_blocks(
 hipError_t mxfp4_resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
                              uint8_t* scales, uint8_t* res_codes, uint8_t* res_meta,
                              uint8_t* res_scales, hipStream_t st) {
-  const int64_t nblocks = rows * (hidden / 32);
-  const dim3 grid((unsigned)((nblocks + 255) / 256)), block(256);
-  hipLaunchKernelGGL(mxfp4_resq_blocks, grid, block, 0, st, (const uint4*)x, nblocks,
-                     (uint4*)codes, scales, (uint2*)res_codes, (uint32_t*)res_meta, res_scales);
+  const int64_t nunits = rows * (hidden / 8);  // a multiple of 4
+  const int64_t max_units = FP4Q_MAX_LAUNCH_ITEMS / 256 * 256 * kUnitsPerLane;
+  for (int64_t u0 = 0; u0 < nunits; u0 += max_units) {
+    const int64_t n = nunits - u0 < max_units ? nunits - u0 : max_units;
+    constexpr int64_t per_wg = 256 * kUnitsPerLane;
+    const dim3 grid((unsigned)((n + per_wg - 1) / per_wg)), block(256);
+    hipLaunchKernelGGL(mxfp4_resq_units, grid, block, 0, st, (const uint4*)x, u0, u0 + n,
+                       (uint32_t*)codes, scales, (uint16_t*)res_codes, res_meta, res_scales);
+  }
   return hipGetLastError();
 }
 

@@ -449,11 +449,11 @@ struct ChunkRef {
 };
 template <int NB>
 __device__ __forceinline__ ChunkRef chunk_ref(int64_t g, int rw, int chunk, int R, int nblk,
-                                              int64_t rows, const int64_t* offs,
-                                              int64_t ngroups) {
+                                              int64_t row0, int64_t row_end, int64_t rows,
+                                              const int64_t* offs, int64_t ngroups) {
   ChunkRef c;
-  c.row = g * R + rw;
-  c.active = c.row < rows && row_range(c.row, rows, offs, ngroups);
+  c.row = row0 + g * R + rw;
+  c.active = c.row < row_end && row_range(c.row, rows, offs, ngroups);
   c.valid = c.active ? min(64 * NB, nblk - chunk * 64 * NB) : 0;
   c.cbase = c.row * nblk + (int64_t)chunk * 64 * NB;
   return c;
@@ -508,8 +508,9 @@ __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, cons
 
 template <bool FOS, bool DQ, int NB>
 __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
-    const uint4* __restrict__ x, int64_t rows, int nblk, int W, int R, int64_t ngrp,
-    const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
+    const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk, int W,
+    int R, int64_t ngrp, const int64_t* __restrict__ offs, int64_t ngroups,
+    uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
     float neg_zero) {
   __shared__ uint32_t wave_max[kMaxWgWaves];
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // Row groups g = blockIdx.x, + gridDim.x, ...: the next group's chunk is
   // loaded while this one is processed.
   int64_t g = blockIdx.x;
-  ChunkRef c = chunk_ref<NB>(g, rw, chunk, R, nblk, rows, offs, ngroups);
+  ChunkRef c = chunk_ref<NB>(g, rw, chunk, R, nblk, row0, row_end, rows, offs, ngroups);
   uint32_t w[NB][8];
   if (kLdsLoad)
     load_chunk_lds<NB>(x, c, lane, wave_lds, w);
@@ -549,7 +550,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     ChunkRef cn;
     uint32_t wn[NB][8];
     if (kPersist) {
-      cn = chunk_ref<NB>(g + gridDim.x, rw, chunk, R, nblk, rows, offs, ngroups);
+      cn = chunk_ref<NB>(g + gridDim.x, rw, chunk, R, nblk, row0, row_end, rows, offs,
+                         ngroups);
       load_chunk<NB>(x, cn, lane, wn);
     }
 
@@ -609,14 +611,15 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
 // second pass (served mostly by L2) for the blocks.
 template <bool FOS, bool DQ>
 __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
-    const uint4* __restrict__ x, int64_t rows, int nblk, const int64_t* __restrict__ offs,
-    int64_t ngroups, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ tscale, uint4* __restrict__ dq, float neg_zero) {
+    const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk,
+    const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
+    float neg_zero) {
   __shared__ float recip[kLongWaves][128];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * kLongWaves + wave;
-  if (row >= rows || !row_range(row, rows, offs, ngroups)) return;
+  const int64_t row = row0 + (int64_t)blockIdx.x * kLongWaves + wave;
+  if (row >= row_end || !row_range(row, rows, offs, ngroups)) return;
   const int64_t base = row * nblk;
 
   uint32_t lmax = 0;
@@ -639,25 +642,51 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
   }
 }
 
-// K2: one lane per 16-element block, the candidate formula on the stored
-// values.
-__global__ __launch_bounds__(256) void nvfp4_dequantize_blocks(
-    const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ tscale, int64_t nblocks, int nblk, uint4* __restrict__ out) {
-  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blk >= nblocks) return;
-  const float s = tscale[blk / nblk];
-  const float e = e4m3_value<0>(scales[blk]);
-  const uint2 cw = codes[blk];
-  uint32_t o[8];
-  static_for<0, 8>([&](auto P) {
-    constexpr int k = decltype(P)::value;
-    const float2v g = e2m1x2_values<k & 3>(k < 4 ? cw.x : cw.y);
-    const float ge0 = g.x * e, ge1 = g.y * e;
-    o[k] = cvt_bf16x2(ge0 * s, ge1 * s);
-  });
-  out[2 * blk] = make_uint4(o[0], o[1], o[2], o[3]);
-  out[2 * blk + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+// K2: one lane per 8-element unit (half a block): 4 code bytes in and 16
+// BF16 bytes out.  Wavefront gw covers part gw % wpr of row gw / wpr: up to
+// 64 * FP4Q_DQ_UNITS consecutive units, lane l taking units l, l + 64, ...,
+// so every load and store instruction is contiguous across the wave and the
+// token scale is one uniform load.
+#ifndef FP4Q_DQ_UNITS
+#define FP4Q_DQ_UNITS 4
+#endif
+__global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
+    const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ tscale, int64_t row0, int64_t row_end, int h8, uint32_t wpr,
+    uint4* __restrict__ out) {
+  constexpr int NU = FP4Q_DQ_UNITS;
+  const int lane = threadIdx.x & 63;
+  const uint32_t gw = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t rr = gw / wpr;  // uniform
+  const int64_t row = row0 + rr;
+  if (row >= row_end) return;
+  const int first = (int)(gw - rr * wpr) * 64 * NU;
+  const int nv = h8 - first < 64 * NU ? h8 - first : 64 * NU;  // units of this wave
+  const int64_t base = row * h8 + first;
+  const uint32_t* cw_in = codes + base;
+  const uint8_t* sc_in = scales + (base >> 1);
+  uint4* o = out + base;
+  const float s = tscale[row];
+  uint32_t cw[NU];
+  uint32_t eb[NU];
+#pragma unroll
+  for (int n = 0; n < NU; ++n) {
+    const int j = min(lane + 64 * n, nv - 1);  // in bounds for every lane
+    cw[n] = cw_in[j];
+    eb[n] = sc_in[j >> 1];
+  }
+#pragma unroll
+  for (int n = 0; n < NU; ++n) {
+    const float e = e4m3_value<0>(eb[n]);
+    uint32_t q[4];
+    static_for<0, 4>([&](auto P) {
+      constexpr int k = decltype(P)::value;
+      const float2v g = e2m1x2_values<k>(cw[n]);
+      const float ge0 = g.x * e, ge1 = g.y * e;  // exact
+      q[k] = cvt_bf16x2(ge0 * s, ge1 * s);
+    });
+    if (lane + 64 * n < nv) o[lane + 64 * n] = make_uint4(q[0], q[1], q[2], q[3]);
+  }
 }
 
 template <bool FOS, bool DQ>
@@ -671,28 +700,39 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const int W = (nblk + 64 * NB - 1) / (64 * NB);  // waves per row
   if (W <= kMaxWgWaves) {
     const int R = W >= FP4Q_NV_WG_WAVES ? 1 : FP4Q_NV_WG_WAVES / W;  // rows per workgroup
-    const int64_t ngrp = (a.rows + R - 1) / R;
-    int64_t nwg = ngrp;
-    if (FP4Q_NV_GRID_PER_CU > 0) {
-      int dev = 0, cus = 0;
-      if (hipGetDevice(&dev) == hipSuccess &&
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-          cus > 0)
-        nwg = (int64_t)cus * FP4Q_NV_GRID_PER_CU < ngrp ? (int64_t)cus * FP4Q_NV_GRID_PER_CU : ngrp;
-    }
-    const dim3 grid((unsigned)nwg), block(64 * W * R);
+    const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * W * R) * R;  // rows per launch
     const bool lds_load = FP4Q_NV_LDS_LOAD && FP4Q_NV_GRID_PER_CU == 0;
     const size_t lds = (size_t)R * 128 * sizeof(float) +
                        (lds_load ? (size_t)W * R * NB * 128 * sizeof(uint4)
                                  : FP4Q_NV_LDS_DQ && DQ ? (size_t)W * R * 128 * sizeof(uint4) : 0);
-    hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, lds, st, x, a.rows, nblk,
-                       W, R, ngrp, a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
-                       neg_zero);
+    int cus = 0;
+    if (FP4Q_NV_GRID_PER_CU > 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    }
+    for (int64_t row0 = 0; row0 < a.rows; row0 += max_rows) {
+      const int64_t row_end = a.rows - row0 < max_rows ? a.rows : row0 + max_rows;
+      const int64_t ngrp = (row_end - row0 + R - 1) / R;
+      int64_t nwg = ngrp;
+      if (cus > 0 && (int64_t)cus * FP4Q_NV_GRID_PER_CU < ngrp)
+        nwg = (int64_t)cus * FP4Q_NV_GRID_PER_CU;
+      const dim3 grid((unsigned)nwg), block(64 * W * R);
+      hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, lds, st, x, a.rows,
+                         row0, row_end, nblk, W, R, ngrp, a.offsets, a.num_groups, codes,
+                         a.block_scales, a.token_scales, dq, neg_zero);
+    }
   } else {
-    const dim3 grid((unsigned)((a.rows + kLongWaves - 1) / kLongWaves)), block(64 * kLongWaves);
-    hipLaunchKernelGGL((nvfp4_quantize_long_rows<FOS, DQ>), grid, block, 0, st, x, a.rows, nblk,
-                       a.offsets, a.num_groups, codes, a.block_scales, a.token_scales, dq,
-                       neg_zero);
+    const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * kLongWaves) * kLongWaves;
+    for (int64_t row0 = 0; row0 < a.rows; row0 += max_rows) {
+      const int64_t row_end = a.rows - row0 < max_rows ? a.rows : row0 + max_rows;
+      const dim3 grid((unsigned)((row_end - row0 + kLongWaves - 1) / kLongWaves)),
+          block(64 * kLongWaves);
+      hipLaunchKernelGGL((nvfp4_quantize_long_rows<FOS, DQ>), grid, block, 0, st, x, a.rows, row0,
+                         row_end, nblk, a.offsets, a.num_groups, codes, a.block_scales,
+                         a.token_scales, dq, neg_zero);
+    }
   }
   return hipGetLastError();
 }
@@ -708,11 +748,16 @@ hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t st) {
 hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,
                                    const float* tscale, int64_t rows, int64_t hidden, void* out,
                                    hipStream_t st) {
-  const int nblk = (int)(hidden / 16);
-  const int64_t nblocks = rows * nblk;
-  const dim3 grid((unsigned)((nblocks + 255) / 256)), block(256);
-  hipLaunchKernelGGL(nvfp4_dequantize_blocks, grid, block, 0, st, (const uint2*)codes, scales,
-                     tscale, nblocks, nblk, (uint4*)out);
+  const int h8 = (int)(hidden / 8);
+  const int64_t per_wave = 64 * FP4Q_DQ_UNITS;
+  const uint32_t wpr = (uint32_t)((h8 + per_wave - 1) / per_wave);  // waves per row
+  const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * (int64_t)wpr);
+  for (int64_t row0 = 0; row0 < rows; row0 += max_rows) {
+    const int64_t n = rows - row0 < max_rows ? rows - row0 : max_rows;
+    const dim3 grid((unsigned)((n * wpr + 3) / 4)), block(256);
+    hipLaunchKernelGGL(nvfp4_dequantize_rows, grid, block, 0, st, (const uint32_t*)codes, scales,
+                       tscale, row0, row0 + n, h8, wpr, (uint4*)out);
+  }
   return hipGetLastError();
 }
 
