@@ -1,5 +1,5 @@
 // fp4q_api.cpp -- the C ABI declared in include/fp4q.h: host-side argument
-// validation, then one kernel launch per call on the caller's stream.
+// validation, then the kernel launches of the call on the caller's stream.
 // Validation touches no HIP API, so a rejected call returns its status
 // even on a machine without a GPU.
 #include "fp4q.h"
@@ -10,8 +10,9 @@
 
 namespace {
 
-// Largest sizes the kernels index: row counts that keep the grid within
-// 2^31 workgroups, and row lengths whose block count fits an int.
+// Largest sizes accepted: element indices fit comfortably in 64 bits and
+// row lengths in an int; calls above 2^31 work-items are split into several
+// launches by the launchers.
 constexpr int64_t kMaxRows = (int64_t)1 << 32;
 constexpr int64_t kMaxHidden = (int64_t)1 << 30;
 constexpr int64_t kMaxElements = (int64_t)1 << 40;
