@@ -6,9 +6,12 @@ workload (Student-t(3) values with a log-normal per-token gain), inputs
 resident in HBM.  value = algorithmic bytes per call / mean call time, in GB
 (10^9 B) per second.  Buffers rotate over several input/output sets (more
 than the 256 MB last-level cache) so repeated calls cannot be served from
-cache.  The timed calls run back to back between two HIP events on the
-stream the library launches on (torch's current stream); a second pass with
-events around every call gives the per-call spread.
+cache.  Each measurement first spins the GPU up with 0.2 s of untimed
+calls (after host-side work the clocks have dropped and the first tens of
+milliseconds run several % slower), then runs the warm-up calls; the timed
+calls run back to back between two HIP events on the stream the library
+launches on (torch's current stream); a second pass with events around
+every call gives the per-call spread.
 
 Also reported on the same JSON line: the roofline of the dominant kernel,
 a CPU baseline (the CPU oracle timed on this host), the other calls of the
@@ -60,11 +63,29 @@ def mx_bytes(rows, hidden):
     return n * 2 + n // 2 + n // 32 + n // 4 + n // 8 + n // 32
 
 
+SPINUP_S = 0.2  # untimed back-to-back calls before the warm-up
+
+
+def spin_up(fn, sets, seconds=SPINUP_S):
+    """Back-to-back calls for `seconds` of wall time: after host-side work
+    (workload generation, allocation) the GPU clocks have dropped, and the
+    first tens of milliseconds of calls run several % slower."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            fn(sets[i % len(sets)])
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_calls(fn, sets, steps, warmup, per_call=False):
-    """Run fn(set) round-robin.  Returns (mean ms per call over `steps`
-    back-to-back calls bracketed by two HIP events on the current stream,
-    per-call ms from a second pass with events around every call or None)."""
+    """Spin up, run `warmup` untimed calls, then time `steps` calls (fn(set)
+    round-robin).  Returns (mean ms per call over the `steps` back-to-back
+    calls bracketed by two HIP events on the current stream, per-call ms
+    from a second pass with events around every call, or None)."""
     stream = torch.cuda.current_stream()
+    spin_up(fn, sets)
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
@@ -165,8 +186,8 @@ def _dispatch_label(name, grid, split_grids):
             "nvfp4_quantize_split<fos,dq> expert_weights 65536x7168"
     if "nvfp4_quantize_split<true, false" in name:
         return "nvfp4_quantize_split<fos> ragged_routed 65536x2048"
-    if "nvfp4_dequantize_blocks" in name:
-        return "nvfp4_dequantize_blocks moe_act 8192x7168"
+    if "nvfp4_dequantize" in name:
+        return "nvfp4_dequantize moe_act 8192x7168"
     if "mxfp4_resq" in name:
         return "mxfp4_resq_quantize resq_act 8192x7168"
     if "copyBuffer" in name:
@@ -246,7 +267,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
             "nvfp4_quantize_split<fos> ragged_routed 65536x2048":
                 (65536 * 2048 * 2 + 65 * 8, nvfp4_bytes(65536, 2048, dequant=False)
                  - 65536 * 2048 * 2),
-            "nvfp4_dequantize_blocks moe_act 8192x7168":
+            "nvfp4_dequantize moe_act 8192x7168":
                 (8192 * 7168 // 2 + 8192 * 7168 // 16 + 8192 * 4, 8192 * 7168 * 2),
             "mxfp4_resq_quantize resq_act 8192x7168":
                 (8192 * 7168 * 2, mx_bytes(8192, 7168) - 8192 * 7168 * 2),
@@ -286,8 +307,6 @@ def main():
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the default warmup (~50 ms of calls) lets the GPU clocks settle: the
-    # first tens of milliseconds of back-to-back calls run several % slower
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
@@ -412,6 +431,7 @@ def main():
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "elements_per_s": rows * hidden / (ms * 1e-3),
         "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+        "spinup_s_before_warmup": SPINUP_S,
     }
     print(json.dumps(line), flush=True)
 

@@ -26,6 +26,33 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Build-time knob: FP4Q_MX_NT_STORES = 1 writes the outputs with
+// non-temporal stores.
+#ifndef FP4Q_MX_NT_LOADS
+#define FP4Q_MX_NT_LOADS 1
+#endif
+#ifndef FP4Q_MX_NT_STORES
+#define FP4Q_MX_NT_STORES 0
+#endif
+#ifndef FP4Q_MX_NT_SMALL
+#define FP4Q_MX_NT_SMALL 1
+#endif
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, T v) {
+  if (FP4Q_MX_NT_STORES)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+// the narrow outputs (2 bytes or less per lane)
+template <typename T>
+__device__ __forceinline__ void store_small(T* p, T v) {
+  if (FP4Q_MX_NT_STORES && FP4Q_MX_NT_SMALL)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
@@ -172,7 +199,16 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   uint4 a[kUnitsPerLane];
 #pragma unroll
   for (int n = 0; n < kUnitsPerLane; ++n)
-    if (64 * n < nv) a[n] = xw[min(lane + 64 * n, nv - 1)];  // in bounds for every lane
+    if (64 * n < nv) {
+      const uint4* src = &xw[min(lane + 64 * n, nv - 1)];  // in bounds for every lane
+      if (FP4Q_MX_NT_LOADS) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)src);
+        a[n] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        a[n] = *src;
+      }
+    }
 #pragma unroll
   for (int n = 0; n < kUnitsPerLane; ++n) {
     const int j = lane + 64 * n;
@@ -181,12 +217,12 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
       int k, kr;
       resq_unit(a[n], tab, cw, rc, meta, k, kr);
       if (j < nv) {
-        cw_out[j] = cw;
-        rc_out[j] = (uint16_t)rc;
-        meta_out[j] = (uint8_t)meta;
+        store_out(&cw_out[j], cw);
+        store_small(&rc_out[j], (uint16_t)rc);
+        store_small(&meta_out[j], (uint8_t)meta);
         if ((lane & 3) == 0) {
-          sc_out[j >> 2] = (uint8_t)(k + 127);
-          rs_out[j >> 2] = (uint8_t)(kr + 127);
+          store_small(&sc_out[j >> 2], (uint8_t)(k + 127));
+          store_small(&rs_out[j >> 2], (uint8_t)(kr + 127));
         }
       }
     }

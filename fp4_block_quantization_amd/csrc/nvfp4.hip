@@ -45,6 +45,12 @@ namespace {
 #define FP4Q_NV_NT_STORES 1
 #endif
 
+// Build-time knob: FP4Q_NV_NT_LOADS = 1 reads the input with non-temporal
+// loads (it is read once).
+#ifndef FP4Q_NV_NT_LOADS
+#define FP4Q_NV_NT_LOADS 0
+#endif
+
 // Build-time knob: FP4Q_NV_LDS_DQ = 1 stages each wave's dequant chunk
 // through LDS so that every dequant store instruction writes 1 KiB
 // contiguously (16 bytes per lane); 0 stores each lane's 32 bytes directly.
@@ -67,6 +73,11 @@ namespace {
 // reads the lane's blocks from there.
 #ifndef FP4Q_NV_LDS_LOAD
 #define FP4Q_NV_LDS_LOAD 0
+#endif
+// Build-time knob: FP4Q_NV_WAVE_SYNC = 1 replaces the workgroup barriers
+// by wave barriers when each row has a single wave.
+#ifndef FP4Q_NV_WAVE_SYNC
+#define FP4Q_NV_WAVE_SYNC 1
 #endif
 // Build-time knob: blocks per lane in the split kernel (1 or 2).
 #ifndef FP4Q_NV_NB
@@ -426,9 +437,17 @@ __device__ __forceinline__ bool row_range(int64_t row, int64_t rows, const int64
   return row >= lo && row < hi;
 }
 
+__device__ __forceinline__ uint4 load_in(const uint4* p) {
+  if (FP4Q_NV_NT_LOADS) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  return *p;
+}
+
 __device__ __forceinline__ void load_block(const uint4* __restrict__ x, int64_t blk,
                                            uint32_t (&w)[8]) {
-  const uint4 a = x[2 * blk], b = x[2 * blk + 1];
+  const uint4 a = load_in(&x[2 * blk]), b = load_in(&x[2 * blk + 1]);
   w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
   w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
@@ -475,6 +494,20 @@ __device__ __forceinline__ void load_chunk(const uint4* __restrict__ x, const Ch
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Barrier for the exchange between the waves of a row: the whole workgroup
+// when rows span several waves; with one wave per row (W == 1, uniform over
+// the workgroup) the row's own wave, so the rows of a workgroup do not wait
+// for each other.
+__device__ __forceinline__ void wg_sync(int W) {
+  if (FP4Q_NV_WAVE_SYNC && W == 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
 
 // The same chunk through LDS: every lane copies 16 consecutive bytes per
 // instruction straight into the wave's LDS tile (1 KiB contiguous per
@@ -557,7 +590,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
 
     const uint32_t m = wave_max_u32(lmax);
     if (lane == 0) wave_max[wave] = m;
-    __syncthreads();
+    wg_sync(W);
     if (chunk < 2) {
       uint32_t amax_bits = 0;
       for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
@@ -568,7 +601,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
       }
       fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
     }
-    __syncthreads();
+    wg_sync(W);
     const RowScale rs = rowinfo[rw];
     constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ;
     const bool stage = kStage && rs.fast;  // wave-uniform
@@ -650,6 +683,9 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
 #ifndef FP4Q_DQ_UNITS
 #define FP4Q_DQ_UNITS 4
 #endif
+#ifndef FP4Q_DQ_NT_STORES
+#define FP4Q_DQ_NT_STORES 1
+#endif
 __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tscale, int64_t row0, int64_t row_end, int h8, uint32_t wpr,
@@ -685,7 +721,12 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
       const float ge0 = g.x * e, ge1 = g.y * e;  // exact
       q[k] = cvt_bf16x2(ge0 * s, ge1 * s);
     });
-    if (lane + 64 * n < nv) o[lane + 64 * n] = make_uint4(q[0], q[1], q[2], q[3]);
+    if (lane + 64 * n < nv) {
+      if (FP4Q_DQ_NT_STORES)
+        __builtin_nontemporal_store((u32x4){q[0], q[1], q[2], q[3]}, (u32x4*)&o[lane + 64 * n]);
+      else
+        o[lane + 64 * n] = make_uint4(q[0], q[1], q[2], q[3]);
+    }
   }
 }
 
