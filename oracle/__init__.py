@@ -39,6 +39,8 @@ def lib():
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_e8m0_exponent.argtypes = [c_f]
         L.oracle_e8m0_exponent.restype = ctypes.c_int
+        L.oracle_fp16_rne.argtypes = [ctypes.c_double]
+        L.oracle_fp16_rne.restype = ctypes.c_double
         L.oracle_nvfp4_block.argtypes = [vp, c_f, ctypes.c_int, vp]
         L.oracle_nvfp4_block.restype = None
         L.nvfp4_quantize_ref.argtypes = [vp, c_i64, c_i64, vp, c_i64,
@@ -60,6 +62,7 @@ class NVFP4Block(ctypes.Structure):
         ("e", ctypes.c_float * 2),
         ("e_byte", ctypes.c_uint8 * 2),
         ("err", ctypes.c_float * 2),
+        ("err16", ctypes.c_float * 2),
         ("cand", (ctypes.c_float * 16) * 2),
         ("code", (ctypes.c_uint8 * 16) * 2),
         ("choice", ctypes.c_int),
@@ -99,12 +102,27 @@ def e8m0_exponent(b: float) -> int:
     return lib().oracle_e8m0_exponent(b)
 
 
-def nvfp4_block(x16, s: float, four_over_six: bool) -> NVFP4Block:
+def fp16_rne(v: float) -> float:
+    return lib().oracle_fp16_rne(v)
+
+
+def mode_of(four_over_six) -> int:
+    """0: 6 only; 1: 4/6 on the FP32 error; 2 (or "fp16"): 4/6 on the FP16
+    fast path's error."""
+    if isinstance(four_over_six, str):
+        return {"fp16": 2}[four_over_six]
+    m = int(four_over_six)
+    if m not in (0, 1, 2):
+        raise ValueError("four_over_six must be 0, 1, 2 or 'fp16'")
+    return m
+
+
+def nvfp4_block(x16, s: float, four_over_six) -> NVFP4Block:
     """One 16-element block (FP32 values) with its internals."""
     x = np.ascontiguousarray(x16, dtype=np.float32)
     assert x.shape == (16,)
     out = NVFP4Block()
-    lib().oracle_nvfp4_block(_ptr(x), float(np.float32(s)), int(bool(four_over_six)),
+    lib().oracle_nvfp4_block(_ptr(x), float(np.float32(s)), mode_of(four_over_six),
                              ctypes.byref(out))
     return out
 
@@ -132,7 +150,7 @@ def nvfp4_quantize(x_bits, four_over_six=True, offsets=None, dequant=True,
         off = np.ascontiguousarray(offsets, dtype=np.int64)
         ng = off.shape[0] - 1
     st = lib().nvfp4_quantize_ref(_ptr(x), rows, hidden, _ptr(off), ng,
-                                  int(bool(four_over_six)), _ptr(codes),
+                                  mode_of(four_over_six), _ptr(codes),
                                   _ptr(scales), _ptr(ts), _ptr(dq))
     _check(st, "nvfp4_quantize_ref")
     return codes, scales, ts, dq

@@ -132,6 +132,28 @@ uint16_t oracle_bf16_rne(float f) {
   return (uint16_t)hi;
 }
 
+/* IEEE binary16 rounding to nearest even of a double (11 significant bits,
+ * normal binades 2^-14 .. 2^15, subnormal step 2^-24, largest finite
+ * 65504; at or above 65520 in magnitude the result is infinity).  Returns
+ * the rounded value as a double. */
+double oracle_fp16_rne(double v) {
+  if (v != v) return v;
+  double a = fabs(v);
+  if (a == 0.0 || isinf(a)) return v;
+  int ex;
+  (void)frexp(a, &ex); /* 2^(ex-1) <= a < 2^ex */
+  int binade = ex - 1;
+  if (binade < -14) binade = -14; /* subnormals share the step of 2^-14 */
+  double step = ldexp(1.0, binade - 10);
+  double n = a / step; /* exact: a has at most 53 bits, step a power of 2 */
+  double lo = floor(n);
+  double frac = n - lo;
+  if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0)) lo += 1.0;
+  double r = lo * step;
+  if (r > 65504.0) r = INFINITY;
+  return v < 0 ? -r : r;
+}
+
 /* MX shared exponent (HiFloat4 page, Rollout-ResQ section: MXFP4 keeps one
  * E8M0 scale per 32 elements).  The page gives no rule; the reading is the
  * OCP MX one -- the largest power of two not above the block max, divided
@@ -184,7 +206,7 @@ void oracle_nvfp4_block(const float* x, float s, int four_over_six,
   }
 
   int candidates = four_over_six ? 2 : 1;
-  for (int k = 0; k < 2; ++k) out->err[k] = NAN;
+  for (int k = 0; k < 2; ++k) out->err[k] = out->err16[k] = NAN;
 
   for (int k = 0; k < candidates; ++k) {
     float t = 0.0f;
@@ -224,6 +246,39 @@ void oracle_nvfp4_block(const float* x, float s, int four_over_six,
   }
   /* Strictly lower error picks 4; equality (and NaN) keeps 6. */
   out->choice = (four_over_six && out->err[1] < out->err[0]) ? 4 : 6;
+
+  /* four_over_six == 2: the NVFP4-RL blog's FP16 fast path for the same
+   * decision (section 4, "The optimization").  The blog keeps the E2M1 x
+   * E4M3 products in FP16, where they are exact, and scales the target
+   * down by the inverse token scale instead of scaling the candidate up.
+   * The reading taken here, with every step one IEEE rounding:
+   *   inv_s = 1 / s                         (FP32, once per row)
+   *   y_i   = FP16(|x_i| * inv_s)           target in units of s
+   *   ge_i  = g(q_i) * e_k                  exact in FP16
+   *   d_i   = FP16(y_i - ge_i)              FP16 difference
+   *   err16_k = sum_i d_i^2                 in FP32, element order; d_i^2
+   *                                         is exact in FP32, so only the
+   *                                         additions round
+   * Squares are summed in FP32 because in FP16 they overflow for the
+   * largest blocks (d up to ~256 in units of s).  Codes, scales and
+   * candidate values are those of the exact path; only the choice
+   * differs, and 4 wins only with a strictly lower err16. */
+  if (four_over_six == 2) {
+    float inv_s = 1.0f / s;
+    for (int k = 0; k < 2; ++k) {
+      float err16 = 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        float scaled = fabsf(x[i]) * inv_s;
+        double y = oracle_fp16_rne((double)scaled);
+        double ge = (double)oracle_e2m1_value(out->code[k][i] & 7) * (double)out->e[k];
+        double d = oracle_fp16_rne(y - ge); /* y - ge exact in double */
+        float sq = (float)(d * d);          /* exact: <= 22 significant bits */
+        err16 = err16 + sq;
+      }
+      out->err16[k] = err16;
+    }
+    out->choice = (out->err16[1] < out->err16[0]) ? 4 : 6;
+  }
 }
 
 /* One token row.  Per-token scaling (humans& article section 1; NVFP4-RL
@@ -237,7 +292,7 @@ static void nvfp4_row(const uint16_t* xrow, int64_t hidden, int four_over_six,
     float a = fabsf(bf16_bits_to_float(xrow[i]));
     if (a > amax) amax = a;
   }
-  float s = amax / (four_over_six ? 1536.0f : 2688.0f);
+  float s = amax / (four_over_six ? 1536.0f : 2688.0f); /* 1 and 2: 4/6 on */
   *token_scale = s;
 
   for (int64_t j = 0; j < hidden / 16; ++j) {
@@ -261,6 +316,7 @@ int nvfp4_quantize_ref(const uint16_t* x, int64_t rows, int64_t hidden,
                        int four_over_six, uint8_t* codes, uint8_t* block_scales,
                        float* token_scales, uint16_t* dequant) {
   if (rows < 0 || hidden <= 0 || hidden % 16 != 0 || num_groups < 0) return 2;
+  if (four_over_six < 0 || four_over_six > 2) return 5;
   if (rows == 0) return 0;
   if (!x || !codes || !block_scales || !token_scales) return 1;
   if (num_groups > 0 && !group_offsets) return 1;

@@ -41,6 +41,9 @@ uint16_t oracle_bf16_rne(float f);
  * floor(log2 b) - 2 clamped to [-127, 127]; b == 0 gives -127. */
 int oracle_e8m0_exponent(float b);
 
+/* IEEE binary16 round-to-nearest-even of v, returned as a double. */
+double oracle_fp16_rne(double v);
+
 /* ---- NVFP4, one block, with its internals (for tests) ------------------ */
 
 typedef struct {
@@ -48,13 +51,16 @@ typedef struct {
   float e[2];      /* E4M3 value e_k                                        */
   uint8_t e_byte[2];
   float err[2];    /* summed squared error of the candidate                 */
+  float err16[2];  /* the FP16 fast path's error (four_over_six == 2)       */
   float cand[2][16]; /* signed FP32 candidate dequant values                */
   uint8_t code[2][16]; /* nibbles (sign << 3 | magnitude code)              */
   int choice;      /* 6 or 4                                                */
 } oracle_nvfp4_block_t;
 
 /* Quantize one 16-element block x16 (FP32 values, exactly BF16) under the
- * token scale s.  four_over_six selects whether the 4-candidate competes. */
+ * token scale s.  four_over_six: 0, the 6-candidate only; 1, 4 and 6
+ * compete on the FP32 squared error; 2, 4 and 6 compete on the FP16 fast
+ * path's error (same codes and scales, possibly a different choice). */
 void oracle_nvfp4_block(const float* x16, float s, int four_over_six,
                         oracle_nvfp4_block_t* out);
 

@@ -32,6 +32,8 @@ def pins():
         fn = getattr(L, name)
         fn.argtypes = [ctypes.c_void_p, u32, u32, ctypes.POINTER(u32)]
         fn.restype = ctypes.c_int64
+    L.pin_fp16.argtypes = [ctypes.c_void_p, u32, u32, ctypes.POINTER(u32)]
+    L.pin_fp16.restype = ctypes.c_int64
     L.pin_e8m0.argtypes = [ctypes.c_void_p, u32, u32, u32, ctypes.POINTER(u32)]
     L.pin_e8m0.restype = ctypes.c_int64
     u64p = ctypes.POINTER(ctypes.c_uint64)

@@ -247,3 +247,59 @@ int64_t cmp_fp8(e4m3_encode_fn f, uint32_t lo, uint64_t n, const uint16_t* got,
   *first = first_bad;
   return bad;
 }
+
+/* ---- IEEE binary16 rounding --------------------------------------------- */
+
+typedef double (*fp16_fn)(double);
+
+/* Value of a positive binary16 pattern (0x0000 .. 0x7C00 = infinity) from
+ * its fields: exponent field 0 is subnormal (m * 2^-24), else
+ * (1024 + m) * 2^(field - 25). */
+static double fp16_value(int pattern) {
+  int field = pattern >> 10, m = pattern & 1023;
+  if (field == 31) return INFINITY;
+  return field == 0 ? ldexp((double)m, -24) : ldexp(1024.0 + m, field - 25);
+}
+
+/* Every binary32 pattern in [lo, hi] (non-negative values): the oracle's
+ * rounding must give the nearest binary16 value, found by binary search in
+ * the table of all non-negative patterns, ties to the even pattern; past
+ * the largest finite value the candidate above is infinity. */
+int64_t pin_fp16(fp16_fn f, uint32_t lo, uint32_t hi, uint32_t* first) {
+  static double table[0x7C01];
+  for (int p = 0; p <= 0x7C00; ++p) table[p] = fp16_value(p);
+  int64_t bad = 0;
+  uint32_t first_bad = 0xFFFFFFFFu;
+  int64_t nchunks = ((int64_t)hi - lo) / CHUNK + 1;
+#pragma omp parallel for schedule(dynamic) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t c = 0; c < nchunks; ++c) {
+    uint64_t a0 = (uint64_t)lo + (uint64_t)c * CHUNK;
+    uint64_t a1 = a0 + CHUNK - 1 > hi ? hi : a0 + CHUNK - 1;
+    for (uint64_t u = a0; u <= a1; ++u) {
+      double a = (double)from_bits((uint32_t)u);
+      double want;
+      if (a >= table[0x7BFF] + 16.0) {  /* 65520 and above: infinity */
+        want = INFINITY;
+      } else {
+        int l = 0, h = 0x7BFF;  /* largest pattern with value <= a */
+        while (l < h) {
+          int mid = (l + h + 1) / 2;
+          if (table[mid] <= a) l = mid; else h = mid - 1;
+        }
+        if (table[l] == a || l == 0x7BFF) {
+          want = table[l];
+        } else {
+          double dl = a - table[l], dh = table[l + 1] - a;
+          want = (dl < dh || (dl == dh && (l % 2 == 0))) ? table[l] : table[l + 1];
+        }
+      }
+      double got = f(a);
+      if (!(got == want)) {
+        bad++;
+        if (u < first_bad) first_bad = (uint32_t)u;
+      }
+    }
+  }
+  *first = first_bad;
+  return bad;
+}
