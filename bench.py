@@ -312,7 +312,7 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--parts", default="copy,dequant,resq,ragged,weights",
+    ap.add_argument("--parts", default="copy,dequant,resq,ragged,weights,fp16",
                     help="secondary measurements to run (comma list)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     args = ap.parse_args()
@@ -410,6 +410,27 @@ def main():
             "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
         del wsets, xw
         torch.cuda.empty_cache()
+    if "fp16" in parts:
+        # the FP16 fast path's 4/6 decision (four_over_six = 2): speed on the
+        # headline shape, and how often its choice equals the FP32 one
+        fsets = rotating_nvfp4_sets(x, args.sets)
+        p, _ = time_calls(lambda s: fq.nvfp4_quantize(s[0], 2, out=s[1]), fsets, 1000, 100)
+        secondary["nvfp4_quantize fp16-decision moe_act 8192x7168"] = {
+            "us": round(p * 1e3, 2), "GBps": round(nbytes / (p * 1e-3) / 1e9, 1)}
+        del fsets
+        torch.cuda.empty_cache()
+        agree = {}
+        for name in ("tiny_ref", "moe_act", "expert_weights"):
+            xa = x if name == "moe_act" else workloads.tensor(name, dev)
+            c1, s1, _, _ = fq.nvfp4_quantize(xa, 1, dequant=False)
+            c2, s2, _, _ = fq.nvfp4_quantize(xa, 2, dequant=False)
+            r, h = xa.shape
+            same = (s1 == s2) & (c1.view(r, h // 16, 8) == c2.view(r, h // 16, 8)).all(-1)
+            agree[name] = {"blocks": same.numel(),
+                           "same_choice_frac": round(float(same.float().mean()), 7)}
+            del xa, c1, s1, c2, s2, same
+            torch.cuda.empty_cache()
+        secondary["fp16-decision agreement with the FP32 choice"] = agree
     if secondary:
         print("[bench] secondary: %s" % json.dumps(secondary), file=sys.stderr, flush=True)
 

@@ -7,6 +7,7 @@ not built, or a tensor is not on a GPU, the call raises.
 
 Calls (same names as the C ABI):
   nvfp4_quantize(x, four_over_six=True, offsets=None, dequant=True)
+      four_over_six: True/1, "fp16"/2 (FP16 fast-path decision), False/0
       -> codes u8 [R, H/2], block_scales u8 [R, H/16] (E4M3FN bits),
          token_scales f32 [R], dequant bf16 [R, H] or None
   nvfp4_dequantize(codes, block_scales, token_scales) -> bf16 [R, H]
@@ -78,12 +79,22 @@ def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _mode(four_over_six):
+    if isinstance(four_over_six, str):
+        if four_over_six != "fp16":
+            raise Fp4qError("four_over_six must be True/False/0/1/2 or 'fp16'")
+        return 2
+    return int(four_over_six)  # the library rejects values other than 0, 1, 2
+
+
 def nvfp4_quantize(x, four_over_six=True, offsets=None, dequant=True, out=None):
     """Per-token NVFP4 with Four-Over-Six of a BF16 [rows, hidden] tensor.
 
-    offsets: optional int64 GPU tensor [groups + 1] (ragged routed rows);
-    only rows [offsets[0], offsets[-1]) are written.  out: optional tuple
-    (codes, block_scales, token_scales, dequant-or-None) to write into."""
+    four_over_six: True/1 (4/6 on the FP32 error), "fp16"/2 (4/6 on the FP16
+    fast path's error), False/0 (6 only).  offsets: optional int64 GPU
+    tensor [groups + 1] (ragged routed rows); only rows [offsets[0],
+    offsets[-1]) are written.  out: optional tuple (codes, block_scales,
+    token_scales, dequant-or-None) to write into."""
     _dev(x, "x", torch.bfloat16)
     if x.dim() != 2:
         raise Fp4qError("x must be 2-D [rows, hidden]")
@@ -109,7 +120,7 @@ def nvfp4_quantize(x, four_over_six=True, offsets=None, dequant=True, out=None):
         ng = offsets.numel() - 1
         if ng < 1:
             raise Fp4qError("offsets needs at least two entries")
-    st = lib().nvfp4_quantize(_p(x), rows, hidden, _p(offsets), ng, int(bool(four_over_six)),
+    st = lib().nvfp4_quantize(_p(x), rows, hidden, _p(offsets), ng, _mode(four_over_six),
                               _p(codes), _p(scales), _p(ts), _p(dq), _stream(x))
     _check(st, "nvfp4_quantize")
     return codes, scales, ts, dq

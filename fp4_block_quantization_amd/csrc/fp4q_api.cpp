@@ -38,6 +38,7 @@ fp4q_status nvfp4_quantize(const void* x, int64_t rows, int64_t hidden,
                            void* dequant, void* stream) {
   fp4q_status st = check_shape(rows, hidden, 16);
   if (st != FP4Q_SUCCESS) return st;
+  if (four_over_six < 0 || four_over_six > 2) return FP4Q_ERROR_INVALID_ARGUMENT;
   if (num_groups < 0 || (num_groups == 0 && group_offsets != nullptr))
     return FP4Q_ERROR_INVALID_SHAPE;
   if (num_groups > 0 && group_offsets == nullptr) return FP4Q_ERROR_NULL_POINTER;
@@ -47,7 +48,7 @@ fp4q_status nvfp4_quantize(const void* x, int64_t rows, int64_t hidden,
       (dequant && !aligned(dequant, 16)) || (group_offsets && !aligned(group_offsets, 8)))
     return FP4Q_ERROR_MISALIGNED;
   fp4q::NvQuantArgs a{x,     rows,         hidden,       group_offsets, num_groups,
-                      four_over_six ? 1 : 0, codes, block_scales, token_scales, dequant};
+                      four_over_six, codes, block_scales, token_scales, dequant};
   return launched(fp4q::nvfp4_quantize_launch(a, (hipStream_t)stream));
 }
 
@@ -85,6 +86,7 @@ const char* fp4q_status_string(fp4q_status status) {
     case FP4Q_ERROR_INVALID_SHAPE: return "invalid shape or group count";
     case FP4Q_ERROR_MISALIGNED: return "a pointer lacks its required alignment";
     case FP4Q_ERROR_LAUNCH: return "HIP kernel launch failed";
+    case FP4Q_ERROR_INVALID_ARGUMENT: return "an option is outside its documented values";
   }
   return "unknown status";
 }

@@ -69,7 +69,6 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
-__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 // S_{2:4} choice for every group of four magnitude codes m0..m3 (3 bits
 // each, index = m0 | m1 << 3 | m2 << 6 | m3 << 9): the two largest

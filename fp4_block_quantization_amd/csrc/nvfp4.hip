@@ -164,9 +164,10 @@ struct RowScale {
   float rks6, rks4;  // approximate reciprocals for the bracketed block scale
   bool fast;         // every decode step e s is 0 or >= 2^-127
   bool certify;      // 2^-50 <= s <= 2^40: the error enclosure applies
+  float inv_s;       // fl(1 / s), for the FP16 decision (FOS == 2)
 };
 
-template <bool FOS>
+template <int FOS>
 __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
   RowScale r;
   r.s = __uint_as_float(amax_bits) / (FOS ? 1536.0f : 2688.0f);
@@ -178,6 +179,7 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
   // step 2^-9 s >= 2^-127 has a finite reciprocal.
   r.fast = r.s >= 0x1p-118f || r.s == 0.0f;
   r.certify = r.s >= 0x1p-50f && r.s <= 0x1p40f;
+  r.inv_s = FOS == 2 ? 1.0f / r.s : 0.0f;
   return r;
 }
 
@@ -257,6 +259,28 @@ __device__ __forceinline__ void dequant_block(const uint32_t (&code)[2], float e
   });
 }
 
+// The FP16 fast path's error of one candidate (FOS == 2; NVFP4-RL blog,
+// section 4, "The optimization"): targets y = FP16(x / s) (signed, from
+// fl(x * inv_s)), candidate values g e exact in FP16, differences rounded
+// to FP16, squares (exact in FP32) summed in FP32 in element order --
+// v_fma_mix_f32 of an exact square and the running sum rounds once, as the
+// separate multiply and add would.  Signed targets and signed candidate
+// values give the same squares as magnitudes.
+__device__ __forceinline__ float fp16_error(const half2v (&y)[8], const uint32_t (&code)[2],
+                                            float e) {
+  const _Float16 eh = (_Float16)e;
+  const half2v e2 = {eh, eh};
+  float err = 0.0f;
+  static_for<0, 8>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    const half2v ge = e2m1x2_values_f16<p & 3>(code[p >> 2]) * e2;  // exact
+    const half2v d = y[p] - ge;                                      // FP16 rounding
+    err = __builtin_fmaf((float)d.x, (float)d.x, err);
+    err = __builtin_fmaf((float)d.y, (float)d.y, err);
+  });
+  return err;
+}
+
 // Certified enclosure [lo, hi] of a candidate's FP32 error err (as the
 // definition computes it) from A and the decode step D = fl(e s), for rows
 // with 2^-50 <= s <= 2^40 and e != 0.  With u = 2^-24: v = x r and the
@@ -299,9 +323,10 @@ __device__ __forceinline__ uint32_t element_portable(float x, float e, float r, 
 // definition step by step -- exact division for the block scale, portable
 // rounding -- in loops that re-read the block from memory.  Nothing here
 // stays live across the hot path, so it costs the common case no registers.
-template <bool FOS, bool DQ>
+template <int FOS, bool DQ>
 __device__ __attribute__((noinline)) void tiny_row_block(const uint16_t* __restrict__ xb,
                                                          float b, const float* tab, float s,
+                                                         float inv_s,
                                                          uint8_t* __restrict__ code_bytes,
                                                          uint8_t* __restrict__ scale,
                                                          uint16_t* __restrict__ dqb) {
@@ -318,10 +343,17 @@ __device__ __attribute__((noinline)) void tiny_row_block(const uint16_t* __restr
     for (int i = 0; i < 16; ++i) {
       const float xi = __uint_as_float((uint32_t)xb[i] << 16);
       float c;
-      element_portable(xi, e, r, s, c);
-      const float d = xi - c;
-      const float sq = d * d;
-      err = err + sq;
+      const uint32_t q = element_portable(xi, e, r, s, c);
+      if (FOS == 2) {  // the FP16 fast path's error (see fp16_error)
+        const half2v y = {(_Float16)(fabsf(xi) * inv_s), (_Float16)0.0f};
+        const half2v ge = {(_Float16)(e2m1_value(q & 7u) * e), (_Float16)0.0f};  // exact
+        const half2v d = y - ge;
+        err = __builtin_fmaf((float)d.x, (float)d.x, err);
+      } else {
+        const float d = xi - c;
+        const float sq = d * d;
+        err = err + sq;
+      }
     }
     if (k == 0 || err < best_err) {  // strictly lower error: 4 wins
       best_err = err;
@@ -353,7 +385,7 @@ struct BlockOut {
   uint32_t deq[8];
 };
 
-template <bool FOS, bool DQ>
+template <int FOS, bool DQ>
 __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32_t bbits,
                                                     const RowScale& rs, const float* tab,
                                                     float neg_zero, BlockOut& out) {
@@ -368,24 +400,36 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
   const float e6 = e4m3_value<0>(eb);
   uint32_t code[2];
   float A6;
-  encode_candidate<FOS>(x, tab[eb & 0xFFu], code, A6);
+  encode_candidate<FOS == 1>(x, tab[eb & 0xFFu], code, A6);
   float e = e6;
   uint32_t ebyte = eb & 0xFFu;
   if (FOS) {
     const float e4 = e4m3_value<1>(eb);
     uint32_t code4[2];
     float A4;
-    encode_candidate<true>(x, tab[eb >> 8], code4, A4);
-    // 4 wins only with a strictly lower error; both scales zero: the same
-    // error, keep 6
-    bool four = false, decided = eb == 0u;
-    if (rs.certify && e4 != 0.0f && e6 != 0.0f) {
-      const ErrBounds b6 = err_bounds(A6, e6 * rs.s), b4 = err_bounds(A4, e4 * rs.s);
-      four = b4.hi < b6.lo;
-      decided = four || b4.lo >= b6.hi;
+    encode_candidate<FOS == 1>(x, tab[eb >> 8], code4, A4);
+    bool four;
+    if (FOS == 2) {
+      half2v y[8];
+      static_for<0, 8>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        y[p] = __builtin_convertvector((float2v){x[2 * p] * rs.inv_s, x[2 * p + 1] * rs.inv_s},
+                                       half2v);
+      });
+      four = fp16_error(y, code4, e4) < fp16_error(y, code, e6);  // ties keep 6
+    } else {
+      // 4 wins only with a strictly lower error; both scales zero: the same
+      // error, keep 6
+      four = false;
+      bool decided = eb == 0u;
+      if (rs.certify && e4 != 0.0f && e6 != 0.0f) {
+        const ErrBounds b6 = err_bounds(A6, e6 * rs.s), b4 = err_bounds(A4, e4 * rs.s);
+        four = b4.hi < b6.lo;
+        decided = four || b4.lo >= b6.hi;
+      }
+      if (__builtin_expect(!decided, 0))
+        four = exact_error(x, code4, e4, rs.s, neg_zero) < exact_error(x, code, e6, rs.s, neg_zero);
     }
-    if (__builtin_expect(!decided, 0))
-      four = exact_error(x, code4, e4, rs.s, neg_zero) < exact_error(x, code, e6, rs.s, neg_zero);
     code[0] = four ? code4[0] : code[0];
     code[1] = four ? code4[1] : code[1];
     e = four ? e4 : e;
@@ -398,7 +442,7 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
 }
 
 // One block, written directly (one lane, 32 contiguous dequant bytes).
-template <bool FOS, bool DQ>
+template <int FOS, bool DQ>
 __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bbits,
                                                const RowScale& rs, const float* tab,
                                                float neg_zero, const uint4* __restrict__ xin,
@@ -408,6 +452,7 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
                                                uint4* stage = nullptr) {
   if (__builtin_expect(!rs.fast, 0)) {
     tiny_row_block<FOS, DQ>((const uint16_t*)(xin + 2 * blk), __uint_as_float(bbits), tab, rs.s,
+                            rs.inv_s,
                             (uint8_t*)(codes + blk), scales + blk,
                             DQ ? (uint16_t*)(dq + 2 * blk) : nullptr);
     return;
@@ -539,7 +584,7 @@ __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, cons
   }
 }
 
-template <bool FOS, bool DQ, int NB>
+template <int FOS, bool DQ, int NB>
 __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk, int W,
     int R, int64_t ngrp, const int64_t* __restrict__ offs, int64_t ngroups,
@@ -642,7 +687,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
 
 // Any row length: one wavefront per row; a first pass for the amax, a
 // second pass (served mostly by L2) for the blocks.
-template <bool FOS, bool DQ>
+template <int FOS, bool DQ>
 __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk,
     const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
@@ -730,7 +775,7 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
   }
 }
 
-template <bool FOS, bool DQ>
+template <int FOS, bool DQ>
 hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const int nblk = (int)(a.hidden / 16);
   const uint4* x = (const uint4*)a.x;
@@ -781,9 +826,11 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t st) {
-  if (a.four_over_six)
-    return a.dequant ? launch_quantize<true, true>(a, st) : launch_quantize<true, false>(a, st);
-  return a.dequant ? launch_quantize<false, true>(a, st) : launch_quantize<false, false>(a, st);
+  if (a.four_over_six == 2)
+    return a.dequant ? launch_quantize<2, true>(a, st) : launch_quantize<2, false>(a, st);
+  if (a.four_over_six == 1)
+    return a.dequant ? launch_quantize<1, true>(a, st) : launch_quantize<1, false>(a, st);
+  return a.dequant ? launch_quantize<0, true>(a, st) : launch_quantize<0, false>(a, st);
 }
 
 hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,

@@ -43,8 +43,10 @@ typedef enum {
                                    or a size too large to index              */
   FP4Q_ERROR_MISALIGNED = 3,    /* a pointer lacks the alignment stated at
                                    its argument                              */
-  FP4Q_ERROR_LAUNCH = 4         /* the HIP launch failed (no device, bad
+  FP4Q_ERROR_LAUNCH = 4,        /* the HIP launch failed (no device, bad
                                    stream, ...)                             */
+  FP4Q_ERROR_INVALID_ARGUMENT = 5 /* an option outside its documented
+                                     values (four_over_six not 0, 1 or 2)   */
 } fp4q_status;
 
 /*
@@ -78,8 +80,20 @@ typedef enum {
  *                 kernel clamps the range to [0, rows), so wrong offsets
  *                 cannot cause an out-of-bounds access.
  *   num_groups    0 when group_offsets is NULL, else >= 1.
- *   four_over_six 1: s = amax/1536 and the 4/6 choice per block;
+ *   four_over_six 1: s = amax/1536 and the 4/6 choice per block on the
+ *                    FP32 squared error above;
+ *                 2: the same, but the choice is made on the FP16 fast
+ *                    path's error ("NVFP4-RL", section 4, "The
+ *                    optimization": products g*e in FP16, where they are
+ *                    exact; the target scaled down by the inverse token
+ *                    scale): y_i = FP16(|x_i| * fl(1/s)), per candidate
+ *                    err16 = sum in element order, in FP32, of
+ *                    FP16(y_i - g_i*e_k)^2; 4 iff err16_4 < err16_6.  Codes,
+ *                    scales and dequant values are those of the chosen
+ *                    candidate, as with 1; on the workloads measured the
+ *                    choice differs from 1's in about 0.1% of blocks;
  *                 0: s = amax/2688 and the 6 candidate only.
+ *                 Other values: FP4Q_ERROR_INVALID_ARGUMENT.
  *   codes         uint8 [rows, hidden/2], 8-byte aligned: E2M1 nibbles,
  *                 sign in bit 3, element 2i in the low nibble of byte i.
  *   block_scales  uint8 [rows, hidden/16]: OCP E4M3FN bit patterns.

@@ -12,7 +12,7 @@ import fp4_block_quantization_amd as fq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-SUCCESS, NULL, SHAPE, MISALIGNED, LAUNCH = 0, 1, 2, 3, 4
+SUCCESS, NULL, SHAPE, MISALIGNED, LAUNCH, INVALID = 0, 1, 2, 3, 4, 5
 
 
 def declared_functions():
@@ -36,8 +36,8 @@ def test_library_exports_every_declared_call():
 
 def test_status_strings():
     L = fq.lib()
-    for s in range(5):
-        assert L.fp4q_status_string(s)
+    for s in range(6):
+        assert L.fp4q_status_string(s) != b"unknown status"
     assert L.fp4q_status_string(99) == b"unknown status"
 
 
@@ -69,6 +69,8 @@ def test_nvfp4_quantize_rejects():
     assert nvq(ts=P(0x10002)) == MISALIGNED
     assert nvq(offs=P(0x10004), ng=1) == MISALIGNED
     assert nvq(rows=1 << 33) == SHAPE
+    assert nvq(fos=3) == INVALID
+    assert nvq(fos=-1) == INVALID
     # empty input: success, nothing launched, pointers may be NULL
     assert nvq(rows=0, x=None, codes=None, scales=None, ts=None, dq=None) == SUCCESS
 

@@ -88,7 +88,7 @@ def edge_rows(H, seed):
 HIDDEN = [16, 32, 48, 1008, 1024, 1040, 2048, 2064, 7168, 8192, 8208, 16400, 32784]
 
 
-@pytest.mark.parametrize("fos", [True, False])
+@pytest.mark.parametrize("fos", [1, 0, 2])
 @pytest.mark.parametrize("H", HIDDEN)
 def test_nvfp4_edge_suite(H, fos):
     check_nvfp4(edge_rows(H, seed=H), fos, label="edge H=%d" % H)
@@ -116,9 +116,18 @@ def test_golden_blocks_on_gpu():
 
 # ------------------------------------------------------ named workloads --
 
-@pytest.mark.parametrize("fos", [True, False])
+@pytest.mark.parametrize("fos", [1, 0, 2])
 def test_tiny_ref(fos):
     check_nvfp4(workloads.rows("tiny_ref"), fos, label="tiny_ref")
+
+
+def test_moe_act_full_size_fp16_decision():
+    # the FP16 fast path's 4/6 choice (four_over_six = 2) at full size
+    check_nvfp4(workloads.rows("moe_act"), 2, label="moe_act fp16-decision")
+
+
+def test_expert_weights_fp16_decision_rows():
+    check_nvfp4(workloads.rows("expert_weights", 0, 4096), 2, label="expert_weights fp16")
 
 
 def test_moe_act_full_size():
