@@ -51,6 +51,11 @@ def lib():
         L.mxfp4_resq_quantize_ref.argtypes = [vp, c_i64, c_i64,
                                               vp, vp, vp, vp, vp]
         L.mxfp4_resq_quantize_ref.restype = ctypes.c_int
+        L.mxfp4_resq_dense_quantize_ref.argtypes = [vp, c_i64, c_i64, vp, vp, vp, vp]
+        L.mxfp4_resq_dense_quantize_ref.restype = ctypes.c_int
+        L.mxfp4_resq_reconstruct_ref.argtypes = [vp, vp, vp, vp, vp, c_i64, c_i64,
+                                                 ctypes.c_int, vp]
+        L.mxfp4_resq_reconstruct_ref.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -183,3 +188,33 @@ def mxfp4_resq_quantize(x_bits):
                                        _ptr(scales), _ptr(rc), _ptr(rm), _ptr(rs))
     _check(st, "mxfp4_resq_quantize_ref")
     return codes, scales, rc, rm, rs
+
+
+def mxfp4_resq_dense_quantize(x_bits):
+    """Rollout-ResQ-Dense.  Returns (codes [R,H/2], scales [R,H/32],
+    res_codes [R,H/2], res_scales [R,H/32]), all uint8."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, hidden = x.shape
+    codes = np.zeros((rows, hidden // 2), np.uint8)
+    scales = np.zeros((rows, hidden // 32), np.uint8)
+    rc = np.zeros((rows, hidden // 2), np.uint8)
+    rs = np.zeros((rows, hidden // 32), np.uint8)
+    st = lib().mxfp4_resq_dense_quantize_ref(_ptr(x), rows, hidden, _ptr(codes), _ptr(scales),
+                                             _ptr(rc), _ptr(rs))
+    _check(st, "mxfp4_resq_dense_quantize_ref")
+    return codes, scales, rc, rs
+
+
+def mxfp4_resq_reconstruct(codes, scales, res_codes=None, res_meta=None, res_scales=None,
+                           residual=0):
+    """FP32 [R, H]: DQ(Q(X)) (+ the sparse (1) or dense (2) residual)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, hidden = codes.shape[0], codes.shape[1] * 2
+    arrs = [None if a is None else np.ascontiguousarray(a, dtype=np.uint8)
+            for a in (res_codes, res_meta, res_scales)]
+    out = np.zeros((rows, hidden), np.float32)
+    st = lib().mxfp4_resq_reconstruct_ref(_ptr(codes), _ptr(scales), *[_ptr(a) for a in arrs],
+                                          rows, hidden, int(residual), _ptr(out))
+    _check(st, "mxfp4_resq_reconstruct_ref")
+    return out

@@ -439,3 +439,83 @@ int mxfp4_resq_quantize_ref(const uint16_t* x, int64_t rows, int64_t hidden,
   }
   return 0;
 }
+
+/* Rollout-ResQ-Dense (HiFloat4 page, the dense residual correction
+ * Q(X)Q(W)^T + Q(dX)Q(W)^T that the sparse variant is compared with): the
+ * same primary and residual quantization, with every residual code kept.
+ * res_codes is [rows, hidden/2], packed like the primary codes. */
+int mxfp4_resq_dense_quantize_ref(const uint16_t* x, int64_t rows, int64_t hidden,
+                                  uint8_t* codes, uint8_t* scales,
+                                  uint8_t* res_codes, uint8_t* res_scales) {
+  if (rows < 0 || hidden <= 0 || hidden % 32 != 0) return 2;
+  if (rows == 0) return 0;
+  if (!x || !codes || !scales || !res_codes || !res_scales) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t j = 0; j < hidden / 32; ++j) {
+      float xb[32], dq[32], delta[32], rdq[32];
+      uint8_t nib[32], rnib[32];
+      for (int i = 0; i < 32; ++i)
+        xb[i] = bf16_bits_to_float(x[r * hidden + j * 32 + i]);
+      int k = mx_block(xb, nib, dq);
+      for (int i = 0; i < 32; ++i) delta[i] = xb[i] - dq[i];
+      int kr = mx_block(delta, rnib, rdq);
+      scales[r * (hidden / 32) + j] = (uint8_t)(k + 127);
+      res_scales[r * (hidden / 32) + j] = (uint8_t)(kr + 127);
+      for (int i = 0; i < 32; i += 2) {
+        codes[r * (hidden / 2) + j * 16 + i / 2] = (uint8_t)(nib[i] | (nib[i + 1] << 4));
+        res_codes[r * (hidden / 2) + j * 16 + i / 2] = (uint8_t)(rnib[i] | (rnib[i + 1] << 4));
+      }
+    }
+  }
+  return 0;
+}
+
+/* The dequantized value of an MX code under the E8M0 byte: +-g * 2^(byte -
+ * 127), exact in FP32 for every code and byte. */
+static float mx_value(uint8_t nibble, uint8_t scale_byte) {
+  float m = ldexpf(oracle_e2m1_value(nibble & 7), (int)scale_byte - 127);
+  return (nibble & 8) ? -m : m;
+}
+
+/* Reconstruction of the rollout input from what Rollout-ResQ stores (the
+ * HiFloat4 page's Q(X) + S(Q(dX)), or + Q(dX) for the dense variant):
+ *   residual 0: X_hat = DQ(Q(X))                      (primary only)
+ *   residual 1: X_hat = DQ(Q(X)) + DQ(S(Q(dX)))        res_codes/res_meta
+ *                                                      of the sparse call
+ *   residual 2: X_hat = DQ(Q(X)) + DQ(Q(dX))           res_codes of the
+ *                                                      dense call
+ * Both terms are exact FP32 values; their sum is one FP32 addition.  The
+ * two elements S drops in each group of four contribute 0. */
+int mxfp4_resq_reconstruct_ref(const uint8_t* codes, const uint8_t* scales,
+                               const uint8_t* res_codes, const uint8_t* res_meta,
+                               const uint8_t* res_scales, int64_t rows, int64_t hidden,
+                               int residual, float* out) {
+  if (rows < 0 || hidden <= 0 || hidden % 32 != 0) return 2;
+  if (residual < 0 || residual > 2) return 5;
+  if (rows == 0) return 0;
+  if (!codes || !scales || !out) return 1;
+  if (residual != 0 && (!res_codes || !res_scales)) return 1;
+  if (residual == 1 && !res_meta) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t i = 0; i < hidden; ++i) {
+      int64_t blk = r * (hidden / 32) + i / 32;
+      uint8_t byte = codes[r * (hidden / 2) + i / 2];
+      float v = mx_value((i % 2) ? (byte >> 4) : (byte & 15), scales[blk]);
+      float rv = 0.0f;
+      if (residual == 2) {
+        uint8_t rb = res_codes[r * (hidden / 2) + i / 2];
+        rv = mx_value((i % 2) ? (rb >> 4) : (rb & 15), res_scales[blk]);
+      } else if (residual == 1) {
+        int64_t group = i / 4; /* within the row */
+        uint8_t mb = res_meta[r * (hidden / 8) + group / 2];
+        int meta = (group % 2) ? (mb >> 4) : (mb & 15);
+        int i0 = meta & 3, i1 = meta >> 2, pos = (int)(i % 4);
+        uint8_t kept = res_codes[r * (hidden / 4) + group];
+        if (pos == i0) rv = mx_value(kept & 15, res_scales[blk]);
+        else if (pos == i1) rv = mx_value(kept >> 4, res_scales[blk]);
+      }
+      out[r * hidden + i] = v + rv;
+    }
+  }
+  return 0;
+}

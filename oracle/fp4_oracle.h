@@ -80,6 +80,18 @@ int mxfp4_resq_quantize_ref(const uint16_t* x, int64_t rows, int64_t hidden,
                             uint8_t* res_codes, uint8_t* res_meta,
                             uint8_t* res_scales);
 
+/* Rollout-ResQ-Dense: res_codes [rows, hidden/2] keeps every residual code. */
+int mxfp4_resq_dense_quantize_ref(const uint16_t* x, int64_t rows, int64_t hidden,
+                                  uint8_t* codes, uint8_t* scales,
+                                  uint8_t* res_codes, uint8_t* res_scales);
+
+/* FP32 reconstruction DQ(Q(X)) (+ DQ(S(Q(dX))) for residual 1, + DQ(Q(dX))
+ * for residual 2). */
+int mxfp4_resq_reconstruct_ref(const uint8_t* codes, const uint8_t* scales,
+                               const uint8_t* res_codes, const uint8_t* res_meta,
+                               const uint8_t* res_scales, int64_t rows, int64_t hidden,
+                               int residual, float* out);
+
 #ifdef __cplusplus
 }
 #endif
