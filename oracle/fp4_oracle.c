@@ -485,7 +485,8 @@ static float mx_value(uint8_t nibble, uint8_t scale_byte) {
  *   residual 2: X_hat = DQ(Q(X)) + DQ(Q(dX))           res_codes of the
  *                                                      dense call
  * Both terms are exact FP32 values; their sum is one FP32 addition.  The
- * two elements S drops in each group of four contribute 0. */
+ * two elements S drops in each group of four contribute +0.  With the
+ * primary only there is no addition, so a negative zero stays -0. */
 int mxfp4_resq_reconstruct_ref(const uint8_t* codes, const uint8_t* scales,
                                const uint8_t* res_codes, const uint8_t* res_meta,
                                const uint8_t* res_scales, int64_t rows, int64_t hidden,
@@ -514,7 +515,7 @@ int mxfp4_resq_reconstruct_ref(const uint8_t* codes, const uint8_t* scales,
         if (pos == i0) rv = mx_value(kept & 15, res_scales[blk]);
         else if (pos == i1) rv = mx_value(kept >> 4, res_scales[blk]);
       }
-      out[r * hidden + i] = v + rv;
+      out[r * hidden + i] = residual == 0 ? v : v + rv; /* primary only: DQ itself */
     }
   }
   return 0;
