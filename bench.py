@@ -312,7 +312,7 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--parts", default="copy,dequant,resq,ragged,weights,fp16",
+    ap.add_argument("--parts", default="copy,dequant,resq,resq_dense,ragged,weights,fp16",
                     help="secondary measurements to run (comma list)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     args = ap.parse_args()
@@ -387,6 +387,39 @@ def main():
         secondary["mxfp4_resq_quantize resq_act 8192x7168"] = {
             "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
         del msets, mouts, xr
+        torch.cuda.empty_cache()
+    if "resq_dense" in parts:
+        # Rollout-ResQ-Dense and the reconstruction error of the three
+        # variants on the resq_act workload (MSE over all elements, FP64)
+        xr = workloads.tensor("resq_act", dev)
+        msets = [xr] + [xr.clone() for _ in range(3)]
+        douts = [fq.mxfp4_resq_dense_quantize(m) for m in msets]
+        p, _ = time_calls(lambda i: fq.mxfp4_resq_dense_quantize(msets[i], out=douts[i]),
+                          list(range(4)), 200, 20)
+        r_, h_ = xr.shape
+        b = r_ * h_ * 2 + r_ * h_ // 2 * 2 + r_ * h_ // 32 * 2
+        secondary["mxfp4_resq_dense_quantize resq_act 8192x7168"] = {
+            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+        sp = fq.mxfp4_resq_quantize(xr)
+        de = douts[0]
+        xf = xr.float().double()
+        mse = {}
+        recon = {"primary only": (sp[0], sp[1], None, None, None, 0),
+                 "primary + S2:4 residual": (sp[0], sp[1], sp[2], sp[3], sp[4], 1),
+                 "primary + dense residual": (de[0], de[1], de[2], None, de[3], 2)}
+        xh = torch.empty((r_, h_), dtype=torch.float32, device=dev)
+        for name, a in recon.items():
+            fq.mxfp4_resq_reconstruct(*a[:5], residual=a[5], out=xh)
+            err = (xf - xh.double())
+            mse[name] = {"mse": float((err * err).mean()),
+                         "rel_mse": float((err * err).sum() / (xf * xf).sum())}
+        p, _ = time_calls(lambda i: fq.mxfp4_resq_reconstruct(
+            sp[0], sp[1], sp[2], sp[3], sp[4], residual=1, out=xh), [0], 200, 20)
+        b = r_ * h_ // 2 + r_ * h_ // 32 * 2 + r_ * h_ // 4 + r_ * h_ // 8 + r_ * h_ * 4
+        secondary["mxfp4_resq_reconstruct (S2:4) resq_act 8192x7168"] = {
+            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+        secondary["Rollout-ResQ reconstruction error resq_act"] = mse
+        del msets, douts, sp, de, xf, xh, xr
         torch.cuda.empty_cache()
     if "ragged" in parts:
         # ragged routed, quantize only

@@ -14,6 +14,11 @@ Calls (same names as the C ABI):
   mxfp4_resq_quantize(x)
       -> codes u8 [R, H/2], scales u8 [R, H/32], res_codes u8 [R, H/4],
          res_meta u8 [R, H/8], res_scales u8 [R, H/32]
+  mxfp4_resq_dense_quantize(x)
+      -> codes u8 [R, H/2], scales u8 [R, H/32], res_codes u8 [R, H/2],
+         res_scales u8 [R, H/32]
+  mxfp4_resq_reconstruct(codes, scales, res_codes, res_meta, res_scales,
+                         residual) -> f32 [R, H]
 """
 import ctypes
 import os
@@ -23,7 +28,7 @@ import torch
 from . import _build
 
 __all__ = ["lib", "nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
-           "Fp4qError", "LIB_PATH"]
+           "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "Fp4qError", "LIB_PATH"]
 
 LIB_PATH = _build.LIB_PATH
 _lib = None
@@ -49,6 +54,10 @@ def lib():
         L.nvfp4_dequantize.restype = ci
         L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mxfp4_resq_quantize.restype = ci
+        L.mxfp4_resq_dense_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+        L.mxfp4_resq_dense_quantize.restype = ci
+        L.mxfp4_resq_reconstruct.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, vp, vp]
+        L.mxfp4_resq_reconstruct.restype = ci
         L.fp4q_status_string.argtypes = [ci]
         L.fp4q_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -159,4 +168,42 @@ def mxfp4_resq_quantize(x, out=None):
         _dev(t, n, torch.uint8)
     st = lib().mxfp4_resq_quantize(_p(x), rows, hidden, *[_p(t) for t in out], _stream(x))
     _check(st, "mxfp4_resq_quantize")
+    return out
+
+
+def mxfp4_resq_dense_quantize(x, out=None):
+    """MXFP4 + Rollout-ResQ-Dense residual (every residual code kept)."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise Fp4qError("x must be 2-D [rows, hidden]")
+    rows, hidden = x.shape
+    if out is None:
+        kw = dict(dtype=torch.uint8, device=x.device)
+        out = (torch.empty((rows, hidden // 2), **kw), torch.empty((rows, hidden // 32), **kw),
+               torch.empty((rows, hidden // 2), **kw), torch.empty((rows, hidden // 32), **kw))
+    for t, n in zip(out, ("codes", "scales", "res_codes", "res_scales")):
+        _dev(t, n, torch.uint8)
+    st = lib().mxfp4_resq_dense_quantize(_p(x), rows, hidden, *[_p(t) for t in out], _stream(x))
+    _check(st, "mxfp4_resq_dense_quantize")
+    return out
+
+
+def mxfp4_resq_reconstruct(codes, scales, res_codes=None, res_meta=None, res_scales=None,
+                           residual=0, out=None):
+    """FP32 X_hat = DQ(Q(X)) (+ DQ(S(Q(dX))) for residual 1, + DQ(Q(dX)) for
+    residual 2, from the sparse or dense quantize outputs)."""
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    for t, n in ((res_codes, "res_codes"), (res_meta, "res_meta"), (res_scales, "res_scales")):
+        if t is not None:
+            _dev(t, n, torch.uint8)
+    rows = codes.shape[0]
+    hidden = codes.numel() // max(rows, 1) * 2
+    if out is None:
+        out = torch.empty((rows, hidden), dtype=torch.float32, device=codes.device)
+    _dev(out, "out", torch.float32)
+    st = lib().mxfp4_resq_reconstruct(_p(codes), _p(scales), _p(res_codes), _p(res_meta),
+                                      _p(res_scales), rows, hidden, int(residual), _p(out),
+                                      _stream(codes))
+    _check(st, "mxfp4_resq_reconstruct")
     return out

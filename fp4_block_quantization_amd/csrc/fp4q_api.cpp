@@ -79,6 +79,38 @@ fp4q_status mxfp4_resq_quantize(const void* x, int64_t rows, int64_t hidden, uin
                                           res_scales, (hipStream_t)stream));
 }
 
+fp4q_status mxfp4_resq_dense_quantize(const void* x, int64_t rows, int64_t hidden,
+                                      uint8_t* codes, uint8_t* scales, uint8_t* res_codes,
+                                      uint8_t* res_scales, void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 32);
+  if (st != FP4Q_SUCCESS) return st;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!x || !codes || !scales || !res_codes || !res_scales) return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(res_codes, 16))
+    return FP4Q_ERROR_MISALIGNED;
+  return launched(fp4q::mxfp4_resq_dense_launch(x, rows, hidden, codes, scales, res_codes,
+                                                res_scales, (hipStream_t)stream));
+}
+
+fp4q_status mxfp4_resq_reconstruct(const uint8_t* codes, const uint8_t* scales,
+                                   const uint8_t* res_codes, const uint8_t* res_meta,
+                                   const uint8_t* res_scales, int64_t rows, int64_t hidden,
+                                   int residual, float* out, void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 32);
+  if (st != FP4Q_SUCCESS) return st;
+  if (residual < 0 || residual > 2) return FP4Q_ERROR_INVALID_ARGUMENT;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!codes || !scales || !out) return FP4Q_ERROR_NULL_POINTER;
+  if (residual != 0 && (!res_codes || !res_scales)) return FP4Q_ERROR_NULL_POINTER;
+  if (residual == 1 && !res_meta) return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(codes, 16) || !aligned(out, 16) ||
+      (residual == 1 && !aligned(res_codes, 8)) || (residual == 2 && !aligned(res_codes, 16)))
+    return FP4Q_ERROR_MISALIGNED;
+  return launched(fp4q::mxfp4_reconstruct_launch(codes, scales, res_codes, res_meta, res_scales,
+                                                 rows, hidden, residual, out,
+                                                 (hipStream_t)stream));
+}
+
 const char* fp4q_status_string(fp4q_status status) {
   switch (status) {
     case FP4Q_SUCCESS: return "success";

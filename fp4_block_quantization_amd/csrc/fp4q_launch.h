@@ -35,4 +35,12 @@ hipError_t mxfp4_resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_
                              uint8_t* scales, uint8_t* res_codes, uint8_t* res_meta,
                              uint8_t* res_scales, hipStream_t stream);
 
+hipError_t mxfp4_resq_dense_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
+                                   uint8_t* scales, uint8_t* res_codes, uint8_t* res_scales,
+                                   hipStream_t stream);
+hipError_t mxfp4_reconstruct_launch(const uint8_t* codes, const uint8_t* scales,
+                                    const uint8_t* res_codes, const uint8_t* res_meta,
+                                    const uint8_t* res_scales, int64_t rows, int64_t hidden,
+                                    int residual, float* out, hipStream_t stream);
+
 }  // namespace fp4q

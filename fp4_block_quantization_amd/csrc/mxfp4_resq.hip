@@ -128,8 +128,8 @@ __device__ __forceinline__ uint32_t select_2of4(uint32_t rw, const uint16_t* tab
 #endif
 constexpr int kUnitsPerLane = FP4Q_MX_UNITS;
 
-__device__ __forceinline__ void resq_unit(const uint4 a, const uint16_t* tab, uint32_t& cw,
-                                          uint32_t& rc, uint32_t& meta, int& k, int& kr) {
+__device__ __forceinline__ void resq_unit(const uint4 a, uint32_t& cw, uint32_t& rw, int& k,
+                                          int& kr) {
   const uint32_t w[4] = {a.x, a.y, a.z, a.w};
   // primary scale: packed 16-bit max of the sign-cleared BF16 patterns
   const u16x2 mw = __builtin_elementwise_max(
@@ -161,24 +161,29 @@ __device__ __forceinline__ void resq_unit(const uint4 a, const uint16_t* tab, ui
   });
   kr = mx_exponent(quad_max(__float_as_uint(rmax)));
   const float rdown = __uint_as_float((uint32_t)(127 - kr) << 23);
-  uint32_t rw = 0u;
+  rw = 0u;
   static_for<0, 4>([&](auto P) {
     constexpr int p = decltype(P)::value;
     rw = cvt_e2m1x2<p>(rw, v[2 * p] * rdown, v[2 * p + 1] * rdown);
   });
-  rc = select_2of4(rw, tab, meta);
 }
 
+// DENSE = false: Rollout-ResQ with S_{2:4} (res_codes uint16 per unit,
+// res_meta one byte per unit); DENSE = true: Rollout-ResQ-Dense (res_codes
+// uint32 per unit, packed like the primary codes).
+template <bool DENSE>
 __global__ __launch_bounds__(256) void mxfp4_resq_units(
     const uint4* __restrict__ x, int64_t u0, int64_t u_end, uint32_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint16_t* __restrict__ res_codes,
+    uint8_t* __restrict__ scales, void* __restrict__ res_codes,
     uint8_t* __restrict__ res_meta, uint8_t* __restrict__ res_scales) {
   // the 2:4 table (8 KiB) into LDS
-  __shared__ uint4 tab_lds[512];
-  const uint4* tab_src = reinterpret_cast<const uint4*>(kSelTable.e);
-  tab_lds[threadIdx.x] = tab_src[threadIdx.x];
-  tab_lds[threadIdx.x + 256] = tab_src[threadIdx.x + 256];
-  __syncthreads();
+  __shared__ uint4 tab_lds[DENSE ? 1 : 512];
+  if (!DENSE) {
+    const uint4* tab_src = reinterpret_cast<const uint4*>(kSelTable.e);
+    tab_lds[threadIdx.x] = tab_src[threadIdx.x];
+    tab_lds[threadIdx.x + 256] = tab_src[threadIdx.x + 256];
+    __syncthreads();
+  }
   const uint16_t* tab = reinterpret_cast<const uint16_t*>(tab_lds);
 
   const int lane = threadIdx.x & 63;
@@ -191,8 +196,6 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   const int nv = left < 64 * kUnitsPerLane ? (int)left : 64 * kUnitsPerLane;
   const uint4* xw = x + ub;  // wave-uniform bases, 32-bit lane offsets
   uint32_t* cw_out = codes + ub;
-  uint16_t* rc_out = res_codes + ub;
-  uint8_t* meta_out = res_meta + ub;
   uint8_t* sc_out = scales + (ub >> 2);
   uint8_t* rs_out = res_scales + (ub >> 2);
   uint4 a[kUnitsPerLane];
@@ -212,13 +215,21 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   for (int n = 0; n < kUnitsPerLane; ++n) {
     const int j = lane + 64 * n;
     if (64 * n < nv) {  // wave-uniform
-      uint32_t cw, rc, meta;
+      uint32_t cw, rw;
       int k, kr;
-      resq_unit(a[n], tab, cw, rc, meta, k, kr);
+      resq_unit(a[n], cw, rw, k, kr);
+      if (DENSE) {
+        if (j < nv) store_out(&(reinterpret_cast<uint32_t*>(res_codes) + ub)[j], rw);
+      } else {
+        uint32_t meta;
+        const uint32_t rc = select_2of4(rw, tab, meta);
+        if (j < nv) {
+          store_small(&(reinterpret_cast<uint16_t*>(res_codes) + ub)[j], (uint16_t)rc);
+          store_small(&(res_meta + ub)[j], (uint8_t)meta);
+        }
+      }
       if (j < nv) {
         store_out(&cw_out[j], cw);
-        store_small(&rc_out[j], (uint16_t)rc);
-        store_small(&meta_out[j], (uint8_t)meta);
         if ((lane & 3) == 0) {
           store_small(&sc_out[j >> 2], (uint8_t)(k + 127));
           store_small(&rs_out[j >> 2], (uint8_t)(kr + 127));
@@ -228,19 +239,96 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   }
 }
 
+// The residual of one unit as a dense code word: the two kept codes of each
+// group of four at the positions their metadata names, zeros elsewhere.
+__device__ __forceinline__ uint32_t expand_2of4(uint32_t rc, uint32_t meta) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t kb = (rc >> (8 * h)) & 0xFFu, m = (meta >> (4 * h)) & 15u;
+    w |= ((kb & 15u) << (4 * (m & 3u) + 16 * h)) | ((kb >> 4) << (4 * (m >> 2) + 16 * h));
+  }
+  return w;
+}
+
+// X_hat = DQ(Q(X)) (+ the residual): one lane per 8-element unit; every
+// dequantized value is +-g 2^k, exact through the scaled decode, and the
+// two terms are added once in FP32.
+template <int RES>
+__global__ __launch_bounds__(256) void mxfp4_reconstruct_units(
+    const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const void* __restrict__ res_codes, const uint8_t* __restrict__ res_meta,
+    const uint8_t* __restrict__ res_scales, int64_t u0, int64_t u_end,
+    uint4* __restrict__ out) {
+  const int64_t u = u0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= u_end) return;
+  const uint32_t cw = codes[u];
+  const float up = __uint_as_float((uint32_t)scales[u >> 2] << 23);  // E8M0 as a scale operand
+  uint32_t rw = 0u;
+  float rup = 0.0f;
+  if (RES == 2) rw = reinterpret_cast<const uint32_t*>(res_codes)[u];
+  if (RES == 1) rw = expand_2of4(reinterpret_cast<const uint16_t*>(res_codes)[u], res_meta[u]);
+  if (RES != 0) rup = __uint_as_float((uint32_t)res_scales[u >> 2] << 23);
+  uint32_t o[8];
+  static_for<0, 4>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    float2v v = e2m1x2_values_scaled<p>(cw, up);
+    if (RES != 0) v = v + e2m1x2_values_scaled<p>(rw, rup);
+    o[2 * p] = __float_as_uint(v.x);
+    o[2 * p + 1] = __float_as_uint(v.y);
+  });
+  out[2 * u] = make_uint4(o[0], o[1], o[2], o[3]);
+  out[2 * u + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 }  // namespace
 
-hipError_t mxfp4_resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
-                             uint8_t* scales, uint8_t* res_codes, uint8_t* res_meta,
-                             uint8_t* res_scales, hipStream_t st) {
+template <bool DENSE>
+hipError_t resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
+                       uint8_t* scales, void* res_codes, uint8_t* res_meta, uint8_t* res_scales,
+                       hipStream_t st) {
   const int64_t nunits = rows * (hidden / 8);  // a multiple of 4
   const int64_t max_units = FP4Q_MAX_LAUNCH_ITEMS / 256 * 256 * kUnitsPerLane;
   for (int64_t u0 = 0; u0 < nunits; u0 += max_units) {
     const int64_t n = nunits - u0 < max_units ? nunits - u0 : max_units;
     constexpr int64_t per_wg = 256 * kUnitsPerLane;
     const dim3 grid((unsigned)((n + per_wg - 1) / per_wg)), block(256);
-    hipLaunchKernelGGL(mxfp4_resq_units, grid, block, 0, st, (const uint4*)x, u0, u0 + n,
-                       (uint32_t*)codes, scales, (uint16_t*)res_codes, res_meta, res_scales);
+    hipLaunchKernelGGL(mxfp4_resq_units<DENSE>, grid, block, 0, st, (const uint4*)x, u0, u0 + n,
+                       (uint32_t*)codes, scales, res_codes, res_meta, res_scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t mxfp4_resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
+                             uint8_t* scales, uint8_t* res_codes, uint8_t* res_meta,
+                             uint8_t* res_scales, hipStream_t st) {
+  return resq_launch<false>(x, rows, hidden, codes, scales, res_codes, res_meta, res_scales, st);
+}
+
+hipError_t mxfp4_resq_dense_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
+                                   uint8_t* scales, uint8_t* res_codes, uint8_t* res_scales,
+                                   hipStream_t st) {
+  return resq_launch<true>(x, rows, hidden, codes, scales, res_codes, nullptr, res_scales, st);
+}
+
+hipError_t mxfp4_reconstruct_launch(const uint8_t* codes, const uint8_t* scales,
+                                    const uint8_t* res_codes, const uint8_t* res_meta,
+                                    const uint8_t* res_scales, int64_t rows, int64_t hidden,
+                                    int residual, float* out, hipStream_t st) {
+  const int64_t nunits = rows * (hidden / 8);
+  const int64_t max_units = FP4Q_MAX_LAUNCH_ITEMS / 256 * 256;
+  for (int64_t u0 = 0; u0 < nunits; u0 += max_units) {
+    const int64_t n = nunits - u0 < max_units ? nunits - u0 : max_units;
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    if (residual == 2)
+      hipLaunchKernelGGL(mxfp4_reconstruct_units<2>, grid, block, 0, st, (const uint32_t*)codes,
+                         scales, res_codes, res_meta, res_scales, u0, u0 + n, (uint4*)out);
+    else if (residual == 1)
+      hipLaunchKernelGGL(mxfp4_reconstruct_units<1>, grid, block, 0, st, (const uint32_t*)codes,
+                         scales, res_codes, res_meta, res_scales, u0, u0 + n, (uint4*)out);
+    else
+      hipLaunchKernelGGL(mxfp4_reconstruct_units<0>, grid, block, 0, st, (const uint32_t*)codes,
+                         scales, res_codes, res_meta, res_scales, u0, u0 + n, (uint4*)out);
   }
   return hipGetLastError();
 }

@@ -158,6 +158,44 @@ fp4q_status mxfp4_resq_quantize(const void* x, int64_t rows, int64_t hidden,
                                 uint8_t* res_codes, uint8_t* res_meta,
                                 uint8_t* res_scales, void* stream);
 
+/*
+ * mxfp4_resq_dense_quantize -- Rollout-ResQ-Dense: the same primary MXFP4
+ * and residual quantization as mxfp4_resq_quantize, with every residual
+ * code kept (the dense correction Q(X)Q(W)^T + Q(dX)Q(W)^T that the same
+ * HiFloat4 page compares with the S_{2:4} one).
+ *
+ *   x, codes, scales, res_scales: as for mxfp4_resq_quantize.
+ *   res_codes   uint8 [rows, hidden/2], 16-byte aligned: residual E2M1
+ *               nibbles, packed like codes.
+ */
+fp4q_status mxfp4_resq_dense_quantize(const void* x, int64_t rows, int64_t hidden,
+                                      uint8_t* codes, uint8_t* scales,
+                                      uint8_t* res_codes, uint8_t* res_scales,
+                                      void* stream);
+
+/*
+ * mxfp4_resq_reconstruct -- the tensor the Rollout-ResQ projection sees,
+ * X_hat = DQ(Q(X)) + DQ(S(Q(dX))) (same HiFloat4 page section), for error
+ * analysis of the residual correction:
+ *   residual 0: X_hat = DQ(Q(X)); res_* are not read (may be NULL);
+ *   residual 1: + DQ(S(Q(dX))) from mxfp4_resq_quantize's res_codes
+ *               [rows, hidden/4] (8-byte aligned), res_meta [rows, hidden/8]
+ *               and res_scales; the two dropped elements of a group add 0;
+ *   residual 2: + DQ(Q(dX)) from mxfp4_resq_dense_quantize's res_codes
+ *               [rows, hidden/2] (16-byte aligned) and res_scales; res_meta
+ *               is not read.
+ * Each term is +-g * 2^(byte-127), exact in FP32; their sum is one FP32
+ * addition.  Other residual values: FP4Q_ERROR_INVALID_ARGUMENT.
+ *
+ *   codes       uint8 [rows, hidden/2], 16-byte aligned; scales [rows, hidden/32].
+ *   rows >= 0; hidden > 0, a multiple of 32.
+ *   out         float [rows, hidden], 16-byte aligned.
+ */
+fp4q_status mxfp4_resq_reconstruct(const uint8_t* codes, const uint8_t* scales,
+                                   const uint8_t* res_codes, const uint8_t* res_meta,
+                                   const uint8_t* res_scales, int64_t rows, int64_t hidden,
+                                   int residual, float* out, void* stream);
+
 /* Static description of a status (never NULL). */
 const char* fp4q_status_string(fp4q_status status);
 

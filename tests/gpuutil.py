@@ -52,6 +52,15 @@ def oracle_mx(x_bits):
     return tuple(np.concatenate([r[k] for r in res], 0) for k in range(5))
 
 
+def oracle_mx_dense(x_bits):
+    rows = x_bits.shape[0]
+    parts = _chunks(rows, WORKERS * 4)
+    with ThreadPoolExecutor(WORKERS) as ex:
+        res = list(ex.map(lambda ab: oracle.mxfp4_resq_dense_quantize(x_bits[ab[0]:ab[1]]),
+                          parts))
+    return tuple(np.concatenate([r[k] for r in res], 0) for k in range(4))
+
+
 def assert_same(got, want, name):
     got = np.asarray(got)
     want = np.asarray(want)

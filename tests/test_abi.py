@@ -28,6 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_call():
     names = declared_functions()
     assert {"nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
+            "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct",
             "fp4q_status_string"} <= set(names)
     L = fq.lib()
     for n in names:
@@ -99,3 +100,27 @@ def test_binding_refuses_cpu_tensors():
         fq.nvfp4_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
     with pytest.raises(fq.Fp4qError):
         fq.mxfp4_resq_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
+def test_mxfp4_resq_dense_and_reconstruct_reject():
+    L = fq.lib()
+    dense = lambda **k: L.mxfp4_resq_dense_quantize(
+        k.get("x", A16), k.get("rows", 4), k.get("hidden", 64), k.get("codes", A16), A16,
+        k.get("rc", A16), A16, None)
+    assert dense(hidden=48) == SHAPE
+    assert dense(x=None) == NULL
+    assert dense(rc=A8) == MISALIGNED
+    assert dense(rows=0, x=None) == SUCCESS
+    rec = lambda **k: L.mxfp4_resq_reconstruct(
+        k.get("codes", A16), A16, k.get("rc", A16), k.get("rm", A16), k.get("rs", A16),
+        k.get("rows", 4), k.get("hidden", 64), k.get("res", 1), k.get("out", A16), None)
+    assert rec(res=3) == INVALID
+    assert rec(res=-1) == INVALID
+    assert rec(hidden=16) == SHAPE
+    assert rec(out=None) == NULL
+    assert rec(rm=None) == NULL          # sparse residual needs its metadata
+    assert rec(res=2, rc=None) == NULL
+    assert rec(res=2, rc=A8) == MISALIGNED
+    assert rec(res=1, rc=P(0x10004)) == MISALIGNED
+    assert rec(out=A8) == MISALIGNED
+    assert rec(rows=0, codes=None, out=None) == SUCCESS

@@ -14,7 +14,7 @@ import fp4_block_quantization_amd as fq
 import oracle
 import workloads
 from goldens import load
-from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_nvfp4, to_dev
+from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -44,12 +44,30 @@ def check_nvfp4(x_bits, fos, dequant=True, label=""):
     return codes, scales, ts, dq
 
 
-def check_mx(x_bits, label=""):
-    got = fq.mxfp4_resq_quantize(to_dev(x_bits))
+def check_mx(x_bits, label="", dense_and_reconstruct=True):
+    x = to_dev(x_bits)
+    got = fq.mxfp4_resq_quantize(x)
     torch.cuda.synchronize()
     want = oracle_mx(x_bits)
     for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
         assert_same(host(g), w, label + " " + n)
+    if not dense_and_reconstruct:
+        return
+    # Rollout-ResQ-Dense
+    gd = fq.mxfp4_resq_dense_quantize(x)
+    torch.cuda.synchronize()
+    wd = oracle_mx_dense(x_bits)
+    for g, w, n in zip(gd, wd, ("codes", "scales", "res_codes", "res_scales")):
+        assert_same(host(g), w, label + " dense " + n)
+    # reconstruction, each side from its own quantize outputs
+    c, s, rc, rm, rs = got
+    for mode, args, wargs in ((0, (None, None, None), (None, None, None)),
+                              (1, (rc, rm, rs), (want[2], want[3], want[4])),
+                              (2, (gd[2], None, gd[3]), (wd[2], None, wd[3]))):
+        xh = fq.mxfp4_resq_reconstruct(c, s, *args, residual=mode)
+        torch.cuda.synchronize()
+        wh = oracle.mxfp4_resq_reconstruct(want[0], want[1], *wargs, residual=mode)
+        assert_same(host(xh), wh, label + " reconstruct residual=%d" % mode)
 
 
 # ------------------------------------------------------------ edge suite --
