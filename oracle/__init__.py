@@ -56,6 +56,8 @@ def lib():
         L.mxfp4_resq_reconstruct_ref.argtypes = [vp, vp, vp, vp, vp, c_i64, c_i64,
                                                  ctypes.c_int, vp]
         L.mxfp4_resq_reconstruct_ref.restype = ctypes.c_int
+        L.nvfp4_quantize_guided_ref.argtypes = [vp, c_i64, c_i64, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize_guided_ref.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -218,3 +220,19 @@ def mxfp4_resq_reconstruct(codes, scales, res_codes=None, res_meta=None, res_sca
                                           rows, hidden, int(residual), _ptr(out))
     _check(st, "mxfp4_resq_reconstruct_ref")
     return out
+
+
+def nvfp4_quantize_guided(x_bits, guide_codes, block_scales, token_scales, dequant=True):
+    """TRACE rollout-guided rounding of x under the rollout's scales.
+    Returns (codes u8 [R, H/2], dequant u16 [R, H] or None)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, hidden = x.shape
+    g = np.ascontiguousarray(guide_codes, dtype=np.uint8)
+    bs = np.ascontiguousarray(block_scales, dtype=np.uint8)
+    ts = np.ascontiguousarray(token_scales, dtype=np.float32)
+    codes = np.zeros((rows, hidden // 2), np.uint8)
+    dq = np.zeros((rows, hidden), np.uint16) if dequant else None
+    st = lib().nvfp4_quantize_guided_ref(_ptr(x), rows, hidden, _ptr(g), _ptr(bs), _ptr(ts),
+                                         _ptr(codes), _ptr(dq))
+    _check(st, "nvfp4_quantize_guided_ref")
+    return codes, dq

@@ -520,3 +520,66 @@ int mxfp4_resq_reconstruct_ref(const uint8_t* codes, const uint8_t* scales,
   }
   return 0;
 }
+
+/* TRACE rollout-guided FP4 rounding ("TRACE FP4 RL -- Rollout-guided FP4
+ * rounding", learnaivisually.com: the training engine rounds each captured
+ * value, between its two neighbouring codewords, toward the codeword the
+ * rollout engine chose, instead of to its own nearest one; the guarantee
+ * holds with the rollout's codeword, the same rollout-side scale and the same
+ * two candidates).
+ *
+ * Inputs: the training-side values x, the rollout's codes (guide) and the
+ * rollout's block and token scales, used as the scale here too.  Per
+ * element, with d = fl(e * s) and r = fl(1 / d) as in the quantizer:
+ *   v = |x| * r;  lo = the largest E2M1 magnitude code with g <= v,
+ *   hi = the smallest with g >= v (the same code when v is a grid value;
+ *   v > 6 gives 7 for both; d == 0 gives 0 for both);
+ *   with sigma the sign of x and G the guide's signed value, the code is hi
+ *   when |sigma g(hi) - G| < |sigma g(lo) - G|, else lo.
+ * The sign bit follows x, as in the quantizer; dequant (optional) is
+ * BF16(+-((g * e) * s)).  Codes outside [off0, off1) of a ragged call are
+ * not part of this entry point: every row is processed. */
+int nvfp4_quantize_guided_ref(const uint16_t* x, int64_t rows, int64_t hidden,
+                              const uint8_t* guide_codes, const uint8_t* block_scales,
+                              const float* token_scales, uint8_t* codes,
+                              uint16_t* dequant) {
+  if (rows < 0 || hidden <= 0 || hidden % 16 != 0) return 2;
+  if (rows == 0) return 0;
+  if (!x || !guide_codes || !block_scales || !token_scales || !codes) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    float s = token_scales[r];
+    for (int64_t i = 0; i < hidden; ++i) {
+      float e = oracle_e4m3_decode(block_scales[r * (hidden / 16) + i / 16]);
+      float d = e * s;
+      float xi = bf16_bits_to_float(x[r * hidden + i]);
+      int neg = signbit(xi) ? 1 : 0;
+      int lo = 0, hi = 0;
+      if (d != 0.0f) {
+        float rr = 1.0f / d;
+        float v = fabsf(xi) * rr;
+        lo = 0;
+        for (int q = 1; q < 8; ++q)
+          if (oracle_e2m1_value(q) <= v) lo = q;
+        hi = lo;
+        if (oracle_e2m1_value(lo) < v && lo < 7) hi = lo + 1;
+      }
+      uint8_t gb = guide_codes[r * (hidden / 2) + i / 2];
+      int gn = (i % 2) ? (gb >> 4) : (gb & 15);
+      double G = (gn & 8) ? -(double)oracle_e2m1_value(gn & 7) : (double)oracle_e2m1_value(gn & 7);
+      double sigma = neg ? -1.0 : 1.0;
+      double dlo = fabs(sigma * oracle_e2m1_value(lo) - G);
+      double dhi = fabs(sigma * oracle_e2m1_value(hi) - G);
+      int q = (dhi < dlo) ? hi : lo;
+      uint8_t nib = (uint8_t)((neg << 3) | q);
+      uint8_t* cb = &codes[r * (hidden / 2) + i / 2];
+      if (i % 2 == 0) *cb = (uint8_t)((*cb & 0xF0) | nib);
+      else *cb = (uint8_t)((*cb & 0x0F) | (nib << 4));
+      if (dequant) {
+        float ge = oracle_e2m1_value(q) * e;
+        float c = ge * s;
+        dequant[r * hidden + i] = oracle_bf16_rne(neg ? -c : c);
+      }
+    }
+  }
+  return 0;
+}
