@@ -312,7 +312,7 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--parts", default="copy,dequant,resq,resq_dense,ragged,weights,fp16",
+    ap.add_argument("--parts", default="copy,dequant,resq,resq_dense,trace,ragged,weights,fp16",
                     help="secondary measurements to run (comma list)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     args = ap.parse_args()
@@ -420,6 +420,41 @@ def main():
             "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
         secondary["Rollout-ResQ reconstruction error resq_act"] = mse
         del msets, douts, sp, de, xf, xh, xr
+        torch.cuda.empty_cache()
+    if "trace" in parts:
+        # TRACE rollout-guided rounding: the rollout quantizes moe_act; the
+        # training side holds the same values perturbed by ~1 BF16 step
+        # (relative N(0, 2^-8)).  Elementwise code mismatches with the
+        # rollout: the training side quantizing on its own (round to
+        # nearest, its own scales), and guided by the rollout's codes under
+        # the rollout's scales; plus the share of the independent mismatches
+        # that land on adjacent codewords.
+        xt = torch.from_numpy(workloads.perturbed(x_bits, seed=2).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        rc, rs, rt, _ = fq.nvfp4_quantize(x, True, dequant=False)
+        gsets = [(xt, (torch.empty_like(rc), None)) for _ in range(2)]
+        p, _ = time_calls(lambda s_: fq.nvfp4_quantize_guided(s_[0], rc, rs, rt, dequant=False,
+                                                              out=s_[1]), gsets, 500, 50)
+        b = rows * hidden * 2 + rows * hidden // 2 * 2 + rows * hidden // 16 + rows * 4
+        secondary["nvfp4_quantize_guided moe_act 8192x7168 (no dequant)"] = {
+            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+
+        def nib(c):
+            return torch.stack([c & 15, c >> 4], -1).reshape(c.shape[0], -1)
+        own = nib(fq.nvfp4_quantize(xt, True, dequant=False)[0])
+        guided = nib(fq.nvfp4_quantize_guided(xt, rc, rs, rt, dequant=False)[0])
+        ref = nib(rc)
+        mis_own = own != ref
+        mag_own, mag_ref = (own & 7).int(), (ref & 7).int()
+        adjacent = mis_own & ((own >> 3) == (ref >> 3)) & ((mag_own - mag_ref).abs() == 1)
+        n_el = ref.numel()
+        secondary["TRACE guided rounding moe_act (training = rollout x (1 + 2^-8 N(0,1)))"] = {
+            "elements": n_el,
+            "mismatch_frac_independent_rne": round(float(mis_own.sum()) / n_el, 7),
+            "mismatch_frac_guided": round(float((guided != ref).sum()) / n_el, 7),
+            "adjacent_share_of_independent_mismatches":
+                round(float(adjacent.sum()) / max(1, int(mis_own.sum())), 5)}
+        del xt, rc, rs, rt, gsets, own, guided, ref, mis_own, adjacent
         torch.cuda.empty_cache()
     if "ragged" in parts:
         # ragged routed, quantize only

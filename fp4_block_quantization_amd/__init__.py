@@ -27,7 +27,8 @@ import torch
 
 from . import _build
 
-__all__ = ["lib", "nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
+__all__ = ["lib", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_quantize_guided",
+           "mxfp4_resq_quantize",
            "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "Fp4qError", "LIB_PATH"]
 
 LIB_PATH = _build.LIB_PATH
@@ -54,6 +55,8 @@ def lib():
         L.nvfp4_dequantize.restype = ci
         L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mxfp4_resq_quantize.restype = ci
+        L.nvfp4_quantize_guided.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize_guided.restype = ci
         L.mxfp4_resq_dense_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.mxfp4_resq_dense_quantize.restype = ci
         L.mxfp4_resq_reconstruct.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, vp, vp]
@@ -207,3 +210,28 @@ def mxfp4_resq_reconstruct(codes, scales, res_codes=None, res_meta=None, res_sca
                                       _stream(codes))
     _check(st, "mxfp4_resq_reconstruct")
     return out
+
+
+def nvfp4_quantize_guided(x, guide_codes, block_scales, token_scales, dequant=True, out=None):
+    """TRACE rollout-guided rounding of x (BF16 [rows, hidden]) under the
+    rollout's scales, toward the rollout's codes.  Returns (codes u8
+    [R, H/2], dequant bf16 [R, H] or None)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(guide_codes, "guide_codes", torch.uint8)
+    _dev(block_scales, "block_scales", torch.uint8)
+    _dev(token_scales, "token_scales", torch.float32)
+    if x.dim() != 2:
+        raise Fp4qError("x must be 2-D [rows, hidden]")
+    rows, hidden = x.shape
+    if (guide_codes.numel() != rows * (hidden // 2) or block_scales.numel() != rows * (hidden // 16)
+            or token_scales.numel() != rows):
+        raise Fp4qError("guide tensor sizes do not match x")
+    if out is None:
+        codes = torch.empty((rows, hidden // 2), dtype=torch.uint8, device=x.device)
+        dq = torch.empty_like(x) if dequant else None
+    else:
+        codes, dq = out
+    st = lib().nvfp4_quantize_guided(_p(x), rows, hidden, _p(guide_codes), _p(block_scales),
+                                     _p(token_scales), _p(codes), _p(dq), _stream(x))
+    _check(st, "nvfp4_quantize_guided")
+    return codes, dq

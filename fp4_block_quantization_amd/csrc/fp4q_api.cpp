@@ -111,6 +111,22 @@ fp4q_status mxfp4_resq_reconstruct(const uint8_t* codes, const uint8_t* scales,
                                                  (hipStream_t)stream));
 }
 
+fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
+                                  const uint8_t* guide_codes, const uint8_t* block_scales,
+                                  const float* token_scales, uint8_t* codes, void* dequant,
+                                  void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 16);
+  if (st != FP4Q_SUCCESS) return st;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!x || !guide_codes || !block_scales || !token_scales || !codes)
+    return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(guide_codes, 4) || !aligned(codes, 4) ||
+      !aligned(token_scales, 4) || (dequant && !aligned(dequant, 16)))
+    return FP4Q_ERROR_MISALIGNED;
+  return launched(fp4q::nvfp4_guided_launch(x, guide_codes, block_scales, token_scales, rows,
+                                            hidden, codes, dequant, (hipStream_t)stream));
+}
+
 const char* fp4q_status_string(fp4q_status status) {
   switch (status) {
     case FP4Q_SUCCESS: return "success";

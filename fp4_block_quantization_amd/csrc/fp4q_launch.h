@@ -43,4 +43,8 @@ hipError_t mxfp4_reconstruct_launch(const uint8_t* codes, const uint8_t* scales,
                                     const uint8_t* res_scales, int64_t rows, int64_t hidden,
                                     int residual, float* out, hipStream_t stream);
 
+hipError_t nvfp4_guided_launch(const void* x, const uint8_t* guide, const uint8_t* scales,
+                              const float* tscale, int64_t rows, int64_t hidden, uint8_t* codes,
+                              void* dequant, hipStream_t stream);
+
 }  // namespace fp4q

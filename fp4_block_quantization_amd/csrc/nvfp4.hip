@@ -102,6 +102,12 @@ __device__ __forceinline__ void store_out(uint2* p, uint2 v) {
   else
     *p = v;
 }
+__device__ __forceinline__ void store_out(uint32_t* p, uint32_t v) {
+  if (FP4Q_NV_NT_STORES)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
 __device__ __forceinline__ void store_out(uint8_t* p, uint8_t v) {
   if (FP4Q_NV_NT_STORES)
     __builtin_nontemporal_store(v, p);
@@ -775,6 +781,71 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
   }
 }
 
+// TRACE rollout-guided rounding ("TRACE FP4 RL -- Rollout-guided FP4
+// rounding", learnaivisually.com): under the rollout's block and token
+// scales, each element takes, of the two E2M1 codewords around
+// v = |x| * fl(1 / fl(e s)), the one nearer the rollout's codeword.  With
+// the same sign, or a zero guide, that is the upper neighbour exactly when
+// the guide's magnitude code is at least the upper one; a guide of the
+// other sign is nearer the lower neighbour.  One lane per 8-element unit,
+// mapped like the dequant kernel.
+__global__ __launch_bounds__(256) void nvfp4_guided_units(
+    const uint4* __restrict__ x, const uint32_t* __restrict__ guide,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tscale, int64_t row0,
+    int64_t row_end, int h8, uint32_t wpr, uint32_t* __restrict__ codes,
+    uint4* __restrict__ dq) {
+  constexpr int NU = FP4Q_DQ_UNITS;
+  const int lane = threadIdx.x & 63;
+  const uint32_t gw = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t rr = gw / wpr;  // uniform
+  const int64_t row = row0 + rr;
+  if (row >= row_end) return;
+  const int first = (int)(gw - rr * wpr) * 64 * NU;
+  const int nv = h8 - first < 64 * NU ? h8 - first : 64 * NU;
+  const int64_t base = row * h8 + first;
+  const float s = tscale[row];
+  const uint4* xin = x + base;
+  const uint32_t* gin = guide + base;
+  const uint8_t* sin = scales + (base >> 1);
+#pragma unroll
+  for (int n = 0; n < NU; ++n) {
+    const int j = lane + 64 * n;
+    if (j >= nv) continue;
+    const uint4 a = xin[j];
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t gwd = gin[j];
+    const float e = e4m3_value<0>(sin[j >> 1]);
+    const float d = e * s;
+    const float r = d != 0.0f ? 1.0f / d : 0.0f;  // fl(1 / fl(e s)), IEEE
+    uint32_t out = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xi = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+      const float v = fabsf(xi) * r;
+      // lower and upper neighbours: the number of grid values <= v (minus
+      // one) and the code above it when v is not itself a grid value
+      uint32_t lo = (v >= 0.5f) + (v >= 1.0f) + (v >= 1.5f) + (v >= 2.0f) + (v >= 3.0f) +
+                    (v >= 4.0f) + (v >= 6.0f);
+      const uint32_t hi = (lo < 7u && e2m1_value(lo) < v) ? lo + 1u : lo;
+      const uint32_t gn = (gwd >> (4 * i)) & 15u;
+      const uint32_t sx = __float_as_uint(xi) >> 31;
+      const uint32_t q = (hi != lo && (gn >> 3) == sx && (gn & 7u) >= hi) ? hi : lo;
+      out |= ((sx << 3) | q) << (4 * i);
+    }
+    store_out(&codes[base + j], out);
+    if (dq != nullptr) {
+      uint32_t o[4];
+      static_for<0, 4>([&](auto P) {
+        constexpr int k = decltype(P)::value;
+        const float2v g = e2m1x2_values<k>(out);
+        const float ge0 = g.x * e, ge1 = g.y * e;  // exact
+        o[k] = cvt_bf16x2(ge0 * s, ge1 * s);
+      });
+      store_out(&dq[base + j], make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  }
+}
+
 template <int FOS, bool DQ>
 hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const int nblk = (int)(a.hidden / 16);
@@ -845,6 +916,23 @@ hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,
     const dim3 grid((unsigned)((n * wpr + 3) / 4)), block(256);
     hipLaunchKernelGGL(nvfp4_dequantize_rows, grid, block, 0, st, (const uint32_t*)codes, scales,
                        tscale, row0, row0 + n, h8, wpr, (uint4*)out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t nvfp4_guided_launch(const void* x, const uint8_t* guide, const uint8_t* scales,
+                              const float* tscale, int64_t rows, int64_t hidden, uint8_t* codes,
+                              void* dequant, hipStream_t st) {
+  const int h8 = (int)(hidden / 8);
+  const int64_t per_wave = 64 * FP4Q_DQ_UNITS;
+  const uint32_t wpr = (uint32_t)((h8 + per_wave - 1) / per_wave);  // waves per row
+  const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * (int64_t)wpr);
+  for (int64_t row0 = 0; row0 < rows; row0 += max_rows) {
+    const int64_t n = rows - row0 < max_rows ? rows - row0 : max_rows;
+    const dim3 grid((unsigned)((n * wpr + 3) / 4)), block(256);
+    hipLaunchKernelGGL(nvfp4_guided_units, grid, block, 0, st, (const uint4*)x,
+                       (const uint32_t*)guide, scales, tscale, row0, row0 + n, h8, wpr,
+                       (uint32_t*)codes, (uint4*)dequant);
   }
   return hipGetLastError();
 }

@@ -128,6 +128,35 @@ fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales,
                              int64_t hidden, void* out, void* stream);
 
 /*
+ * nvfp4_quantize_guided -- TRACE rollout-guided rounding.
+ *
+ * Definition: "TRACE FP4 RL -- Rollout-guided FP4 rounding"
+ * (learnaivisually.com): the training engine rounds each captured value,
+ * between its two neighbouring FP4 codewords, toward the codeword the
+ * rollout engine chose, under the same rollout-side scale.  With the
+ * rollout's E4M3 block scale e and token scale s (as nvfp4_quantize stored
+ * them), per element:
+ *   v = |x_i| * fl(1 / fl(e*s))  (0 when e*s == 0);
+ *   lo = the largest E2M1 magnitude code with g <= v, hi = the smallest
+ *   with g >= v (equal when v is a grid value; 7 for both above 6);
+ *   with G the guide's signed value and sigma the sign of x_i, the code is
+ *   hi if |sigma*g(hi) - G| < |sigma*g(lo) - G|, else lo; the sign bit
+ *   follows x_i.  Guided by its own round-to-nearest codes it returns them.
+ *
+ *   x             BF16 [rows, hidden] (training side), 16-byte aligned.
+ *   guide_codes   uint8 [rows, hidden/2], 4-byte aligned: the rollout's codes.
+ *   block_scales  uint8 [rows, hidden/16], token_scales float [rows] (4-byte
+ *                 aligned): the rollout's scales, read only.
+ *   codes         uint8 [rows, hidden/2], 4-byte aligned: the guided codes.
+ *   dequant       BF16 [rows, hidden], 16-byte aligned, or NULL:
+ *                 BF16(+-((g*e)*s)) of the guided codes.
+ */
+fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
+                                  const uint8_t* guide_codes, const uint8_t* block_scales,
+                                  const float* token_scales, uint8_t* codes, void* dequant,
+                                  void* stream);
+
+/*
  * mxfp4_resq_quantize -- MXFP4 with a Rollout-ResQ residual.
  *
  * Definition: "HiFloat4 Format for End-To-End Reinforcement Learning

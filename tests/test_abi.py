@@ -28,7 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_call():
     names = declared_functions()
     assert {"nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
-            "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct",
+            "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "nvfp4_quantize_guided",
             "fp4q_status_string"} <= set(names)
     L = fq.lib()
     for n in names:
@@ -124,3 +124,18 @@ def test_mxfp4_resq_dense_and_reconstruct_reject():
     assert rec(res=1, rc=P(0x10004)) == MISALIGNED
     assert rec(out=A8) == MISALIGNED
     assert rec(rows=0, codes=None, out=None) == SUCCESS
+
+
+def test_nvfp4_quantize_guided_rejects():
+    L = fq.lib()
+    g = lambda **k: L.nvfp4_quantize_guided(
+        k.get("x", A16), k.get("rows", 4), k.get("hidden", 64), k.get("guide", A16), A16,
+        k.get("ts", A16), k.get("codes", A16), k.get("dq", A16), None)
+    assert g(hidden=24) == SHAPE
+    assert g(x=None) == NULL
+    assert g(guide=None) == NULL
+    assert g(codes=None) == NULL
+    assert g(x=A8) == MISALIGNED
+    assert g(guide=P(0x10002)) == MISALIGNED
+    assert g(dq=A8) == MISALIGNED
+    assert g(rows=0, x=None, guide=None, codes=None) == SUCCESS

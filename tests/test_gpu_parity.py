@@ -254,3 +254,45 @@ def test_empty_and_rejected_calls():
     flat = torch.zeros(16 * 5, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fq.Fp4qError):  # 2-byte offset: misaligned
         fq.nvfp4_quantize(flat[1:1 + 64].view(4, 16))
+
+
+# ------------------------------------------------- TRACE guided rounding --
+
+def check_guided(x_rollout, x_train, label):
+    codes, scales, ts, _ = oracle_nvfp4(x_rollout, 1, dequant=False)  # the rollout's outputs
+    got = fq.nvfp4_quantize_guided(to_dev(x_train), torch.from_numpy(codes).cuda(),
+                                   torch.from_numpy(scales).cuda(), torch.from_numpy(ts).cuda())
+    torch.cuda.synchronize()
+    want = oracle.nvfp4_quantize_guided(x_train, codes, scales, ts)
+    assert_same(host(got[0]), want[0], label + " codes")
+    assert_same(bits_of(got[1]), want[1], label + " dequant")
+
+
+@pytest.mark.parametrize("H", [16, 2048, 7168, 7184])
+def test_guided_edge_rows(H):
+    x = edge_rows(H, seed=H + 7)
+    check_guided(x, workloads.perturbed(x, seed=H), "guided edge H=%d" % H)
+    # a guide from unrelated values, and the tensor guided by itself
+    check_guided(edge_rows(H, seed=H + 99), x, "guided cross H=%d" % H)
+    check_guided(x, x, "guided self H=%d" % H)
+
+
+def test_guided_random_guides_and_scales():
+    # arbitrary guide bytes and block scales (every branch of the rule)
+    rng = np.random.default_rng(77)
+    rows, H = 64, 2048
+    x = workloads.rows("moe_act", 0, rows)[:, :H].copy()
+    guide = rng.integers(0, 256, (rows, H // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (rows, H // 16), dtype=np.uint8)
+    ts = (np.abs(rng.standard_normal(rows)) * 0.01).astype(np.float32)
+    got = fq.nvfp4_quantize_guided(to_dev(x), torch.from_numpy(guide).cuda(),
+                                   torch.from_numpy(scales).cuda(), torch.from_numpy(ts).cuda())
+    torch.cuda.synchronize()
+    want = oracle.nvfp4_quantize_guided(x, guide, scales, ts)
+    assert_same(host(got[0]), want[0], "guided random codes")
+    assert_same(bits_of(got[1]), want[1], "guided random dequant")
+
+
+def test_guided_moe_act_full_size():
+    x = workloads.rows("moe_act")
+    check_guided(x, workloads.perturbed(x, seed=2), "guided moe_act")

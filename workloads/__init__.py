@@ -157,3 +157,16 @@ def random_rows(seed: int, nrows: int, hidden: int, dist=0, scale=1.0,
     """Free-form seeded rows (BF16 bits) for property tests."""
     return to_bf16_bits(fill_fp32(seed, 0, nrows, hidden, dist, scale,
                                   row_gain_sigma, elem_p, elem_mult))
+
+
+def perturbed(x_bits: np.ndarray, seed: int, rel_sigma: float = 2.0 ** -8) -> np.ndarray:
+    """A training-side copy of a rollout tensor: each BF16 value times
+    (1 + rel_sigma * N(0, 1)), rounded back to BF16 (seeded; the draws come
+    from numpy's PCG64)."""
+    rng = np.random.default_rng(seed)
+    x = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    noise = rng.standard_normal(x.shape).astype(np.float32)
+    bf16_max = np.float32(3.3895313892515355e38)  # largest finite BF16: values stay finite
+    with np.errstate(over="ignore"):
+        y = x * (np.float32(1) + np.float32(rel_sigma) * noise)
+    return to_bf16_bits(np.clip(y, -bf16_max, bf16_max))
