@@ -58,6 +58,8 @@ def lib():
         L.mxfp4_resq_reconstruct_ref.restype = ctypes.c_int
         L.nvfp4_quantize_guided_ref.argtypes = [vp, c_i64, c_i64, vp, vp, vp, vp, vp]
         L.nvfp4_quantize_guided_ref.restype = ctypes.c_int
+        L.nvfp4_quantize_global_ref.argtypes = [vp, c_i64, c_i64, ctypes.c_int, vp, vp, vp, vp]
+        L.nvfp4_quantize_global_ref.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -236,3 +238,18 @@ def nvfp4_quantize_guided(x_bits, guide_codes, block_scales, token_scales, dequa
                                          _ptr(codes), _ptr(dq))
     _check(st, "nvfp4_quantize_guided_ref")
     return codes, dq
+
+
+def nvfp4_quantize_global(x_bits, four_over_six=True, dequant=True):
+    """One FP32 scale for the whole tensor.  Returns (codes, scales,
+    tensor_scale f32 [1], dequant u16 or None)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, hidden = x.shape
+    codes = np.zeros((rows, hidden // 2), np.uint8)
+    scales = np.zeros((rows, hidden // 16), np.uint8)
+    ts = np.zeros((1,), np.float32)
+    dq = np.zeros((rows, hidden), np.uint16) if dequant else None
+    st = lib().nvfp4_quantize_global_ref(_ptr(x), rows, hidden, mode_of(four_over_six),
+                                         _ptr(codes), _ptr(scales), _ptr(ts), _ptr(dq))
+    _check(st, "nvfp4_quantize_global_ref")
+    return codes, scales, ts, dq

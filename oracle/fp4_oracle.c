@@ -284,6 +284,10 @@ void oracle_nvfp4_block(const float* x, float s, int four_over_six,
 /* One token row.  Per-token scaling (humans& article section 1; NVFP4-RL
  * blog section 2): each row takes its own FP32 scale from the max magnitude
  * over its hidden dimension, so nothing outside the row matters. */
+static void nvfp4_row_with_scale(const uint16_t* xrow, int64_t hidden, int four_over_six,
+                                 float s, uint8_t* codes, uint8_t* block_scales,
+                                 uint16_t* dequant);
+
 static void nvfp4_row(const uint16_t* xrow, int64_t hidden, int four_over_six,
                       uint8_t* codes, uint8_t* block_scales, float* token_scale,
                       uint16_t* dequant) {
@@ -294,6 +298,14 @@ static void nvfp4_row(const uint16_t* xrow, int64_t hidden, int four_over_six,
   }
   float s = amax / (four_over_six ? 1536.0f : 2688.0f); /* 1 and 2: 4/6 on */
   *token_scale = s;
+  nvfp4_row_with_scale(xrow, hidden, four_over_six, s, codes, block_scales, dequant);
+}
+
+/* The blocks of one row under a given FP32 scale s (the row's own, or the
+ * whole tensor's). */
+static void nvfp4_row_with_scale(const uint16_t* xrow, int64_t hidden, int four_over_six,
+                                 float s, uint8_t* codes, uint8_t* block_scales,
+                                 uint16_t* dequant) {
 
   for (int64_t j = 0; j < hidden / 16; ++j) {
     float x16[16];
@@ -581,5 +593,30 @@ int nvfp4_quantize_guided_ref(const uint16_t* x, int64_t rows, int64_t hidden,
       }
     }
   }
+  return 0;
+}
+
+/* The naive NVFP4 the pages contrast with per-token scaling (humans&
+ * article section 1; NVFP4-RL blog section 2): one FP32 scale for the whole
+ * activation tensor, s = amax_tensor / 1536 (4/6 on) or / 2688, then the
+ * same block path in every row.  A row's outputs then depend on the other
+ * rows of the tensor (the batch dependency the pages warn about). */
+int nvfp4_quantize_global_ref(const uint16_t* x, int64_t rows, int64_t hidden,
+                              int four_over_six, uint8_t* codes, uint8_t* block_scales,
+                              float* tensor_scale, uint16_t* dequant) {
+  if (rows < 0 || hidden <= 0 || hidden % 16 != 0) return 2;
+  if (four_over_six < 0 || four_over_six > 2) return 5;
+  if (rows == 0) return 0;
+  if (!x || !codes || !block_scales || !tensor_scale) return 1;
+  float amax = 0.0f;
+  for (int64_t i = 0; i < rows * hidden; ++i) {
+    float a = fabsf(bf16_bits_to_float(x[i]));
+    if (a > amax) amax = a;
+  }
+  float s = amax / (four_over_six ? 1536.0f : 2688.0f);
+  *tensor_scale = s;
+  for (int64_t r = 0; r < rows; ++r)
+    nvfp4_row_with_scale(x + r * hidden, hidden, four_over_six, s, codes + r * (hidden / 2),
+                         block_scales + r * (hidden / 16), dequant ? dequant + r * hidden : NULL);
   return 0;
 }

@@ -92,6 +92,11 @@ int mxfp4_resq_reconstruct_ref(const uint8_t* codes, const uint8_t* scales,
                                const uint8_t* res_scales, int64_t rows, int64_t hidden,
                                int residual, float* out);
 
+/* One FP32 scale for the whole tensor (the naive baseline). */
+int nvfp4_quantize_global_ref(const uint16_t* x, int64_t rows, int64_t hidden,
+                              int four_over_six, uint8_t* codes, uint8_t* block_scales,
+                              float* tensor_scale, uint16_t* dequant);
+
 /* TRACE rollout-guided rounding under the rollout's scales. */
 int nvfp4_quantize_guided_ref(const uint16_t* x, int64_t rows, int64_t hidden,
                               const uint8_t* guide_codes, const uint8_t* block_scales,
