@@ -312,7 +312,8 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--parts", default="copy,dequant,resq,resq_dense,trace,ragged,weights,fp16",
+    ap.add_argument("--parts",
+                    default="copy,dequant,resq,resq_dense,trace,global,ragged,weights,fp16",
                     help="secondary measurements to run (comma list)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     args = ap.parse_args()
@@ -455,6 +456,34 @@ def main():
             "adjacent_share_of_independent_mismatches":
                 round(float(adjacent.sum()) / max(1, int(mis_own.sum())), 5)}
         del xt, rc, rs, rt, gsets, own, guided, ref, mis_own, adjacent
+        torch.cuda.empty_cache()
+    if "global" in parts:
+        # the naive one-scale-per-tensor NVFP4: speed, and the batch
+        # dependency -- the blocks of each 1024-row slice that change when
+        # the slice is quantized on its own instead of in the full tensor
+        gsets = rotating_nvfp4_sets(x, args.sets)
+        outs = [(s_[1][0], s_[1][1], torch.empty(1, dtype=torch.float32, device=dev), s_[1][3])
+                for s_ in gsets]
+        p, _ = time_calls(lambda i: fq.nvfp4_quantize_global(gsets[i][0], True, out=outs[i]),
+                          list(range(len(gsets))), 500, 50)
+        secondary["nvfp4_quantize_global moe_act 8192x7168 (amax pass + quantize)"] = {
+            "us": round(p * 1e3, 2), "GBps": round(nbytes / (p * 1e-3) / 1e9, 1)}
+        del gsets, outs
+        torch.cuda.empty_cache()
+        full = fq.nvfp4_quantize_global(x, True, dequant=False)
+        pt_full = fq.nvfp4_quantize(x, True, dequant=False)
+        changed = pt_changed = 0
+        for r0 in range(0, rows, 1024):
+            part = fq.nvfp4_quantize_global(x[r0:r0 + 1024], True, dequant=False)
+            same = (part[1] == full[1][r0:r0 + 1024]) & (
+                part[0].view(-1, hidden // 16, 8) == full[0][r0:r0 + 1024].view(-1, hidden // 16, 8)).all(-1)
+            changed += int((~same).sum())
+            pp = fq.nvfp4_quantize(x[r0:r0 + 1024], True, dequant=False)
+            pt_changed += int((pp[0] != pt_full[0][r0:r0 + 1024]).sum() + (pp[1] != pt_full[1][r0:r0 + 1024]).sum())
+        secondary["batch dependency moe_act (8 slices of 1024 rows vs the whole tensor)"] = {
+            "global_scale_blocks_changed_frac": round(changed / (rows * hidden // 16), 6),
+            "per_token_bytes_changed": pt_changed}
+        del full, pt_full
         torch.cuda.empty_cache()
     if "ragged" in parts:
         # ragged routed, quantize only

@@ -28,6 +28,7 @@ import torch
 from . import _build
 
 __all__ = ["lib", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_quantize_guided",
+           "nvfp4_quantize_global",
            "mxfp4_resq_quantize",
            "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "Fp4qError", "LIB_PATH"]
 
@@ -55,6 +56,8 @@ def lib():
         L.nvfp4_dequantize.restype = ci
         L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mxfp4_resq_quantize.restype = ci
+        L.nvfp4_quantize_global.argtypes = [vp, i64, i64, ci, vp, vp, vp, vp, vp]
+        L.nvfp4_quantize_global.restype = ci
         L.nvfp4_quantize_guided.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
         L.nvfp4_quantize_guided.restype = ci
         L.mxfp4_resq_dense_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
@@ -235,3 +238,23 @@ def nvfp4_quantize_guided(x, guide_codes, block_scales, token_scales, dequant=Tr
                                      _p(token_scales), _p(codes), _p(dq), _stream(x))
     _check(st, "nvfp4_quantize_guided")
     return codes, dq
+
+
+def nvfp4_quantize_global(x, four_over_six=True, dequant=True, out=None):
+    """NVFP4 with one FP32 scale for the whole tensor (the naive baseline).
+    Returns (codes, block_scales, tensor_scale f32 [1], dequant or None)."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise Fp4qError("x must be 2-D [rows, hidden]")
+    rows, hidden = x.shape
+    if out is None:
+        codes = torch.empty((rows, hidden // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, hidden // 16), dtype=torch.uint8, device=x.device)
+        ts = torch.empty((1,), dtype=torch.float32, device=x.device)
+        dq = torch.empty_like(x) if dequant else None
+    else:
+        codes, scales, ts, dq = out
+    st = lib().nvfp4_quantize_global(_p(x), rows, hidden, _mode(four_over_six), _p(codes),
+                                     _p(scales), _p(ts), _p(dq), _stream(x))
+    _check(st, "nvfp4_quantize_global")
+    return codes, scales, ts, dq

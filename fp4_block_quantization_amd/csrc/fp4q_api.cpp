@@ -127,6 +127,22 @@ fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
                                             hidden, codes, dequant, (hipStream_t)stream));
 }
 
+fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
+                                  int four_over_six, uint8_t* codes, uint8_t* block_scales,
+                                  float* tensor_scale, void* dequant, void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 16);
+  if (st != FP4Q_SUCCESS) return st;
+  if (four_over_six < 0 || four_over_six > 2) return FP4Q_ERROR_INVALID_ARGUMENT;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!x || !codes || !block_scales || !tensor_scale) return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) ||
+      (dequant && !aligned(dequant, 16)))
+    return FP4Q_ERROR_MISALIGNED;
+  fp4q::NvQuantArgs a{x,     rows,         hidden,  nullptr, 0,
+                      four_over_six, codes, block_scales, nullptr, dequant};
+  return launched(fp4q::nvfp4_quantize_global_launch(a, tensor_scale, (hipStream_t)stream));
+}
+
 const char* fp4q_status_string(fp4q_status status) {
   switch (status) {
     case FP4Q_SUCCESS: return "success";

@@ -25,9 +25,12 @@ struct NvQuantArgs {
   uint8_t* block_scales;
   float* token_scales;
   void* dequant;
+  const uint32_t* global_amax = nullptr;  // set: one scale for the whole tensor
 };
 
 hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t stream);
+hipError_t nvfp4_quantize_global_launch(const NvQuantArgs& a, float* tensor_scale,
+                                        hipStream_t stream);
 hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,
                                    const float* token_scales, int64_t rows, int64_t hidden,
                                    void* out, hipStream_t stream);

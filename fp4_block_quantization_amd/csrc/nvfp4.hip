@@ -596,7 +596,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     int R, int64_t ngrp, const int64_t* __restrict__ offs, int64_t ngroups,
     uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
-    float neg_zero) {
+    float neg_zero, const uint32_t* __restrict__ gamax) {
   __shared__ uint32_t wave_max[kMaxWgWaves];
   __shared__ RowScale rowinfo[kMaxWgWaves];
   // dynamic LDS: the reciprocal table of each row (R x 128 floats), then,
@@ -645,10 +645,11 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     if (chunk < 2) {
       uint32_t amax_bits = 0;
       for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+      if (gamax != nullptr) amax_bits = *gamax;  // one scale for the whole tensor
       const RowScale rs = row_scale<FOS>(amax_bits);
       if (chunk == 0 && lane == 0) {
         rowinfo[rw] = rs;
-        if (c.active) tscale[c.row] = rs.s;
+        if (c.active && tscale != nullptr) tscale[c.row] = rs.s;
       }
       fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
     }
@@ -698,7 +699,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk,
     const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
-    float neg_zero) {
+    float neg_zero, const uint32_t* __restrict__ gamax) {
   __shared__ float recip[kLongWaves][128];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -712,8 +713,9 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     load_block(x, base + j, w);
     lmax = max(lmax, block_absmax_bits(w));
   }
-  const RowScale rs = row_scale<FOS>(wave_max_u32(lmax));
-  if (lane == 0) tscale[row] = rs.s;
+  const uint32_t row_amax = wave_max_u32(lmax);
+  const RowScale rs = row_scale<FOS>(gamax != nullptr ? *gamax : row_amax);
+  if (lane == 0 && tscale != nullptr) tscale[row] = rs.s;
   fill_recip(recip[wave], rs.s, lane, 64);
   __builtin_amdgcn_wave_barrier();
   for (int j = lane; j < nblk; j += 64) {
@@ -846,6 +848,53 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
   }
 }
 
+// One FP32 scale for the whole tensor: the tensor amax is gathered with a
+// vector atomic max on its bit pattern (non-negative floats order like
+// their bits) into the caller's scale slot, the blocks are quantized under
+// it, and the slot finally receives s = amax / C.
+__global__ void global_amax_init(uint32_t* slot) { *slot = 0u; }
+
+__global__ __launch_bounds__(256) void global_amax_pass(const uint4* __restrict__ x,
+                                                        int64_t n16, uint32_t* slot) {
+  __shared__ uint32_t wmax[4];
+  uint32_t m = 0u;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {  // four loads in flight per lane
+    uint4 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = x[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w[4] = {a[u].x & 0x7FFF7FFFu, a[u].y & 0x7FFF7FFFu, a[u].z & 0x7FFF7FFFu,
+                             a[u].w & 0x7FFF7FFFu};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = max(m, max(w[k] << 16, w[k] & 0xFFFF0000u));
+    }
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = x[i];
+    const uint32_t w[4] = {a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu, a.z & 0x7FFF7FFFu,
+                           a.w & 0x7FFF7FFFu};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(w[k] << 16, w[k] & 0xFFFF0000u));
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    // one atomic per workgroup, skipped when the slot already holds as much
+    if (m > __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(slot, m);
+  }
+}
+
+template <int FOS>
+__global__ void global_scale_final(uint32_t* slot) {
+  *reinterpret_cast<float*>(slot) = __uint_as_float(*slot) / (FOS ? 1536.0f : 2688.0f);
+}
+
 template <int FOS, bool DQ>
 hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const int nblk = (int)(a.hidden / 16);
@@ -878,7 +927,7 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
       const dim3 grid((unsigned)nwg), block(64 * W * R);
       hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, lds, st, x, a.rows,
                          row0, row_end, nblk, W, R, ngrp, a.offsets, a.num_groups, codes,
-                         a.block_scales, a.token_scales, dq, neg_zero);
+                         a.block_scales, a.token_scales, dq, neg_zero, a.global_amax);
     }
   } else {
     const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * kLongWaves) * kLongWaves;
@@ -888,13 +937,34 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
           block(64 * kLongWaves);
       hipLaunchKernelGGL((nvfp4_quantize_long_rows<FOS, DQ>), grid, block, 0, st, x, a.rows, row0,
                          row_end, nblk, a.offsets, a.num_groups, codes, a.block_scales,
-                         a.token_scales, dq, neg_zero);
+                         a.token_scales, dq, neg_zero, a.global_amax);
     }
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t nvfp4_quantize_global_launch(const NvQuantArgs& args, float* tensor_scale,
+                                        hipStream_t st) {
+  NvQuantArgs a = args;
+  uint32_t* slot = reinterpret_cast<uint32_t*>(tensor_scale);
+  hipLaunchKernelGGL(global_amax_init, dim3(1), dim3(1), 0, st, slot);
+  const int64_t n16 = a.rows * a.hidden / 8;  // 16-byte units
+  int64_t grid = (n16 + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  hipLaunchKernelGGL(global_amax_pass, dim3((unsigned)grid), dim3(256), 0, st,
+                     (const uint4*)a.x, n16, slot);
+  a.global_amax = slot;
+  a.token_scales = nullptr;
+  hipError_t e = nvfp4_quantize_launch(a, st);
+  if (e != hipSuccess) return e;
+  if (a.four_over_six)
+    hipLaunchKernelGGL(global_scale_final<1>, dim3(1), dim3(1), 0, st, slot);
+  else
+    hipLaunchKernelGGL(global_scale_final<0>, dim3(1), dim3(1), 0, st, slot);
+  return hipGetLastError();
+}
 
 hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t st) {
   if (a.four_over_six == 2)

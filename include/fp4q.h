@@ -128,6 +128,26 @@ fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales,
                              int64_t hidden, void* out, void* stream);
 
 /*
+ * nvfp4_quantize_global -- NVFP4 with one FP32 scale for the whole tensor.
+ *
+ * The naive NVFP4 that "humans& Open-Sources the First Stable 4-Bit RL
+ * Training Recipe" (section 1) and "NVFP4-RL" (section 2) contrast with
+ * per-token scaling: s = amax over the whole tensor / 1536 (four_over_six 1
+ * or 2) or / 2688 (0), then the block path of nvfp4_quantize in every row
+ * under that s.  A row's outputs therefore depend on the other rows (the
+ * batch dependency those pages warn about).
+ *
+ *   x, codes, block_scales, dequant, four_over_six: as for nvfp4_quantize
+ *                 (no ragged rows).
+ *   tensor_scale  float [1], 4-byte aligned, device memory: receives s; it
+ *                 holds the amax's bit pattern while the call runs, so it
+ *                 must not be read or shared by a concurrent call.
+ */
+fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
+                                  int four_over_six, uint8_t* codes, uint8_t* block_scales,
+                                  float* tensor_scale, void* dequant, void* stream);
+
+/*
  * nvfp4_quantize_guided -- TRACE rollout-guided rounding.
  *
  * Definition: "TRACE FP4 RL -- Rollout-guided FP4 rounding"

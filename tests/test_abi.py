@@ -29,6 +29,7 @@ def test_library_exports_every_declared_call():
     names = declared_functions()
     assert {"nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
             "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "nvfp4_quantize_guided",
+            "nvfp4_quantize_global",
             "fp4q_status_string"} <= set(names)
     L = fq.lib()
     for n in names:
@@ -139,3 +140,17 @@ def test_nvfp4_quantize_guided_rejects():
     assert g(guide=P(0x10002)) == MISALIGNED
     assert g(dq=A8) == MISALIGNED
     assert g(rows=0, x=None, guide=None, codes=None) == SUCCESS
+
+
+def test_nvfp4_quantize_global_rejects():
+    L = fq.lib()
+    g = lambda **k: L.nvfp4_quantize_global(
+        k.get("x", A16), k.get("rows", 4), k.get("hidden", 64), k.get("fos", 1),
+        k.get("codes", A16), A16, k.get("ts", A16), k.get("dq", A16), None)
+    assert g(hidden=24) == SHAPE
+    assert g(fos=3) == INVALID
+    assert g(x=None) == NULL
+    assert g(ts=None) == NULL
+    assert g(ts=P(0x10002)) == MISALIGNED
+    assert g(dq=A8) == MISALIGNED
+    assert g(rows=0, x=None, codes=None, ts=None) == SUCCESS

@@ -296,3 +296,39 @@ def test_guided_random_guides_and_scales():
 def test_guided_moe_act_full_size():
     x = workloads.rows("moe_act")
     check_guided(x, workloads.perturbed(x, seed=2), "guided moe_act")
+
+
+# ------------------------------------------------- global per-tensor scale --
+
+def check_global(x_bits, fos, label):
+    got = fq.nvfp4_quantize_global(to_dev(x_bits), fos)
+    torch.cuda.synchronize()
+    want = oracle.nvfp4_quantize_global(x_bits, fos)
+    assert_same(host(got[0]), want[0], label + " codes")
+    assert_same(host(got[1]), want[1], label + " scales")
+    assert_same(host(got[2])[None, :], want[2][None, :], label + " tensor scale")
+    assert_same(bits_of(got[3]), want[3], label + " dequant")
+
+
+@pytest.mark.parametrize("fos", [1, 0, 2])
+@pytest.mark.parametrize("H", [16, 2048, 7168, 33024])
+def test_global_scale_edge_rows(H, fos):
+    check_global(edge_rows(H, seed=H + 3), fos, "global edge H=%d fos=%d" % (H, fos))
+
+
+def test_global_scale_moe_act_full_size():
+    check_global(workloads.rows("moe_act"), 1, "global moe_act")
+
+
+def test_global_scale_batch_dependency_on_gpu():
+    # per-token results of a row do not depend on its batch; global ones do
+    x = workloads.rows("moe_act", 0, 64)
+    xs = to_dev(x)
+    solo = fq.nvfp4_quantize_global(xs[5:6].contiguous())[0]
+    batch = fq.nvfp4_quantize_global(xs)[0]
+    torch.cuda.synchronize()
+    assert not torch.equal(solo[0], batch[5])
+    p_solo = fq.nvfp4_quantize(xs[5:6].contiguous())[0]
+    p_batch = fq.nvfp4_quantize(xs)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(p_solo[0], p_batch[5])
