@@ -180,29 +180,52 @@ def traffic_record(kernel_key):
 HEADLINE_KEY = "nvfp4_quantize_split<fos,dq> moe_act 8192x7168"
 
 
-def _dispatch_label(name, grid, split_grids):
-    if "nvfp4_quantize_split<true, true" in name:
-        return HEADLINE_KEY if grid == min(split_grids) else \
-            "nvfp4_quantize_split<fos,dq> expert_weights 65536x7168"
-    if "nvfp4_quantize_split<true, false" in name:
-        return "nvfp4_quantize_split<fos> ragged_routed 65536x2048"
-    if "nvfp4_dequantize" in name:
-        return "nvfp4_dequantize moe_act 8192x7168"
-    if "mxfp4_resq" in name:
-        return "mxfp4_resq_quantize resq_act 8192x7168"
-    if "copyBuffer" in name:
-        return "copyBuffer 256 MiB (device copy, counter calibration)"
-    return None
+def _labels(rows):
+    """Name each dispatch of a bench run by what it computes: the kernel,
+    its total work-items (Grid_Size / Grid_Size_X) and, for the global-scale
+    call, the tensor-max pass that precedes its quantize pass."""
+    out = []
+    prev = ""
+    for r in rows:
+        name = r["Kernel_Name"]
+        grid = int(r.get("Grid_Size") or r.get("Grid_Size_X"))
+        lab = None
+        if "nvfp4_quantize_split<1, true" in name:
+            if grid == 8192 * 256:
+                lab = ("nvfp4_quantize_global (quantize pass) moe_act 8192x7168"
+                       if "global_amax_pass" in prev else HEADLINE_KEY)
+            elif grid == 65536 * 256:
+                lab = "nvfp4_quantize_split<fos,dq> expert_weights 65536x7168"
+        elif "nvfp4_quantize_split<1, false" in name and grid == 65536 // 4 * 256:
+            lab = "nvfp4_quantize_split<fos> ragged_routed 65536x2048"
+        elif "nvfp4_quantize_split<2, true" in name and grid == 8192 * 256:
+            lab = "nvfp4_quantize_split<fp16-decision,dq> moe_act 8192x7168"
+        elif "global_amax_pass" in name:
+            lab = "nvfp4_quantize_global (amax pass) moe_act 8192x7168"
+        elif "nvfp4_dequantize" in name:
+            lab = "nvfp4_dequantize moe_act 8192x7168"
+        elif "nvfp4_guided" in name:
+            lab = "nvfp4_quantize_guided moe_act 8192x7168"
+        elif "mxfp4_resq_units<false>" in name:
+            lab = "mxfp4_resq_quantize resq_act 8192x7168"
+        elif "mxfp4_resq_units<true>" in name:
+            lab = "mxfp4_resq_dense_quantize resq_act 8192x7168"
+        elif "mxfp4_reconstruct_units<1>" in name:
+            lab = "mxfp4_resq_reconstruct (S2:4) resq_act 8192x7168"
+        elif "copyBuffer" in name and grid == 131072:
+            lab = "copyBuffer 256 MiB (device copy, counter calibration)"
+        out.append(lab)
+        prev = name
+    return out
 
 
-def _read_dispatches(path):
+def _read_dispatches(path, counter=None):
     import csv
     rows = list(csv.DictReader(open(path)))
-    for r in rows:  # the trace names it Grid_Size_X, the counter table Grid_Size
-        r["Grid_Size"] = r.get("Grid_Size") or r.get("Grid_Size_X")
-    split_grids = {int(r["Grid_Size"]) for r in rows
-                   if "nvfp4_quantize_split<true, true" in r["Kernel_Name"]}
-    return rows, split_grids
+    if counter is not None:  # one row per dispatch and counter
+        rows = [r for r in rows if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0))
+    return rows, _labels(rows)
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
@@ -216,10 +239,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
                "--warmup 2 --sets 2 --no-cpu")
     # kernel durations per (kernel, workload)
     trace = glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0]
-    rows, split_grids = _read_dispatches(trace)
+    rows, labels = _read_dispatches(trace)
     dur = {}
-    for r in rows:
-        lab = _dispatch_label(r["Kernel_Name"], int(r["Grid_Size"]), split_grids)
+    for r, lab in zip(rows, labels):
         if lab:
             dur.setdefault(lab, []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -246,12 +268,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
     # HBM bytes per dispatch, calibrated on the 256 MiB device copy
     def counter(dir_, cname):
         path = glob.glob(os.path.join(dir_, "*counter_collection.csv"))[0]
-        rows, grids = _read_dispatches(path)
+        rows, labels = _read_dispatches(path, cname)
         per = {}
-        for r in rows:
-            if r["Counter_Name"] != cname:
-                continue
-            lab = _dispatch_label(r["Kernel_Name"], int(r["Grid_Size"]), grids)
+        for r, lab in zip(rows, labels):
             if lab:
                 per.setdefault(lab, []).append(float(r["Counter_Value"]))
         return {k: float(np.median(v)) for k, v in per.items()}
@@ -271,6 +290,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
                 (8192 * 7168 // 2 + 8192 * 7168 // 16 + 8192 * 4, 8192 * 7168 * 2),
             "mxfp4_resq_quantize resq_act 8192x7168":
                 (8192 * 7168 * 2, mx_bytes(8192, 7168) - 8192 * 7168 * 2),
+            "mxfp4_resq_dense_quantize resq_act 8192x7168":
+                (8192 * 7168 * 2, 8192 * 7168 // 2 * 2 + 8192 * 7168 // 32 * 2),
+            "mxfp4_resq_reconstruct (S2:4) resq_act 8192x7168":
+                (8192 * 7168 // 2 + 8192 * 7168 // 32 * 2 + 8192 * 7168 // 4 + 8192 * 7168 // 8,
+                 8192 * 7168 * 4),
+            "nvfp4_quantize_guided moe_act 8192x7168":
+                (8192 * 7168 * 2 + 8192 * 7168 // 2 + 8192 * 7168 // 16 + 8192 * 4,
+                 8192 * 7168 // 2),
+            "nvfp4_quantize_split<fp16-decision,dq> moe_act 8192x7168":
+                (8192 * 7168 * 2, nvfp4_bytes(8192, 7168) - 8192 * 7168 * 2),
+            "nvfp4_quantize_global (amax pass) moe_act 8192x7168": (8192 * 7168 * 2, 4),
+            "nvfp4_quantize_global (quantize pass) moe_act 8192x7168":
+                (8192 * 7168 * 2 + 4, nvfp4_bytes(8192, 7168) - 8192 * 7168 * 2 - 8192 * 4),
             copy_key: (copy_bytes, copy_bytes)}
     digest = source_digest()
     table = {}
