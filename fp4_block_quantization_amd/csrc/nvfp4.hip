@@ -79,6 +79,11 @@ namespace {
 #ifndef FP4Q_NV_WAVE_SYNC
 #define FP4Q_NV_WAVE_SYNC 1
 #endif
+// Build-time knob: FP4Q_NV_LDS_CODES = 1 also stages the codes and block
+// scales of each 64-block group in LDS and writes them as 16-byte pieces.
+#ifndef FP4Q_NV_LDS_CODES
+#define FP4Q_NV_LDS_CODES 0
+#endif
 // Build-time knob: blocks per lane in the split kernel (1 or 2).
 #ifndef FP4Q_NV_NB
 #define FP4Q_NV_NB 2
@@ -455,7 +460,9 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
                                                int64_t blk, uint2* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
                                                uint4* __restrict__ dq,
-                                               uint4* stage = nullptr) {
+                                               uint4* stage = nullptr,
+                                               uint2* code_stage = nullptr,
+                                               uint8_t* scale_stage = nullptr) {
   if (__builtin_expect(!rs.fast, 0)) {
     tiny_row_block<FOS, DQ>((const uint16_t*)(xin + 2 * blk), __uint_as_float(bbits), tab, rs.s,
                             rs.inv_s,
@@ -465,8 +472,13 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
   }
   BlockOut o;
   quantize_block_fast<FOS, DQ>(x, bbits, rs, tab, neg_zero, o);
-  store_out(&codes[blk], make_uint2(o.code0, o.code1));
-  store_out(&scales[blk], (uint8_t)o.ebyte);
+  if (code_stage != nullptr) {  // the caller writes codes and scales out contiguously
+    *code_stage = make_uint2(o.code0, o.code1);
+    *scale_stage = (uint8_t)o.ebyte;
+  } else {
+    store_out(&codes[blk], make_uint2(o.code0, o.code1));
+    store_out(&scales[blk], (uint8_t)o.ebyte);
+  }
   if (DQ) {
     if (stage != nullptr) {  // the caller writes the chunk out contiguously
       stage[0] = make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]);
@@ -608,7 +620,12 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // per wave: the input tile (NB x 2 KiB) when loading through LDS, whose
   // half n, once read, stages the dequant values of block group n; else
   // 2 KiB of staging
-  uint4* wave_lds = dyn_lds + 32 * R + (kLdsLoad ? 128 * NB : 128) * (threadIdx.x >> 6);
+  constexpr int kWaveLds = (kLdsLoad ? 128 * NB : 128) + (FP4Q_NV_LDS_CODES ? 36 : 0);
+  uint4* wave_lds = dyn_lds + 32 * R + kWaveLds * (threadIdx.x >> 6);
+  // codes (32 x 16 B) and scales (4 x 16 B) of a 64-block group, after the
+  // dequant staging
+  uint2* code_stage = reinterpret_cast<uint2*>(wave_lds + (kLdsLoad ? 128 * NB : 128));
+  uint8_t* scale_stage = reinterpret_cast<uint8_t*>(wave_lds + (kLdsLoad ? 128 * NB : 128) + 32);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
@@ -657,6 +674,10 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     const RowScale rs = rowinfo[rw];
     constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ;
     const bool stage = kStage && rs.fast;  // wave-uniform
+    // codes and scales leave as 16-byte pieces when the group starts on a
+    // 16-byte boundary of both outputs (wave-uniform)
+    const bool cstage = FP4Q_NV_LDS_CODES && rs.fast && (c.cbase & 15) == 0 &&
+                        ((uintptr_t)scales & 15) == 0 && ((uintptr_t)codes & 15) == 0;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int j = lane + 64 * n;
@@ -665,17 +686,32 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
         float xv[16];
         unpack16(w[n], xv);
         quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, c.cbase + j, codes,
-                                scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr);
+                                scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr,
+                                cstage ? &code_stage[lane] : nullptr,
+                                cstage ? &scale_stage[lane] : nullptr);
       }
-      if (stage && 64 * n < c.valid) {
-        // the 64 blocks' dequant values leave as two contiguous KiB
-        const int nv2 = 2 * min(64, c.valid - 64 * n);
+      if ((stage || cstage) && 64 * n < c.valid) {
+        const int nv = min(64, c.valid - 64 * n);  // blocks of this group
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint4* dqc = dq + 2 * (c.cbase + 64 * n);
-        if (lane < nv2) store_out(&dqc[lane], dq_stage_n[lane]);
-        if (64 + lane < nv2) store_out(&dqc[64 + lane], dq_stage_n[64 + lane]);
+        if (stage) {  // the 64 blocks' dequant values leave as two contiguous KiB
+          uint4* dqc = dq + 2 * (c.cbase + 64 * n);
+          if (lane < 2 * nv) store_out(&dqc[lane], dq_stage_n[lane]);
+          if (64 + lane < 2 * nv) store_out(&dqc[64 + lane], dq_stage_n[64 + lane]);
+        }
+        if (cstage) {
+          const uint4* cs = reinterpret_cast<const uint4*>(code_stage);
+          uint4* cg = reinterpret_cast<uint4*>(codes + c.cbase + 64 * n);
+          if (2 * lane + 1 < nv) store_out(&cg[lane], cs[lane]);
+          if ((nv & 1) && lane == (nv >> 1))  // an odd last block
+            store_out(&codes[c.cbase + 64 * n + nv - 1], code_stage[nv - 1]);
+          const uint4* ss = reinterpret_cast<const uint4*>(scale_stage);
+          uint4* sg = reinterpret_cast<uint4*>(scales + c.cbase + 64 * n);
+          if (16 * lane + 15 < nv) store_out(&sg[lane], ss[lane]);
+          if (lane >= (nv >> 4) * 16 && lane < nv && (nv & 15))  // a partial last piece
+            store_out(&scales[c.cbase + 64 * n + lane], scale_stage[lane]);
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -909,8 +945,10 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
     const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * W * R) * R;  // rows per launch
     const bool lds_load = FP4Q_NV_LDS_LOAD && FP4Q_NV_GRID_PER_CU == 0;
     const size_t lds = (size_t)R * 128 * sizeof(float) +
-                       (lds_load ? (size_t)W * R * NB * 128 * sizeof(uint4)
-                                 : FP4Q_NV_LDS_DQ && DQ ? (size_t)W * R * 128 * sizeof(uint4) : 0);
+                       (size_t)W * R * ((lds_load || (FP4Q_NV_LDS_DQ && DQ) || FP4Q_NV_LDS_CODES)
+                                            ? (lds_load ? (size_t)NB * 128 : 128) +
+                                                  (FP4Q_NV_LDS_CODES ? 36 : 0)
+                                            : 0) * sizeof(uint4);
     int cus = 0;
     if (FP4Q_NV_GRID_PER_CU > 0) {
       int dev = 0;

@@ -31,6 +31,9 @@
 
 #include <stdint.h>
 
+/* The calls below are the library's only exported symbols. */
+#define FP4Q_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -102,7 +105,7 @@ typedef enum {
  *                 BF16_RNE(c_i) of the chosen candidate.
  *   stream        hipStream_t or NULL.
  */
-fp4q_status nvfp4_quantize(const void* x, int64_t rows, int64_t hidden,
+FP4Q_API fp4q_status nvfp4_quantize(const void* x, int64_t rows, int64_t hidden,
                            const int64_t* group_offsets, int64_t num_groups,
                            int four_over_six, uint8_t* codes,
                            uint8_t* block_scales, float* token_scales,
@@ -123,7 +126,7 @@ fp4q_status nvfp4_quantize(const void* x, int64_t rows, int64_t hidden,
  *   rows          >= 0; hidden > 0, a multiple of 16.
  *   out           BF16 [rows, hidden], 16-byte aligned.
  */
-fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales,
+FP4Q_API fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales,
                              const float* token_scales, int64_t rows,
                              int64_t hidden, void* out, void* stream);
 
@@ -143,7 +146,7 @@ fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales,
  *                 holds the amax's bit pattern while the call runs, so it
  *                 must not be read or shared by a concurrent call.
  */
-fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
+FP4Q_API fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
                                   int four_over_six, uint8_t* codes, uint8_t* block_scales,
                                   float* tensor_scale, void* dequant, void* stream);
 
@@ -171,7 +174,7 @@ fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
  *   dequant       BF16 [rows, hidden], 16-byte aligned, or NULL:
  *                 BF16(+-((g*e)*s)) of the guided codes.
  */
-fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
+FP4Q_API fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
                                   const uint8_t* guide_codes, const uint8_t* block_scales,
                                   const float* token_scales, uint8_t* codes, void* dequant,
                                   void* stream);
@@ -202,7 +205,7 @@ fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
  *               nibble i0 | i1 << 2; group 2m in the low nibble of byte m.
  *   res_scales  uint8 [rows, hidden/32]: residual E8M0.
  */
-fp4q_status mxfp4_resq_quantize(const void* x, int64_t rows, int64_t hidden,
+FP4Q_API fp4q_status mxfp4_resq_quantize(const void* x, int64_t rows, int64_t hidden,
                                 uint8_t* codes, uint8_t* scales,
                                 uint8_t* res_codes, uint8_t* res_meta,
                                 uint8_t* res_scales, void* stream);
@@ -217,7 +220,7 @@ fp4q_status mxfp4_resq_quantize(const void* x, int64_t rows, int64_t hidden,
  *   res_codes   uint8 [rows, hidden/2], 16-byte aligned: residual E2M1
  *               nibbles, packed like codes.
  */
-fp4q_status mxfp4_resq_dense_quantize(const void* x, int64_t rows, int64_t hidden,
+FP4Q_API fp4q_status mxfp4_resq_dense_quantize(const void* x, int64_t rows, int64_t hidden,
                                       uint8_t* codes, uint8_t* scales,
                                       uint8_t* res_codes, uint8_t* res_scales,
                                       void* stream);
@@ -240,13 +243,13 @@ fp4q_status mxfp4_resq_dense_quantize(const void* x, int64_t rows, int64_t hidde
  *   rows >= 0; hidden > 0, a multiple of 32.
  *   out         float [rows, hidden], 16-byte aligned.
  */
-fp4q_status mxfp4_resq_reconstruct(const uint8_t* codes, const uint8_t* scales,
+FP4Q_API fp4q_status mxfp4_resq_reconstruct(const uint8_t* codes, const uint8_t* scales,
                                    const uint8_t* res_codes, const uint8_t* res_meta,
                                    const uint8_t* res_scales, int64_t rows, int64_t hidden,
                                    int residual, float* out, void* stream);
 
 /* Static description of a status (never NULL). */
-const char* fp4q_status_string(fp4q_status status);
+FP4Q_API const char* fp4q_status_string(fp4q_status status);
 
 #ifdef __cplusplus
 }

@@ -20,13 +20,14 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         src = open(h).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
-                            src, flags=re.M)
+        names += re.findall(r"^\s*(?:FP4Q_API\s+)?(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
+                            r"([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
 def test_library_exports_every_declared_call():
     names = declared_functions()
+    assert len(names) == 8, names
     assert {"nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
             "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "nvfp4_quantize_guided",
             "nvfp4_quantize_global",
