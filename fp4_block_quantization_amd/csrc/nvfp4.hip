@@ -855,20 +855,52 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
     const float e = e4m3_value<0>(sin[j >> 1]);
     const float d = e * s;
     const float r = d != 0.0f ? 1.0f / d : 0.0f;  // fl(1 / fl(e s)), IEEE
+    // With lo <= hi adjacent (or equal) codes, the guide rule is a clamp:
+    // the guide's magnitude code when the signs agree (else 0), clamped to
+    // [lo, hi].
     uint32_t out = 0u;
+    if (__builtin_expect(r < __builtin_inff(), 1)) {
+      // v is finite: the hardware rounding to nearest gives q, its value g,
+      // and the neighbours q - [g > v] and q + [g < v] (not above 7)
+      float v[8];
+      uint32_t qw = 0u;
+      static_for<0, 4>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        v[2 * p] = fabsf(bf16_lo(w[p])) * r;
+        v[2 * p + 1] = fabsf(bf16_hi(w[p])) * r;
+        qw = cvt_e2m1x2<p>(qw, v[2 * p], v[2 * p + 1]);
+      });
+      static_for<0, 4>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        const float2v g = e2m1x2_values<p>(qw);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float xi = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
-      const float v = fabsf(xi) * r;
-      // lower and upper neighbours: the number of grid values <= v (minus
-      // one) and the code above it when v is not itself a grid value
-      uint32_t lo = (v >= 0.5f) + (v >= 1.0f) + (v >= 1.5f) + (v >= 2.0f) + (v >= 3.0f) +
-                    (v >= 4.0f) + (v >= 6.0f);
-      const uint32_t hi = (lo < 7u && e2m1_value(lo) < v) ? lo + 1u : lo;
-      const uint32_t gn = (gwd >> (4 * i)) & 15u;
-      const uint32_t sx = __float_as_uint(xi) >> 31;
-      const uint32_t q = (hi != lo && (gn >> 3) == sx && (gn & 7u) >= hi) ? hi : lo;
-      out |= ((sx << 3) | q) << (4 * i);
+        for (int h = 0; h < 2; ++h) {
+          const int i = 2 * p + h;
+          const uint32_t q = (qw >> (4 * i)) & 7u;
+          const float gi = h ? g.y : g.x;
+          const uint32_t lo = q - (gi > v[i] ? 1u : 0u);
+          const uint32_t hi = q + ((gi < v[i] && q < 7u) ? 1u : 0u);
+          const uint32_t gn = (gwd >> (4 * i)) & 15u;
+          const uint32_t sx = (w[p] >> (h ? 31 : 15)) & 1u;
+          const uint32_t m = (gn >> 3) == sx ? (gn & 7u) : 0u;
+          out |= ((sx << 3) | min(max(m, lo), hi)) << (4 * i);
+        }
+      });
+    } else {
+      // r = +inf (a subnormal decode step): v may be +inf or NaN, which the
+      // threshold counts follow as the definition does
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xi = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+        const float vi = fabsf(xi) * r;
+        const uint32_t lo = (vi >= 0.5f) + (vi >= 1.0f) + (vi >= 1.5f) + (vi >= 2.0f) +
+                            (vi >= 3.0f) + (vi >= 4.0f) + (vi >= 6.0f);
+        const uint32_t hi = (lo < 7u && e2m1_value(lo) < vi) ? lo + 1u : lo;
+        const uint32_t gn = (gwd >> (4 * i)) & 15u;
+        const uint32_t sx = __float_as_uint(xi) >> 31;
+        const uint32_t m = (gn >> 3) == sx ? (gn & 7u) : 0u;
+        out |= ((sx << 3) | min(max(m, lo), hi)) << (4 * i);
+      }
     }
     store_out(&codes[base + j], out);
     if (dq != nullptr) {
