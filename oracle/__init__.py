@@ -21,9 +21,12 @@ def lib():
     """Load (building first if needed) the oracle shared library."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB_PATH):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB_PATH)
+        path = os.environ.get("FP4Q_ORACLE_LIB")  # a test may load another build
+        if path is None:
+            if not os.path.exists(_build.LIB_PATH):
+                _build.build()
+            path = _build.LIB_PATH
+        L = ctypes.CDLL(path)
         c_f = ctypes.c_float
         c_i64 = ctypes.c_int64
         vp = ctypes.c_void_p

@@ -16,6 +16,8 @@ scaled down by the inverse token scale).
   large fraction.
 - Codes and scales of each candidate are those of the exact path: where the
   two choices agree, the outputs are identical.
+- A block with one nonzero element reduces to one term, (FP16(FP16(|x| *
+  inv_s) - g e))^2, with numpy's IEEE binary16 conversion as the rounding.
 """
 import ctypes
 import math
@@ -115,3 +117,25 @@ def test_fp16_choice_agreement_on_workloads(name, nrows):
         blk = oracle.nvfp4_block(
             (x[r, 16 * j:16 * j + 16].astype(np.uint32) << 16).view(np.float32), exact[2][r], 2)
         assert {int(exact[1][r, j]), int(fast[1][r, j])} == set(int(v) for v in blk.e_byte)
+
+
+def test_single_element_blocks_reduce_to_one_fp16_term():
+    rng = np.random.default_rng(13)
+    checked = 0
+    for _ in range(3000):
+        s = np.float32(2.0 ** rng.uniform(-30, 20) * rng.uniform(1, 2))
+        x = np.zeros(16, np.float32)
+        mag = np.float32(s * rng.uniform(1, 1536))
+        x[rng.integers(16)] = np.float32(-mag if rng.integers(2) else mag)
+        x = (x.view(np.uint32) & 0xFFFF0000).view(np.float32)  # BF16 values
+        b = oracle.nvfp4_block(x, float(s), 2)
+        inv_s = np.float32(1) / np.float32(s)
+        i = int(np.nonzero(x)[0][0])
+        y = np.float16(np.abs(x[i]) * inv_s)
+        for k in range(2):
+            ge = np.float16(oracle.e2m1_value(b.code[k][i] & 7) * b.e[k])
+            d = np.float16(y - ge)
+            want = np.float32(np.float32(d) * np.float32(d))
+            assert b.err16[k] == want, (x[i], s, k)
+        checked += 1
+    assert checked == 3000
