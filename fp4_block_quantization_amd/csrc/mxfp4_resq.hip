@@ -26,21 +26,32 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Build-time knob: FP4Q_MX_NT_STORES = 1 writes the outputs with
-// non-temporal stores.
+// Build-time knobs: FP4Q_MX_NT_STORES = 1 writes the outputs with
+// non-temporal stores; FP4Q_MX_LDS_STAGE = 1 gathers a wavefront's outputs
+// in LDS and writes them as 16-byte pieces.
+#ifndef FP4Q_MX_LDS_STAGE
+#define FP4Q_MX_LDS_STAGE 1
+#endif
 #ifndef FP4Q_MX_NT_LOADS
 #define FP4Q_MX_NT_LOADS 1
 #endif
 #ifndef FP4Q_MX_NT_STORES
-#define FP4Q_MX_NT_STORES 0
+#define FP4Q_MX_NT_STORES 1
 #endif
 #ifndef FP4Q_MX_NT_SMALL
-#define FP4Q_MX_NT_SMALL 1
+#define FP4Q_MX_NT_SMALL 0
 #endif
 template <typename T>
 __device__ __forceinline__ void store_out(T* p, T v) {
   if (FP4Q_MX_NT_STORES)
     __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+__device__ __forceinline__ void store_out(uint4* p, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  if (FP4Q_MX_NT_STORES)
+    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, (u32x4*)p);
   else
     *p = v;
 }
@@ -124,7 +135,7 @@ __device__ __forceinline__ uint32_t select_2of4(uint32_t rw, const uint16_t* tab
 // load instruction reads 1 KiB contiguously.  The four lanes of a quad hold
 // one 32-element block per unit slot and share its scale through DPP.
 #ifndef FP4Q_MX_UNITS
-#define FP4Q_MX_UNITS 2
+#define FP4Q_MX_UNITS 4
 #endif
 constexpr int kUnitsPerLane = FP4Q_MX_UNITS;
 
@@ -171,11 +182,30 @@ __device__ __forceinline__ void resq_unit(const uint4 a, uint32_t& cw, uint32_t&
 // DENSE = false: Rollout-ResQ with S_{2:4} (res_codes uint16 per unit,
 // res_meta one byte per unit); DENSE = true: Rollout-ResQ-Dense (res_codes
 // uint32 per unit, packed like the primary codes).
+//
+// Staged stores (stage != 0: every output 16-byte aligned; wave-uniform
+// for a wavefront whose 64 * NU units all exist): the five outputs of the
+// wavefront's units are contiguous ranges -- codes 4 bytes a unit, residual
+// codes 2 (dense 4), metadata 1, each scale 1 per 4 units -- so they are
+// gathered in the wavefront's LDS area, in that order, and leave as 16-byte
+// pieces, each lane writing one piece of whichever output it falls in.
+template <bool DENSE>
+struct StageLayout {
+  static constexpr int kCode = 16 * kUnitsPerLane;  // 16-byte pieces of each output
+  static constexpr int kRes = (DENSE ? 16 : 8) * kUnitsPerLane;
+  static constexpr int kMeta = DENSE ? 0 : 4 * kUnitsPerLane;
+  static constexpr int kSc = kUnitsPerLane;
+  static constexpr int kResAt = kCode, kMetaAt = kResAt + kRes, kScAt = kMetaAt + kMeta,
+                       kRscAt = kScAt + kSc, kPieces = kRscAt + kSc;
+};
+
 template <bool DENSE>
 __global__ __launch_bounds__(256) void mxfp4_resq_units(
     const uint4* __restrict__ x, int64_t u0, int64_t u_end, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, void* __restrict__ res_codes,
-    uint8_t* __restrict__ res_meta, uint8_t* __restrict__ res_scales) {
+    uint8_t* __restrict__ res_meta, uint8_t* __restrict__ res_scales, int stage) {
+  typedef StageLayout<DENSE> SL;
+  __shared__ uint4 stage_lds[FP4Q_MX_LDS_STAGE ? 4 * SL::kPieces : 1];
   // the 2:4 table (8 KiB) into LDS
   __shared__ uint4 tab_lds[DENSE ? 1 : 512];
   if (!DENSE) {
@@ -198,6 +228,8 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   uint32_t* cw_out = codes + ub;
   uint8_t* sc_out = scales + (ub >> 2);
   uint8_t* rs_out = res_scales + (ub >> 2);
+  const bool staged = FP4Q_MX_LDS_STAGE && stage != 0 && nv == 64 * kUnitsPerLane;
+  uint8_t* sb = reinterpret_cast<uint8_t*>(stage_lds + (FP4Q_MX_LDS_STAGE ? wave * SL::kPieces : 0));
   uint4 a[kUnitsPerLane];
 #pragma unroll
   for (int n = 0; n < kUnitsPerLane; ++n)
@@ -218,6 +250,22 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
       uint32_t cw, rw;
       int k, kr;
       resq_unit(a[n], cw, rw, k, kr);
+      if (staged) {
+        reinterpret_cast<uint32_t*>(sb)[j] = cw;
+        if (DENSE) {
+          reinterpret_cast<uint32_t*>(sb + 16 * SL::kResAt)[j] = rw;
+        } else {
+          uint32_t meta;
+          const uint32_t rc = select_2of4(rw, tab, meta);
+          reinterpret_cast<uint16_t*>(sb + 16 * SL::kResAt)[j] = (uint16_t)rc;
+          sb[16 * SL::kMetaAt + j] = (uint8_t)meta;
+        }
+        if ((lane & 3) == 0) {
+          sb[16 * SL::kScAt + (j >> 2)] = (uint8_t)(k + 127);
+          sb[16 * SL::kRscAt + (j >> 2)] = (uint8_t)(kr + 127);
+        }
+        continue;
+      }
       if (DENSE) {
         if (j < nv) store_out(&(reinterpret_cast<uint32_t*>(res_codes) + ub)[j], rw);
       } else {
@@ -234,6 +282,31 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
           store_small(&sc_out[j >> 2], (uint8_t)(k + 127));
           store_small(&rs_out[j >> 2], (uint8_t)(kr + 127));
         }
+      }
+    }
+  }
+  if (staged) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint4* st = stage_lds + wave * SL::kPieces;
+#pragma unroll
+    for (int p0 = 0; p0 < SL::kPieces; p0 += 64) {
+      const int p = p0 + lane;
+      if (p < SL::kPieces) {
+        uint4* dst;
+        if (p < SL::kResAt)
+          dst = reinterpret_cast<uint4*>(cw_out) + p;
+        else if (p < SL::kMetaAt)
+          dst = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(res_codes) +
+                                         ub * (DENSE ? 4 : 2)) + (p - SL::kResAt);
+        else if (p < SL::kScAt)
+          dst = reinterpret_cast<uint4*>(res_meta + ub) + (p - SL::kMetaAt);
+        else if (p < SL::kRscAt)
+          dst = reinterpret_cast<uint4*>(sc_out) + (p - SL::kScAt);
+        else
+          dst = reinterpret_cast<uint4*>(rs_out) + (p - SL::kRscAt);
+        store_out(dst, st[p]);
       }
     }
   }
@@ -289,12 +362,15 @@ hipError_t resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* cod
                        hipStream_t st) {
   const int64_t nunits = rows * (hidden / 8);  // a multiple of 4
   const int64_t max_units = FP4Q_MAX_LAUNCH_ITEMS / 256 * 256 * kUnitsPerLane;
+  const auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const int stage = a16(codes) && a16(scales) && a16(res_codes) && a16(res_scales) &&
+                    (DENSE || a16(res_meta));
   for (int64_t u0 = 0; u0 < nunits; u0 += max_units) {
     const int64_t n = nunits - u0 < max_units ? nunits - u0 : max_units;
     constexpr int64_t per_wg = 256 * kUnitsPerLane;
     const dim3 grid((unsigned)((n + per_wg - 1) / per_wg)), block(256);
     hipLaunchKernelGGL(mxfp4_resq_units<DENSE>, grid, block, 0, st, (const uint4*)x, u0, u0 + n,
-                       (uint32_t*)codes, scales, res_codes, res_meta, res_scales);
+                       (uint32_t*)codes, scales, res_codes, res_meta, res_scales, stage);
   }
   return hipGetLastError();
 }

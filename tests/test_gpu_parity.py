@@ -196,6 +196,51 @@ def test_resq_act_full_size():
     check_mx(workloads.rows("resq_act"), label="resq_act")
 
 
+def _at_offset(shape, offset, bufs):
+    """A contiguous uint8 tensor whose data starts `offset` bytes past a
+    256-byte aligned allocation filled with 0xA5 (kept in bufs with the
+    view's range, to check that nothing outside it is written)."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 256,), 0xA5, dtype=torch.uint8, device="cuda")
+    bufs.append((buf, offset, n))
+    return buf[offset:offset + n].view(shape)
+
+
+def _guards_intact(bufs):
+    for buf, o, n in bufs:
+        b = buf.cpu().numpy()
+        assert (b[:o] == 0xA5).all() and (b[o + n:] == 0xA5).all(), (o, n)
+
+
+@pytest.mark.parametrize("offsets", [(0, 1, 0, 0, 3), (0, 0, 8, 4, 0), (0, 5, 8, 4, 9)])
+def test_mx_outputs_not_16_byte_aligned(offsets):
+    """Outputs that are not all 16-byte aligned are written lane by lane
+    instead of as staged 16-byte pieces; the bytes are the same."""
+    rng = np.random.default_rng(sum(offsets))
+    x_bits = np.concatenate([edge_rows(2048, seed=7),
+                             f32_to_bf16_bits(rng.standard_normal((48, 2048)).astype(np.float32))])
+    R, H = x_bits.shape
+    shapes = ((R, H // 2), (R, H // 32), (R, H // 4), (R, H // 8), (R, H // 32))
+    bufs = []
+    out = tuple(_at_offset(sh, o, bufs) for sh, o in zip(shapes, offsets))
+    got = fq.mxfp4_resq_quantize(to_dev(x_bits), out=out)
+    torch.cuda.synchronize()
+    _guards_intact(bufs)
+    want = oracle_mx(x_bits)
+    for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
+        assert_same(host(g), w, "offsets %s %s" % (offsets, n))
+    dshapes = ((R, H // 2), (R, H // 32), (R, H // 2), (R, H // 32))
+    dbufs = []
+    dout = tuple(_at_offset(sh, o, dbufs)
+                 for sh, o in zip(dshapes, (0, offsets[1], 0, offsets[4])))
+    gd = fq.mxfp4_resq_dense_quantize(to_dev(x_bits), out=dout)
+    torch.cuda.synchronize()
+    _guards_intact(dbufs)
+    wd = oracle_mx_dense(x_bits)
+    for g, w, n in zip(gd, wd, ("codes", "scales", "res_codes", "res_scales")):
+        assert_same(host(g), w, "dense offsets %s %s" % (offsets, n))
+
+
 # -------------------------------------------------------------- dequant --
 
 def test_standalone_dequant_matches_fused():
