@@ -45,10 +45,13 @@ namespace {
 #define FP4Q_NV_NT_STORES 1
 #endif
 
-// Build-time knob: FP4Q_NV_NT_LOADS = 1 reads the input with non-temporal
-// loads (it is read once).
+// Build-time knob: FP4Q_NV_NT_LOADS = 1 makes the contiguous input copies
+// into LDS (FP4Q_NV_LDS_LOAD) non-temporal: the input is read once, and each
+// of those instructions covers whole cache lines.  Loads straight into
+// registers stay ordinary: a lane's block is two 16-byte loads 32 bytes
+// apart, so every line is read by two instructions.
 #ifndef FP4Q_NV_NT_LOADS
-#define FP4Q_NV_NT_LOADS 0
+#define FP4Q_NV_NT_LOADS 1
 #endif
 
 // Build-time knob: FP4Q_NV_LDS_DQ = 1 stages each wave's dequant chunk
@@ -72,7 +75,7 @@ namespace {
 // into LDS with 16-byte-per-lane contiguous loads (global_load_lds) and
 // reads the lane's blocks from there.
 #ifndef FP4Q_NV_LDS_LOAD
-#define FP4Q_NV_LDS_LOAD 0
+#define FP4Q_NV_LDS_LOAD 1
 #endif
 // Build-time knob: FP4Q_NV_WAVE_SYNC = 1 replaces the workgroup barriers
 // by wave barriers when each row has a single wave.
@@ -302,14 +305,23 @@ __device__ __forceinline__ float fp16_error(const half2v (&y)[8], const uint32_t
 // The FP32 error is sum (x-c)^2 (1 +- 18.1u), plus at most 2^-145 from
 // underflow.  Every coefficient below carries a factor of two or more over
 // these (which also covers the rounding of this arithmetic), and the range of
-// s keeps D^2 normal and every error finite.
+// s keeps D^2 normal and every error finite.  sqrt(A) enters through an
+// upper bound: halving the exponent of A (adding the bias, then a right
+// shift of the bit pattern) gives 2^k (1 + f/2) for A = 4^k (1 + f) and
+// 2^k (3/2 + f/2) for A = 2 4^k (1 + f), both >= the square root (AM-GM,
+// and (3/2 + f/2)^2 - 2(1 + f) = (1 - f)^2 / 4), within a factor 1.07 of it
+// for normal A (for subnormal A it is 2^-63 or more, still >= sqrt(A)).
+// Adding one more before the shift rounds the halving up, so the dropped
+// bit cannot take the result below the square root where the two meet
+// (f -> 1).  A < 2^64 here, so the sum does not wrap.
 struct ErrBounds {
   float lo, hi;
 };
 __device__ __forceinline__ ErrBounds err_bounds(float A, float D) {
   constexpr float u = 0x1p-24f;
   const float D2 = D * D;
-  const float t = __builtin_fmaf(520.0f * u, __builtin_amdgcn_sqrtf(A), 40.0f * u);
+  const float sq = __uint_as_float((__float_as_uint(A) + 0x3F800001u) >> 1);  // >= sqrt(A)
+  const float t = __builtin_fmaf(520.0f * u, sq, 40.0f * u);
   const float hi = __builtin_fmaf(A, 1.0f + 80.0f * u, t);
   const float lo = __builtin_fmaf(A, 1.0f - 80.0f * u, -t);
   return {__builtin_fmaf(D2, lo, -0x1p-136f), __builtin_fmaf(D2, hi, 0x1p-136f)};
@@ -500,13 +512,7 @@ __device__ __forceinline__ bool row_range(int64_t row, int64_t rows, const int64
   return row >= lo && row < hi;
 }
 
-__device__ __forceinline__ uint4 load_in(const uint4* p) {
-  if (FP4Q_NV_NT_LOADS) {
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-  }
-  return *p;
-}
+__device__ __forceinline__ uint4 load_in(const uint4* p) { return *p; }
 
 __device__ __forceinline__ void load_block(const uint4* __restrict__ x, int64_t blk,
                                            uint32_t (&w)[8]) {
@@ -586,7 +592,8 @@ __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, cons
     for (int k = 0; k < 2; ++k) {
       const int q = 128 * n + 64 * k + lane;  // 16-byte unit of the chunk
       if (64 * n < c.valid && (q >> 1) < c.valid)
-        __builtin_amdgcn_global_load_lds(xc + q, (lds_void*)(tile + 128 * n + 64 * k), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(xc + q, (lds_void*)(tile + 128 * n + 64 * k), 16, 0,
+                                         FP4Q_NV_NT_LOADS ? 2 : 0);  // 2: non-temporal
     }
   __builtin_amdgcn_s_waitcnt(0);  // the copies have landed in LDS
 #pragma unroll
