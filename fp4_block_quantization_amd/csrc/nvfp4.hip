@@ -782,6 +782,11 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
 #ifndef FP4Q_DQ_NT_STORES
 #define FP4Q_DQ_NT_STORES 1
 #endif
+// Build-time knob: FP4Q_GUIDED_NT_LOADS = 1 reads the input (bit 0) and the
+// guide codes (bit 1) of the guided quantizer with non-temporal loads.
+#ifndef FP4Q_GUIDED_NT_LOADS
+#define FP4Q_GUIDED_NT_LOADS 1
+#endif
 __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tscale, int64_t row0, int64_t row_end, int h8, uint32_t wpr,
@@ -856,9 +861,15 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
   for (int n = 0; n < NU; ++n) {
     const int j = lane + 64 * n;
     if (j >= nv) continue;
-    const uint4 a = xin[j];
+    uint4 a;
+    if (FP4Q_GUIDED_NT_LOADS & 1) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)&xin[j]);
+      a = make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+      a = xin[j];
+    }
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t gwd = gin[j];
+    const uint32_t gwd = (FP4Q_GUIDED_NT_LOADS & 2) ? __builtin_nontemporal_load(&gin[j]) : gin[j];
     const float e = e4m3_value<0>(sin[j >> 1]);
     const float d = e * s;
     const float r = d != 0.0f ? 1.0f / d : 0.0f;  // fl(1 / fl(e s)), IEEE
