@@ -198,7 +198,8 @@ HEADLINE_KEY = "nvfp4_quantize_split<fos,dq> moe_act 8192x7168"
 def _labels(rows):
     """Name each dispatch of a bench run by what it computes: the kernel,
     its total work-items (Grid_Size / Grid_Size_X) and, for the global-scale
-    call, the tensor-max pass that precedes its quantize pass."""
+    call, the reduction of the tensor-max partials that precedes its
+    quantize pass."""
     out = []
     prev = ""
     for r in rows:
@@ -208,7 +209,7 @@ def _labels(rows):
         if "nvfp4_quantize_split<1, true" in name:
             if grid == 8192 * 256:
                 lab = ("nvfp4_quantize_global (quantize pass) moe_act 8192x7168"
-                       if "global_amax_pass" in prev else HEADLINE_KEY)
+                       if "global_amax_reduce" in prev else HEADLINE_KEY)
             elif grid == 65536 * 256:
                 lab = "nvfp4_quantize_split<fos,dq> expert_weights 65536x7168"
         elif "nvfp4_quantize_split<1, false" in name and grid == 65536 // 4 * 256:
@@ -217,6 +218,8 @@ def _labels(rows):
             lab = "nvfp4_quantize_split<fp16-decision,dq> moe_act 8192x7168"
         elif "global_amax_pass" in name:
             lab = "nvfp4_quantize_global (amax pass) moe_act 8192x7168"
+        elif "global_amax_reduce" in name:
+            lab = "nvfp4_quantize_global (partials reduce) moe_act 8192x7168"
         elif "nvfp4_dequantize" in name:
             lab = "nvfp4_dequantize moe_act 8192x7168"
         elif "nvfp4_guided" in name:
@@ -315,7 +318,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
                  8192 * 7168 // 2),
             "nvfp4_quantize_split<fp16-decision,dq> moe_act 8192x7168":
                 (8192 * 7168 * 2, nvfp4_bytes(8192, 7168) - 8192 * 7168 * 2),
-            "nvfp4_quantize_global (amax pass) moe_act 8192x7168": (8192 * 7168 * 2, 4),
+            "nvfp4_quantize_global (amax pass) moe_act 8192x7168": (8192 * 7168 * 2, 4 * 1024),
+            "nvfp4_quantize_global (partials reduce) moe_act 8192x7168": (4 * 1024, 4),
             "nvfp4_quantize_global (quantize pass) moe_act 8192x7168":
                 (8192 * 7168 * 2 + 4, nvfp4_bytes(8192, 7168) - 8192 * 7168 * 2 - 8192 * 4),
             copy_key: (copy_bytes, copy_bytes)}

@@ -25,7 +25,7 @@ struct NvQuantArgs {
   uint8_t* block_scales;
   float* token_scales;
   void* dequant;
-  const uint32_t* global_amax = nullptr;  // set: one scale for the whole tensor
+  const float* global_scale = nullptr;  // set: the token scale s of every row (one for the tensor)
 };
 
 hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t stream);

@@ -181,10 +181,11 @@ struct RowScale {
   float inv_s;       // fl(1 / s), for the FP16 decision (FOS == 2)
 };
 
+// Row constants from the token scale s itself.
 template <int FOS>
-__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
+__device__ __forceinline__ RowScale row_scale_s(float s) {
   RowScale r;
-  r.s = __uint_as_float(amax_bits) / (FOS ? 1536.0f : 2688.0f);
+  r.s = s;
   r.ks6 = (r.s != 0.0f) ? 6.0f * r.s : 1.0f;
   r.ks4 = (r.s != 0.0f) ? 4.0f * r.s : 1.0f;
   r.rks6 = __builtin_amdgcn_rcpf(r.ks6);
@@ -195,6 +196,13 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
   r.certify = r.s >= 0x1p-50f && r.s <= 0x1p40f;
   r.inv_s = FOS == 2 ? 1.0f / r.s : 0.0f;
   return r;
+}
+
+// Row constants from the row amax (a non-negative float's bit pattern):
+// s = fl(amax / C).
+template <int FOS>
+__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
+  return row_scale_s<FOS>(__uint_as_float(amax_bits) / (FOS ? 1536.0f : 2688.0f));
 }
 
 // tab[byte] = 1 / fl(e(byte) s) for the E4M3 bytes this lane covers.
@@ -615,7 +623,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     int R, int64_t ngrp, const int64_t* __restrict__ offs, int64_t ngroups,
     uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
-    float neg_zero, const uint32_t* __restrict__ gamax) {
+    float neg_zero, const float* __restrict__ gscale) {
   __shared__ uint32_t wave_max[kMaxWgWaves];
   __shared__ RowScale rowinfo[kMaxWgWaves];
   // dynamic LDS: the reciprocal table of each row (R x 128 floats), then,
@@ -669,8 +677,9 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     if (chunk < 2) {
       uint32_t amax_bits = 0;
       for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
-      if (gamax != nullptr) amax_bits = *gamax;  // one scale for the whole tensor
-      const RowScale rs = row_scale<FOS>(amax_bits);
+      // with gscale, one token scale for the whole tensor
+      const RowScale rs =
+          gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
       if (chunk == 0 && lane == 0) {
         rowinfo[rw] = rs;
         if (c.active && tscale != nullptr) tscale[c.row] = rs.s;
@@ -742,7 +751,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk,
     const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
-    float neg_zero, const uint32_t* __restrict__ gamax) {
+    float neg_zero, const float* __restrict__ gscale) {
   __shared__ float recip[kLongWaves][128];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -757,7 +766,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     lmax = max(lmax, block_absmax_bits(w));
   }
   const uint32_t row_amax = wave_max_u32(lmax);
-  const RowScale rs = row_scale<FOS>(gamax != nullptr ? *gamax : row_amax);
+  const RowScale rs = gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(row_amax);
   if (lane == 0 && tscale != nullptr) tscale[row] = rs.s;
   fill_recip(recip[wave], rs.s, lane, 64);
   __builtin_amdgcn_wave_barrier();
@@ -934,24 +943,48 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
   }
 }
 
-// One FP32 scale for the whole tensor: the tensor amax is gathered with a
-// vector atomic max on its bit pattern (non-negative floats order like
-// their bits) into the caller's scale slot, the blocks are quantized under
-// it, and the slot finally receives s = amax / C.
-__global__ void global_amax_init(uint32_t* slot) { *slot = 0u; }
+// One FP32 scale for the whole tensor: every workgroup of the max pass
+// writes the max of its share as a bit pattern (non-negative floats order
+// like their bits) to its own word of a partial array, one workgroup
+// reduces the partials and writes s = fl(amax / C) to the caller's scale,
+// and the blocks are quantized under it.  (With one atomic max per
+// workgroup on a single word instead, the atomics serialize and grow with
+// the grid.)
+
+// Build-time knobs of the tensor max pass: workgroups (FP4Q_GAMAX_GRID),
+// 16-byte loads in flight per lane (FP4Q_GAMAX_DEPTH), non-temporal loads
+// (FP4Q_GAMAX_NT).
+#ifndef FP4Q_GAMAX_GRID
+#define FP4Q_GAMAX_GRID 512
+#endif
+#ifndef FP4Q_GAMAX_DEPTH
+#define FP4Q_GAMAX_DEPTH 4
+#endif
+#ifndef FP4Q_GAMAX_NT
+#define FP4Q_GAMAX_NT 0
+#endif
 
 __global__ __launch_bounds__(256) void global_amax_pass(const uint4* __restrict__ x,
-                                                        int64_t n16, uint32_t* slot) {
+                                                        int64_t n16,
+                                                        uint32_t* __restrict__ partial) {
   __shared__ uint32_t wmax[4];
   uint32_t m = 0u;
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {  // four loads in flight per lane
-    uint4 a[4];
+  constexpr int D = FP4Q_GAMAX_DEPTH;
+  for (; i + (D - 1) * stride < n16; i += D * stride) {  // D loads in flight per lane
+    uint4 a[D];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = x[i + u * stride];
+    for (int u = 0; u < D; ++u) {
+      if (FP4Q_GAMAX_NT) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)&x[i + u * stride]);
+        a[u] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        a[u] = x[i + u * stride];
+      }
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < D; ++u) {
       const uint32_t w[4] = {a[u].x & 0x7FFF7FFFu, a[u].y & 0x7FFF7FFFu, a[u].z & 0x7FFF7FFFu,
                              a[u].w & 0x7FFF7FFFu};
 #pragma unroll
@@ -968,18 +1001,23 @@ __global__ __launch_bounds__(256) void global_amax_pass(const uint4* __restrict_
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-    // one atomic per workgroup, skipped when the slot already holds as much
-    if (m > __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-      atomicMax(slot, m);
-  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
 }
 
 template <int FOS>
-__global__ void global_scale_final(uint32_t* slot) {
-  *reinterpret_cast<float*>(slot) = __uint_as_float(*slot) / (FOS ? 1536.0f : 2688.0f);
+__global__ __launch_bounds__(256) void global_amax_reduce(const uint32_t* __restrict__ partial,
+                                                          int n, float* __restrict__ scale) {
+  __shared__ uint32_t wmax[4];
+  uint32_t m = 0u;
+  for (int i = threadIdx.x; i < n; i += 256) m = max(m, partial[i]);
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *scale = __uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]))) /
+             (FOS ? 1536.0f : 2688.0f);
 }
+
 
 template <int FOS, bool DQ>
 hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
@@ -1015,7 +1053,7 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
       const dim3 grid((unsigned)nwg), block(64 * W * R);
       hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, lds, st, x, a.rows,
                          row0, row_end, nblk, W, R, ngrp, a.offsets, a.num_groups, codes,
-                         a.block_scales, a.token_scales, dq, neg_zero, a.global_amax);
+                         a.block_scales, a.token_scales, dq, neg_zero, a.global_scale);
     }
   } else {
     const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * kLongWaves) * kLongWaves;
@@ -1025,7 +1063,7 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
           block(64 * kLongWaves);
       hipLaunchKernelGGL((nvfp4_quantize_long_rows<FOS, DQ>), grid, block, 0, st, x, a.rows, row0,
                          row_end, nblk, a.offsets, a.num_groups, codes, a.block_scales,
-                         a.token_scales, dq, neg_zero, a.global_amax);
+                         a.token_scales, dq, neg_zero, a.global_scale);
     }
   }
   return hipGetLastError();
@@ -1036,22 +1074,24 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
 hipError_t nvfp4_quantize_global_launch(const NvQuantArgs& args, float* tensor_scale,
                                         hipStream_t st) {
   NvQuantArgs a = args;
-  uint32_t* slot = reinterpret_cast<uint32_t*>(tensor_scale);
-  hipLaunchKernelGGL(global_amax_init, dim3(1), dim3(1), 0, st, slot);
-  const int64_t n16 = a.rows * a.hidden / 8;  // 16-byte units
+  const int64_t n16 = a.rows * a.hidden / 8;  // 16-byte units, >= 2
   int64_t grid = (n16 + 255) / 256;
-  if (grid > 1024) grid = 1024;
+  if (grid > FP4Q_GAMAX_GRID) grid = FP4Q_GAMAX_GRID;
+  // The partial maxima (4 bytes per workgroup) live in the codes output,
+  // which the quantize pass overwrites afterwards: it holds 4 n16 >= 4 grid
+  // bytes and is 8-byte aligned.
+  uint32_t* partial = reinterpret_cast<uint32_t*>(a.codes);
   hipLaunchKernelGGL(global_amax_pass, dim3((unsigned)grid), dim3(256), 0, st,
-                     (const uint4*)a.x, n16, slot);
-  a.global_amax = slot;
-  a.token_scales = nullptr;
-  hipError_t e = nvfp4_quantize_launch(a, st);
-  if (e != hipSuccess) return e;
+                     (const uint4*)a.x, n16, partial);
   if (a.four_over_six)
-    hipLaunchKernelGGL(global_scale_final<1>, dim3(1), dim3(1), 0, st, slot);
+    hipLaunchKernelGGL(global_amax_reduce<1>, dim3(1), dim3(256), 0, st, partial, (int)grid,
+                       tensor_scale);
   else
-    hipLaunchKernelGGL(global_scale_final<0>, dim3(1), dim3(1), 0, st, slot);
-  return hipGetLastError();
+    hipLaunchKernelGGL(global_amax_reduce<0>, dim3(1), dim3(256), 0, st, partial, (int)grid,
+                       tensor_scale);
+  a.global_scale = tensor_scale;
+  a.token_scales = nullptr;
+  return nvfp4_quantize_launch(a, st);
 }
 
 hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t st) {

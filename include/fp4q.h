@@ -142,9 +142,13 @@ FP4Q_API fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block
  *
  *   x, codes, block_scales, dequant, four_over_six: as for nvfp4_quantize
  *                 (no ragged rows).
- *   tensor_scale  float [1], 4-byte aligned, device memory: receives s; it
- *                 holds the amax's bit pattern while the call runs, so it
- *                 must not be read or shared by a concurrent call.
+ *   tensor_scale  float [1], 4-byte aligned, device memory: receives s
+ *                 before the blocks are quantized, which read it back.
+ *   codes         also serves, before the blocks are quantized, as scratch
+ *                 for the per-workgroup maxima of the tensor max (4 bytes
+ *                 per workgroup, at most 512 workgroups and never more than
+ *                 the codes hold).
+ * Concurrent calls must not share tensor_scale or codes.
  */
 FP4Q_API fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
                                   int four_over_six, uint8_t* codes, uint8_t* block_scales,
