@@ -326,14 +326,34 @@ __device__ __forceinline__ uint32_t expand_2of4(uint32_t rc, uint32_t meta) {
 
 // X_hat = DQ(Q(X)) (+ the residual): one lane per 8-element unit; every
 // dequantized value is +-g 2^k, exact through the scaled decode, and the
-// two terms are added once in FP32.
+// two terms are added once in FP32.  A wavefront's 64 units are 2 KiB of
+// output: with FP4Q_MX_REC_STAGE each lane puts its 32 bytes in the wave's
+// LDS area and the wave writes them back as two 1 KiB contiguous store
+// instructions (waves at a ragged end store lane by lane).
+#ifndef FP4Q_MX_REC_STAGE
+#define FP4Q_MX_REC_STAGE 1
+#endif
+#ifndef FP4Q_MX_REC_NT
+#define FP4Q_MX_REC_NT 1
+#endif
+__device__ __forceinline__ void store_rec(uint4* p, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  if (FP4Q_MX_REC_NT)
+    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, (u32x4*)p);
+  else
+    *p = v;
+}
 template <int RES>
 __global__ __launch_bounds__(256) void mxfp4_reconstruct_units(
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const void* __restrict__ res_codes, const uint8_t* __restrict__ res_meta,
     const uint8_t* __restrict__ res_scales, int64_t u0, int64_t u_end,
     uint4* __restrict__ out) {
+  __shared__ uint4 stage_lds[FP4Q_MX_REC_STAGE ? 512 : 1];
   const int64_t u = u0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t uw = u - lane;  // the wave's first unit (uniform)
+  const bool staged = FP4Q_MX_REC_STAGE && uw + 64 <= u_end;
   if (u >= u_end) return;
   const uint32_t cw = codes[u];
   const float up = __uint_as_float((uint32_t)scales[u >> 2] << 23);  // E8M0 as a scale operand
@@ -350,8 +370,19 @@ __global__ __launch_bounds__(256) void mxfp4_reconstruct_units(
     o[2 * p] = __float_as_uint(v.x);
     o[2 * p + 1] = __float_as_uint(v.y);
   });
-  out[2 * u] = make_uint4(o[0], o[1], o[2], o[3]);
-  out[2 * u + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+  if (staged) {
+    uint4* st = stage_lds + 128 * (threadIdx.x >> 6);
+    st[2 * lane] = make_uint4(o[0], o[1], o[2], o[3]);
+    st[2 * lane + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    store_rec(&out[2 * uw + lane], st[lane]);
+    store_rec(&out[2 * uw + 64 + lane], st[64 + lane]);
+  } else {
+    store_rec(&out[2 * u], make_uint4(o[0], o[1], o[2], o[3]));
+    store_rec(&out[2 * u + 1], make_uint4(o[4], o[5], o[6], o[7]));
+  }
 }
 
 }  // namespace

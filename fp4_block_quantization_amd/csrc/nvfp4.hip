@@ -44,6 +44,13 @@ namespace {
 #ifndef FP4Q_NV_NT_STORES
 #define FP4Q_NV_NT_STORES 1
 #endif
+// Build-time knob: FP4Q_NV_NT_BYTES selects which block-scale stores (one
+// byte per lane, 64 bytes per instruction) are non-temporal: 0 none, 1 all,
+// 2 those of calls without dequant (measured: plain bytes help beside the
+// dequant stream, non-temporal ones help without it).
+#ifndef FP4Q_NV_NT_BYTES
+#define FP4Q_NV_NT_BYTES 2
+#endif
 
 // Build-time knob: FP4Q_NV_NT_LOADS = 1 makes the contiguous input copies
 // into LDS (FP4Q_NV_LDS_LOAD) non-temporal: the input is read once, and each
@@ -119,6 +126,15 @@ __device__ __forceinline__ void store_out(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void store_out(uint8_t* p, uint8_t v) {
   if (FP4Q_NV_NT_STORES)
     __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+// A block scale byte: non-temporal per FP4Q_NV_NT_BYTES (DQ: the call also
+// writes the dequant).
+template <bool DQ>
+__device__ __forceinline__ void store_scale(uint8_t* p, uint8_t v) {
+  if (FP4Q_NV_NT_BYTES == 1 || (FP4Q_NV_NT_BYTES == 2 && !DQ))
+    store_out(p, v);
   else
     *p = v;
 }
@@ -497,7 +513,7 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
     *scale_stage = (uint8_t)o.ebyte;
   } else {
     store_out(&codes[blk], make_uint2(o.code0, o.code1));
-    store_out(&scales[blk], (uint8_t)o.ebyte);
+    store_scale<DQ>(&scales[blk], (uint8_t)o.ebyte);
   }
   if (DQ) {
     if (stage != nullptr) {  // the caller writes the chunk out contiguously

@@ -365,6 +365,21 @@ def test_global_scale_moe_act_full_size():
     check_global(workloads.rows("moe_act"), 1, "global moe_act")
 
 
+@pytest.mark.parametrize("where", ["first", "last", "tail"])
+def test_global_scale_max_anywhere(where):
+    """The tensor max is found wherever it sits: the first element, the last
+    one, or inside the part of the tensor past the last whole stride of the
+    max pass (2000 x 7168 is 1,792,000 16-byte units; a 512 x 256 grid strides
+    131,072 units, four at a time)."""
+    rng = np.random.default_rng(11)
+    R, H = 2000, 7168
+    x = rng.standard_normal((R, H)).astype(np.float32)
+    pos = {"first": (0, 0), "last": (R - 1, H - 1), "tail": (R - 37, 1000)}[where]
+    x[pos] = -1000.0
+    x_bits = f32_to_bf16_bits(x)
+    check_global(x_bits, 1, "global max at %s" % where)
+
+
 def test_global_scale_batch_dependency_on_gpu():
     # per-token results of a row do not depend on its batch; global ones do
     x = workloads.rows("moe_act", 0, 64)
