@@ -31,6 +31,17 @@ __device__ __forceinline__ uint32_t cvt_e2m1x2(uint32_t acc, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, SEL);
 }
 
+// The E2M1 codes of the grid points at or below a and b (a, b >= 0;
+// saturating at code 7) in bits 0-7 (a in the low nibble): the
+// stochastic-rounding conversion with a zero seed adds nothing before
+// truncating, so it rounds toward zero (checked over every binary32 value in
+// [0, 8], saturation windows and +inf by the conversion probes).  Only the
+// selected byte of that instruction's result is defined -- the others do
+// not keep the accumulator operand's bytes -- so the rest are cleared.
+__device__ __forceinline__ uint32_t cvt_e2m1x2_floor(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (float2v){a, b}, 0u, 1.0f, 0) & 0xFFu;
+}
+
 // Signed values of the two nibbles of byte SEL of src (low nibble in .x).
 template <int SEL>
 __device__ __forceinline__ float2v e2m1x2_values(uint32_t src) {

@@ -802,10 +802,15 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
 // so every load and store instruction is contiguous across the wave and the
 // token scale is one uniform load.
 #ifndef FP4Q_DQ_UNITS
-#define FP4Q_DQ_UNITS 4
+#define FP4Q_DQ_UNITS 2
 #endif
 #ifndef FP4Q_DQ_NT_STORES
 #define FP4Q_DQ_NT_STORES 1
+#endif
+// Build-time knob: FP4Q_DQ_NT_LOADS reads the codes (bit 0) and the block
+// scales (bit 1) of the dequantizer with non-temporal loads.
+#ifndef FP4Q_DQ_NT_LOADS
+#define FP4Q_DQ_NT_LOADS 0
 #endif
 // Build-time knob: FP4Q_GUIDED_NT_LOADS = 1 reads the input (bit 0) and the
 // guide codes (bit 1) of the guided quantizer with non-temporal loads.
@@ -834,8 +839,8 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
 #pragma unroll
   for (int n = 0; n < NU; ++n) {
     const int j = min(lane + 64 * n, nv - 1);  // in bounds for every lane
-    cw[n] = cw_in[j];
-    eb[n] = sc_in[j >> 1];
+    cw[n] = (FP4Q_DQ_NT_LOADS & 1) ? __builtin_nontemporal_load(&cw_in[j]) : cw_in[j];
+    eb[n] = (FP4Q_DQ_NT_LOADS & 2) ? __builtin_nontemporal_load(&sc_in[j >> 1]) : sc_in[j >> 1];
   }
 #pragma unroll
   for (int n = 0; n < NU; ++n) {
@@ -903,32 +908,37 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
     // [lo, hi].
     uint32_t out = 0u;
     if (__builtin_expect(r < __builtin_inff(), 1)) {
-      // v is finite: the hardware rounding to nearest gives q, its value g,
-      // and the neighbours q - [g > v] and q + [g < v] (not above 7)
+      // r finite (v may still overflow to +inf, whose lower neighbour is
+      // code 7): the lower neighbours of all eight elements from the
+      // truncating conversion, the upper ones one code up where v is off the
+      // grid (not above 7), and the clamp on whole code words, nibble by
+      // nibble: every nibble difference below stays in its nibble because
+      // the minuend nibbles are 8 + (0..7) and the subtrahends 0..7.
       float v[8];
-      uint32_t qw = 0u;
+      uint32_t lw = 0u;
       static_for<0, 4>([&](auto P) {
         constexpr int p = decltype(P)::value;
         v[2 * p] = fabsf(bf16_lo(w[p])) * r;
         v[2 * p + 1] = fabsf(bf16_hi(w[p])) * r;
-        qw = cvt_e2m1x2<p>(qw, v[2 * p], v[2 * p + 1]);
+        lw |= cvt_e2m1x2_floor(v[2 * p], v[2 * p + 1]) << (8 * p);
       });
+      uint32_t up = 0u, sx = 0u;
       static_for<0, 4>([&](auto P) {
         constexpr int p = decltype(P)::value;
-        const float2v g = e2m1x2_values<p>(qw);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int i = 2 * p + h;
-          const uint32_t q = (qw >> (4 * i)) & 7u;
-          const float gi = h ? g.y : g.x;
-          const uint32_t lo = q - (gi > v[i] ? 1u : 0u);
-          const uint32_t hi = q + ((gi < v[i] && q < 7u) ? 1u : 0u);
-          const uint32_t gn = (gwd >> (4 * i)) & 15u;
-          const uint32_t sx = (w[p] >> (h ? 31 : 15)) & 1u;
-          const uint32_t m = (gn >> 3) == sx ? (gn & 7u) : 0u;
-          out |= ((sx << 3) | min(max(m, lo), hi)) << (4 * i);
-        }
+        const float2v g = e2m1x2_values<p>(lw);
+        up |= ((g.x != v[2 * p]) ? 0x01u : 0u) << (8 * p);
+        up |= ((g.y != v[2 * p + 1]) ? 0x10u : 0u) << (8 * p);
+        sx |= (((w[p] >> 12) & 0x08u) | ((w[p] >> 24) & 0x80u)) << (8 * p);  // x's signs
       });
+      up &= ~(lw & (lw >> 1) & (lw >> 2));  // no step up from code 7
+      const uint32_t hw = lw + up;
+      // the guide's magnitude where its sign is x's, else 0
+      const uint32_t agree = ~(gwd ^ sx) & 0x88888888u;
+      const uint32_t m = gwd & (agree - (agree >> 3));
+      const uint32_t ge = ((((m | 0x88888888u) - lw) >> 3) & 0x11111111u) * 15u;  // m >= lo
+      const uint32_t mx = (m & ge) | (lw & ~ge);
+      const uint32_t le = ((((hw | 0x88888888u) - mx) >> 3) & 0x11111111u) * 15u;  // mx <= hi
+      out = ((mx & le) | (hw & ~le)) | sx;
     } else {
       // r = +inf (a subnormal decode step): v may be +inf or NaN, which the
       // threshold counts follow as the definition does

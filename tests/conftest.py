@@ -39,6 +39,8 @@ def pins():
     u64p = ctypes.POINTER(ctypes.c_uint64)
     L.cmp_fp4.argtypes = [ctypes.c_void_p, u32, u32, ctypes.c_uint64, ctypes.c_void_p, u64p]
     L.cmp_fp4.restype = ctypes.c_int64
+    L.cmp_fp4_floor.argtypes = [u32, ctypes.c_uint64, ctypes.c_void_p, u64p]
+    L.cmp_fp4_floor.restype = ctypes.c_int64
     for name in ("cmp_bf16", "cmp_fp8"):
         fn = getattr(L, name)
         fn.argtypes = [ctypes.c_void_p, u32, ctypes.c_uint64, ctypes.c_void_p, u64p]

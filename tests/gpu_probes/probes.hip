@@ -117,13 +117,24 @@ __global__ void k_hw_fp4_decode_scaled(uint32_t sbits, float* out) {
   out[2 * b + 1] = d.y;
 }
 
+// out[i] = FP4 byte of patterns lo+2i (low nibble) and lo+2i+1 from the
+// stochastic-rounding conversion with seed 0 and scale 1.0 (the guided
+// quantizer's lower neighbour)
+__global__ void k_hw_fp4_sr0(uint32_t lo, uint64_t n, uint8_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float a = pat(lo, 2 * i, 0u), b = pat(lo, 2 * i + 1, 0u);
+  out[i] = (uint8_t)fp4q::cvt_e2m1x2_floor(a, b);
+}
+
 dim3 grid_for(uint64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 
 }  // namespace
 
 extern "C" {
 
-// which: 0 hw fp4, 1 sw fp4, 2 hw bf16, 3 sw bf16, 4 hw fp8, 5 sw fp8
+// which: 0 hw fp4, 1 sw fp4, 2 hw bf16, 3 sw bf16, 4 hw fp8, 5 sw fp8,
+// 6 hw fp4 lower neighbour (flip ignored)
 int probe_launch(int which, uint32_t lo, uint32_t flip, uint64_t n, void* out, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (n == 0 || n > (1ull << 31)) return 2;
@@ -134,6 +145,7 @@ int probe_launch(int which, uint32_t lo, uint32_t flip, uint64_t n, void* out, v
     case 3: hipLaunchKernelGGL(k_sw_bf16, grid_for(n), dim3(256), 0, st, lo, n, (uint32_t*)out); break;
     case 4: hipLaunchKernelGGL(k_hw_fp8, grid_for(n), dim3(256), 0, st, lo, n, (uint16_t*)out); break;
     case 5: hipLaunchKernelGGL(k_sw_fp8, grid_for(n), dim3(256), 0, st, lo, n, (uint16_t*)out); break;
+    case 6: hipLaunchKernelGGL(k_hw_fp4_sr0, grid_for(n), dim3(256), 0, st, lo, n, (uint8_t*)out); break;
     default: return 2;
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;

@@ -206,6 +206,37 @@ int64_t cmp_fp4(e2m1_code_fn f, uint32_t lo, uint32_t flip, uint64_t n,
   return bad;
 }
 
+/* E2M1 code of the largest grid point at or below a >= 0 (7 above 6): the
+ * number of nonzero grid points 0.5, 1, 1.5, 2, 3, 4, 6 that are <= a. */
+static int e2m1_floor_code(float a) {
+  static const float g[7] = {0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  int q = 0;
+  for (int k = 0; k < 7; ++k) q += a >= g[k];
+  return q;
+}
+
+/* got[i]: two floor codes, of patterns lo + 2i (low nibble) and lo + 2i + 1
+ * (non-negative patterns; NaN patterns skipped). */
+int64_t cmp_fp4_floor(uint32_t lo, uint64_t n, const uint8_t* got, uint64_t* first) {
+  int64_t bad = 0;
+  uint64_t first_bad = UINT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t i = 0; i < (int64_t)n; ++i) {
+    int ok = 1;
+    for (int h = 0; h < 2; ++h) {
+      uint32_t u = (uint32_t)(lo + 2 * (uint64_t)i + h);
+      if (is_nan_bits(u)) continue;
+      if (((got[i] >> (4 * h)) & 15) != e2m1_floor_code(from_bits(u))) ok = 0;
+    }
+    if (!ok) {
+      ++bad;
+      if ((uint64_t)i < first_bad) first_bad = (uint64_t)i;
+    }
+  }
+  *first = first_bad;
+  return bad;
+}
+
 int64_t cmp_bf16(bf16_fn f, uint32_t lo, uint64_t n, const uint32_t* got,
                  uint64_t* first) {
   int64_t bad = 0;

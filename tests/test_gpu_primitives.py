@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROBES = os.path.join(ROOT, "tests", "_build", "libprobes.so")
 CHUNK = 1 << 26  # result pairs per launch
 
-HW_FP4, SW_FP4, HW_BF16, SW_BF16, HW_FP8, SW_FP8 = range(6)
+HW_FP4, SW_FP4, HW_BF16, SW_BF16, HW_FP8, SW_FP8, HW_FP4_FLOOR = range(7)
 
 
 def bits(f):
@@ -89,6 +89,28 @@ def test_e2m1_hw_conversion_saturation(probes, pins, olib):
     # +-inf saturate (the kernels feed +-inf only through the portable path)
     got = run(probes, HW_FP4, 0x7F7FFFFF, 0, 1, torch.uint8)[0]
     assert got == 0x77
+
+
+def floor_sweep(probes, pins, lo, hi):
+    start = lo
+    while start <= hi:
+        n = min(CHUNK, (hi - start + 1) // 2)
+        got = np.ascontiguousarray(run(probes, HW_FP4_FLOOR, start, 0, n, torch.uint8))
+        first = ctypes.c_uint64(0)
+        bad = pins.cmp_fp4_floor(start, n, got.ctypes.data, ctypes.byref(first))
+        assert bad == 0, "floor: %d mismatches, first pair at pattern %#x" % (
+            bad, start + 2 * first.value)
+        start += 2 * n
+
+
+def test_e2m1_lower_neighbour_exhaustive(probes, pins):
+    # the zero-seed stochastic-rounding conversion is the E2M1 floor: every
+    # FP32 value in [0, 8], then strided windows up to +inf (code 7)
+    floor_sweep(probes, pins, 0, bits(8.0) + 1)
+    for lo in range(bits(8.0) + 2, 0x7F800000, 0x00800000):
+        floor_sweep(probes, pins, lo, lo + (1 << 16) - 1)
+    floor_sweep(probes, pins, 0x7F7FFFFE, 0x7F7FFFFF)
+    floor_sweep(probes, pins, 0x7F7FFFFF, 0x7F800000)  # the largest finite and +inf
 
 
 def test_bf16_hw_conversion_exhaustive(probes, pins, olib):
