@@ -318,8 +318,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
                  8192 * 7168 // 2),
             "nvfp4_quantize_split<fp16-decision,dq> moe_act 8192x7168":
                 (8192 * 7168 * 2, nvfp4_bytes(8192, 7168) - 8192 * 7168 * 2),
-            "nvfp4_quantize_global (amax pass) moe_act 8192x7168": (8192 * 7168 * 2, 4 * 1024),
-            "nvfp4_quantize_global (partials reduce) moe_act 8192x7168": (4 * 1024, 4),
+            "nvfp4_quantize_global (amax pass) moe_act 8192x7168": (8192 * 7168 * 2, 4 * 512),
+            "nvfp4_quantize_global (partials reduce) moe_act 8192x7168": (4 * 512, 4),
             "nvfp4_quantize_global (quantize pass) moe_act 8192x7168":
                 (8192 * 7168 * 2 + 4, nvfp4_bytes(8192, 7168) - 8192 * 7168 * 2 - 8192 * 4),
             copy_key: (copy_bytes, copy_bytes)}
