@@ -72,12 +72,6 @@ namespace {
 #ifndef FP4Q_NV_WG_WAVES
 #define FP4Q_NV_WG_WAVES 4
 #endif
-// Build-time knob: FP4Q_NV_GRID_PER_CU > 0 launches at most that many
-// workgroups per compute unit, each looping over row groups; 0 launches one
-// workgroup per row group.
-#ifndef FP4Q_NV_GRID_PER_CU
-#define FP4Q_NV_GRID_PER_CU 0
-#endif
 // Build-time knob: FP4Q_NV_LDS_LOAD = 1 copies each wave's input chunk
 // into LDS with 16-byte-per-lane contiguous loads (global_load_lds) and
 // reads the lane's blocks from there.
@@ -88,11 +82,6 @@ namespace {
 // by wave barriers when each row has a single wave.
 #ifndef FP4Q_NV_WAVE_SYNC
 #define FP4Q_NV_WAVE_SYNC 1
-#endif
-// Build-time knob: FP4Q_NV_LDS_CODES = 1 also stages the codes and block
-// scales of each 64-block group in LDS and writes them as 16-byte pieces.
-#ifndef FP4Q_NV_LDS_CODES
-#define FP4Q_NV_LDS_CODES 0
 #endif
 // Build-time knob: blocks per lane in the split kernel (1 or 2).
 #ifndef FP4Q_NV_NB
@@ -496,9 +485,7 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
                                                int64_t blk, uint2* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
                                                uint4* __restrict__ dq,
-                                               uint4* stage = nullptr,
-                                               uint2* code_stage = nullptr,
-                                               uint8_t* scale_stage = nullptr) {
+                                               uint4* stage = nullptr) {
   if (__builtin_expect(!rs.fast, 0)) {
     tiny_row_block<FOS, DQ>((const uint16_t*)(xin + 2 * blk), __uint_as_float(bbits), tab, rs.s,
                             rs.inv_s,
@@ -508,13 +495,8 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
   }
   BlockOut o;
   quantize_block_fast<FOS, DQ>(x, bbits, rs, tab, neg_zero, o);
-  if (code_stage != nullptr) {  // the caller writes codes and scales out contiguously
-    *code_stage = make_uint2(o.code0, o.code1);
-    *scale_stage = (uint8_t)o.ebyte;
-  } else {
-    store_out(&codes[blk], make_uint2(o.code0, o.code1));
-    store_scale<DQ>(&scales[blk], (uint8_t)o.ebyte);
-  }
+  store_out(&codes[blk], make_uint2(o.code0, o.code1));
+  store_scale<DQ>(&scales[blk], (uint8_t)o.ebyte);
   if (DQ) {
     if (stage != nullptr) {  // the caller writes the chunk out contiguously
       stage[0] = make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]);
@@ -636,7 +618,7 @@ __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, cons
 template <int FOS, bool DQ, int NB>
 __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk, int W,
-    int R, int64_t ngrp, const int64_t* __restrict__ offs, int64_t ngroups,
+    int R, const int64_t* __restrict__ offs, int64_t ngroups,
     uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
     float neg_zero, const float* __restrict__ gscale) {
@@ -647,116 +629,73 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // for each group of 64 blocks)
   extern __shared__ uint4 dyn_lds[];
   float(*recip)[128] = (float(*)[128])dyn_lds;
-  constexpr bool kLdsLoad = FP4Q_NV_LDS_LOAD && FP4Q_NV_GRID_PER_CU == 0;
+  constexpr bool kLdsLoad = FP4Q_NV_LDS_LOAD;
   // per wave: the input tile (NB x 2 KiB) when loading through LDS, whose
   // half n, once read, stages the dequant values of block group n; else
   // 2 KiB of staging
-  constexpr int kWaveLds = (kLdsLoad ? 128 * NB : 128) + (FP4Q_NV_LDS_CODES ? 36 : 0);
+  constexpr int kWaveLds = kLdsLoad ? 128 * NB : 128;
   uint4* wave_lds = dyn_lds + 32 * R + kWaveLds * (threadIdx.x >> 6);
-  // codes (32 x 16 B) and scales (4 x 16 B) of a 64-block group, after the
-  // dequant staging
-  uint2* code_stage = reinterpret_cast<uint2*>(wave_lds + (kLdsLoad ? 128 * NB : 128));
-  uint8_t* scale_stage = reinterpret_cast<uint8_t*>(wave_lds + (kLdsLoad ? 128 * NB : 128) + 32);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
 
-  // Row groups g = blockIdx.x, + gridDim.x, ...: the next group's chunk is
-  // loaded while this one is processed.
-  int64_t g = blockIdx.x;
-  ChunkRef c = chunk_ref<NB>(g, rw, chunk, R, nblk, row0, row_end, rows, offs, ngroups);
+  const ChunkRef c =
+      chunk_ref<NB>(blockIdx.x, rw, chunk, R, nblk, row0, row_end, rows, offs, ngroups);
   uint32_t w[NB][8];
   if (kLdsLoad)
     load_chunk_lds<NB>(x, c, lane, wave_lds, w);
   else
     load_chunk<NB>(x, c, lane, w);
-  constexpr bool kPersist = FP4Q_NV_GRID_PER_CU > 0;
-  for (;;) {  // gridDim.x <= ngrp: every workgroup has a first group
-    uint32_t bmax[NB];
-    uint32_t lmax = 0;
+  uint32_t bmax[NB];
+  uint32_t lmax = 0;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      bmax[n] = lane + 64 * n < c.valid ? block_absmax_bits(w[n]) : 0u;
-      lmax = max(lmax, bmax[n]);
-    }
-    ChunkRef cn;
-    uint32_t wn[NB][8];
-    if (kPersist) {
-      cn = chunk_ref<NB>(g + gridDim.x, rw, chunk, R, nblk, row0, row_end, rows, offs,
-                         ngroups);
-      load_chunk<NB>(x, cn, lane, wn);
-    }
+  for (int n = 0; n < NB; ++n) {
+    bmax[n] = lane + 64 * n < c.valid ? block_absmax_bits(w[n]) : 0u;
+    lmax = max(lmax, bmax[n]);
+  }
 
-    const uint32_t m = wave_max_u32(lmax);
-    if (lane == 0) wave_max[wave] = m;
-    wg_sync(W);
-    if (chunk < 2) {
-      uint32_t amax_bits = 0;
-      for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
-      // with gscale, one token scale for the whole tensor
-      const RowScale rs =
-          gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
-      if (chunk == 0 && lane == 0) {
-        rowinfo[rw] = rs;
-        if (c.active && tscale != nullptr) tscale[c.row] = rs.s;
-      }
-      fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
+  const uint32_t m = wave_max_u32(lmax);
+  if (lane == 0) wave_max[wave] = m;
+  wg_sync(W);
+  if (chunk < 2) {
+    uint32_t amax_bits = 0;
+    for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+    // with gscale, one token scale for the whole tensor
+    const RowScale rs =
+        gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
+    if (chunk == 0 && lane == 0) {
+      rowinfo[rw] = rs;
+      if (c.active && tscale != nullptr) tscale[c.row] = rs.s;
     }
-    wg_sync(W);
-    const RowScale rs = rowinfo[rw];
-    constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ;
-    const bool stage = kStage && rs.fast;  // wave-uniform
-    // codes and scales leave as 16-byte pieces when the group starts on a
-    // 16-byte boundary of both outputs (wave-uniform)
-    const bool cstage = FP4Q_NV_LDS_CODES && rs.fast && (c.cbase & 15) == 0 &&
-                        ((uintptr_t)scales & 15) == 0 && ((uintptr_t)codes & 15) == 0;
+    fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
+  }
+  wg_sync(W);
+  const RowScale rs = rowinfo[rw];
+  constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ;
+  const bool stage = kStage && rs.fast;  // wave-uniform
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int j = lane + 64 * n;
-      uint4* dq_stage_n = wave_lds + (kLdsLoad ? 128 * n : 0);
-      if (64 * n < c.valid && j < c.valid) {
-        float xv[16];
-        unpack16(w[n], xv);
-        quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, c.cbase + j, codes,
-                                scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr,
-                                cstage ? &code_stage[lane] : nullptr,
-                                cstage ? &scale_stage[lane] : nullptr);
-      }
-      if ((stage || cstage) && 64 * n < c.valid) {
-        const int nv = min(64, c.valid - 64 * n);  // blocks of this group
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (stage) {  // the 64 blocks' dequant values leave as two contiguous KiB
-          uint4* dqc = dq + 2 * (c.cbase + 64 * n);
-          if (lane < 2 * nv) store_out(&dqc[lane], dq_stage_n[lane]);
-          if (64 + lane < 2 * nv) store_out(&dqc[64 + lane], dq_stage_n[64 + lane]);
-        }
-        if (cstage) {
-          const uint4* cs = reinterpret_cast<const uint4*>(code_stage);
-          uint4* cg = reinterpret_cast<uint4*>(codes + c.cbase + 64 * n);
-          if (2 * lane + 1 < nv) store_out(&cg[lane], cs[lane]);
-          if ((nv & 1) && lane == (nv >> 1))  // an odd last block
-            store_out(&codes[c.cbase + 64 * n + nv - 1], code_stage[nv - 1]);
-          const uint4* ss = reinterpret_cast<const uint4*>(scale_stage);
-          uint4* sg = reinterpret_cast<uint4*>(scales + c.cbase + 64 * n);
-          if (16 * lane + 15 < nv) store_out(&sg[lane], ss[lane]);
-          if (lane >= (nv >> 4) * 16 && lane < nv && (nv & 15))  // a partial last piece
-            store_out(&scales[c.cbase + 64 * n + lane], scale_stage[lane]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
+  for (int n = 0; n < NB; ++n) {
+    const int j = lane + 64 * n;
+    uint4* dq_stage_n = wave_lds + (kLdsLoad ? 128 * n : 0);
+    if (64 * n < c.valid && j < c.valid) {
+      float xv[16];
+      unpack16(w[n], xv);
+      quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, c.cbase + j, codes,
+                              scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr);
     }
-    if (!kPersist) break;
-    g += gridDim.x;
-    if (g >= ngrp) break;
-    c = cn;
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w[n][k] = wn[n][k];
+    if (stage && 64 * n < c.valid) {
+      // the group's dequant values leave as two contiguous KiB
+      const int nv = min(64, c.valid - 64 * n);  // blocks of this group
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint4* dqc = dq + 2 * (c.cbase + 64 * n);
+      if (lane < 2 * nv) store_out(&dqc[lane], dq_stage_n[lane]);
+      if (64 + lane < 2 * nv) store_out(&dqc[64 + lane], dq_stage_n[64 + lane]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   }
 }
 
@@ -1057,28 +996,16 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   if (W <= kMaxWgWaves) {
     const int R = W >= FP4Q_NV_WG_WAVES ? 1 : FP4Q_NV_WG_WAVES / W;  // rows per workgroup
     const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * W * R) * R;  // rows per launch
-    const bool lds_load = FP4Q_NV_LDS_LOAD && FP4Q_NV_GRID_PER_CU == 0;
-    const size_t lds = (size_t)R * 128 * sizeof(float) +
-                       (size_t)W * R * ((lds_load || (FP4Q_NV_LDS_DQ && DQ) || FP4Q_NV_LDS_CODES)
-                                            ? (lds_load ? (size_t)NB * 128 : 128) +
-                                                  (FP4Q_NV_LDS_CODES ? 36 : 0)
-                                            : 0) * sizeof(uint4);
-    int cus = 0;
-    if (FP4Q_NV_GRID_PER_CU > 0) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 0;
-    }
+    // the rows' reciprocal tables, then per wave the input tile (NB x 2 KiB)
+    // or, without it, 2 KiB of dequant staging
+    const size_t wave_lds = FP4Q_NV_LDS_LOAD ? (size_t)NB * 128
+                            : (FP4Q_NV_LDS_DQ && DQ) ? 128 : 0;
+    const size_t lds = (size_t)R * 128 * sizeof(float) + (size_t)W * R * wave_lds * sizeof(uint4);
     for (int64_t row0 = 0; row0 < a.rows; row0 += max_rows) {
       const int64_t row_end = a.rows - row0 < max_rows ? a.rows : row0 + max_rows;
-      const int64_t ngrp = (row_end - row0 + R - 1) / R;
-      int64_t nwg = ngrp;
-      if (cus > 0 && (int64_t)cus * FP4Q_NV_GRID_PER_CU < ngrp)
-        nwg = (int64_t)cus * FP4Q_NV_GRID_PER_CU;
-      const dim3 grid((unsigned)nwg), block(64 * W * R);
+      const dim3 grid((unsigned)((row_end - row0 + R - 1) / R)), block(64 * W * R);
       hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB>), grid, block, lds, st, x, a.rows,
-                         row0, row_end, nblk, W, R, ngrp, a.offsets, a.num_groups, codes,
+                         row0, row_end, nblk, W, R, a.offsets, a.num_groups, codes,
                          a.block_scales, a.token_scales, dq, neg_zero, a.global_scale);
     }
   } else {
