@@ -9,8 +9,10 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
-from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_nvfp4, to_dev
+from gpuutil import (assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4,
+                     to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +31,10 @@ def lib():
     L.nvfp4_quantize.argtypes = [vp, i64, i64, vp, i64, ci, vp, vp, vp, vp, vp]
     L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
     L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.mxfp4_resq_dense_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    L.mxfp4_resq_reconstruct.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, vp, vp]
+    L.nvfp4_quantize_guided.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize_global.argtypes = [vp, i64, i64, ci, vp, vp, vp, vp, vp]
     return L
 
 
@@ -104,3 +110,62 @@ def test_mx_split_launch(lib, H):
     want = oracle_mx(x_bits)
     for g, w, n in zip(out, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
         assert_same(host(g), w, "mx split H=%d %s" % (H, n))
+
+
+def test_next_rows_split_launch(lib):
+    """The guided, global-scale, dense-residual and reconstruction calls
+    split into many launches too."""
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    # TRACE guided rounding under a rollout's scales, 300 x 2048
+    rows, H = 300, 2048
+    x_bits = workloads.rows("moe_act", 0, rows)[:, :H].copy()
+    roll = oracle_nvfp4(workloads.perturbed(x_bits, seed=5), True, dequant=False)
+    x = to_dev(x_bits)
+    g, bs, ts = (torch.from_numpy(a).cuda() for a in roll[:3])
+    codes = torch.empty((rows, H // 2), **u8)
+    dq = torch.empty_like(x)
+    assert lib.nvfp4_quantize_guided(ptr(x), rows, H, ptr(g), ptr(bs), ptr(ts), ptr(codes),
+                                     ptr(dq), stream()) == 0
+    torch.cuda.synchronize()
+    want = oracle.nvfp4_quantize_guided(x_bits, roll[0], roll[1], roll[2])
+    assert_same(host(codes), want[0], "split guided codes")
+    assert_same(bits_of(dq), want[1], "split guided dequant")
+    # one scale for the whole tensor, 67 x 7168
+    rows, H = 67, 7168
+    x_bits = workloads.rows("moe_act", 100, rows)
+    x = to_dev(x_bits)
+    codes = torch.empty((rows, H // 2), **u8)
+    scales = torch.empty((rows, H // 16), **u8)
+    tsc = torch.empty(1, dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(x)
+    assert lib.nvfp4_quantize_global(ptr(x), rows, H, 1, ptr(codes), ptr(scales), ptr(tsc),
+                                     ptr(dq), stream()) == 0
+    torch.cuda.synchronize()
+    want = oracle.nvfp4_quantize_global(x_bits, True)
+    assert_same(host(codes), want[0], "split global codes")
+    assert_same(host(scales), want[1], "split global scales")
+    assert_same(host(tsc)[None, :], want[2][None, :], "split global tensor scale")
+    assert_same(bits_of(dq), want[3], "split global dequant")
+    # Rollout-ResQ-Dense and the three reconstructions, 40 x 7168
+    rows, H = 40, 7168
+    x_bits = np.ascontiguousarray(workloads.rows("resq_act", 0, rows))
+    x = to_dev(x_bits)
+    dense = (torch.empty((rows, H // 2), **u8), torch.empty((rows, H // 32), **u8),
+             torch.empty((rows, H // 2), **u8), torch.empty((rows, H // 32), **u8))
+    assert lib.mxfp4_resq_dense_quantize(ptr(x), rows, H, *[ptr(t) for t in dense],
+                                         stream()) == 0
+    torch.cuda.synchronize()
+    wd = oracle_mx_dense(x_bits)
+    for gt, w, n in zip(dense, wd, ("codes", "scales", "res_codes", "res_scales")):
+        assert_same(host(gt), w, "split dense " + n)
+    ws = oracle_mx(x_bits)
+    sparse = [torch.from_numpy(a).cuda() for a in ws]
+    for mode, (rc, rm, rs) in ((0, (None, None, None)), (1, tuple(sparse[2:5])),
+                               (2, (dense[2], None, dense[3]))):
+        out = torch.empty((rows, H), dtype=torch.float32, device="cuda")
+        assert lib.mxfp4_resq_reconstruct(ptr(sparse[0]), ptr(sparse[1]), ptr(rc), ptr(rm),
+                                          ptr(rs), rows, H, mode, ptr(out), stream()) == 0
+        torch.cuda.synchronize()
+        wargs = {0: (None, None, None), 1: (ws[2], ws[3], ws[4]), 2: (wd[2], None, wd[3])}[mode]
+        wh = oracle.mxfp4_resq_reconstruct(ws[0], ws[1], *wargs, residual=mode)
+        assert_same(host(out), wh, "split reconstruct residual=%d" % mode)
