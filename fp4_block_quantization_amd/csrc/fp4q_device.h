@@ -62,9 +62,18 @@ __device__ __forceinline__ half2v e2m1x2_values_f16(uint32_t src) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, 1.0f, SEL);
 }
 
+// A register whose every bit the caller overwrites before reading it (a
+// code word filled byte by byte by the conversions below, or masked): the
+// empty asm defines it, so no zero is materialized first.
+__device__ __forceinline__ uint32_t any_word() {
+  uint32_t w;
+  asm volatile("" : "=v"(w));  // volatile: each call its own register
+  return w;
+}
+
 // E4M3FN bytes of a (byte 0) and b (byte 1), both in [0, 448].
 __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)any_word(), false) & 0xFFFFu;
 }
 
 template <int SEL>

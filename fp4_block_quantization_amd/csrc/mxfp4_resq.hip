@@ -153,7 +153,7 @@ __device__ __forceinline__ void resq_unit(const uint4 a, uint32_t& cw, uint32_t&
 
   // primary codes; x * 2^-k is exact (or far below the first code)
   float v[8];
-  cw = 0u;
+  cw = any_word();  // bytes 0-3 all written below
   static_for<0, 4>([&](auto P) {
     constexpr int p = decltype(P)::value;
     v[2 * p] = bf16_lo(w[p]);
@@ -172,7 +172,7 @@ __device__ __forceinline__ void resq_unit(const uint4 a, uint32_t& cw, uint32_t&
   });
   kr = mx_exponent(quad_max(__float_as_uint(rmax)));
   const float rdown = __uint_as_float((uint32_t)(127 - kr) << 23);
-  rw = 0u;
+  rw = any_word();
   static_for<0, 4>([&](auto P) {
     constexpr int p = decltype(P)::value;
     rw = cvt_e2m1x2<p>(rw, v[2 * p] * rdown, v[2 * p + 1] * rdown);

@@ -228,7 +228,7 @@ __device__ __forceinline__ void encode_candidate(const float (&x)[16], float r,
   static_for<0, 2>([&](auto H) {
     constexpr int h = decltype(H)::value;
     float v[8];
-    uint32_t word = 0u;
+    uint32_t word = any_word();  // bytes 0-3 all written below
     static_for<0, 4>([&](auto P) {
       constexpr int p = decltype(P)::value;
       v[2 * p] = x[8 * h + 2 * p] * r;
@@ -602,16 +602,13 @@ __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, cons
                                          FP4Q_NV_NT_LOADS ? 2 : 0);  // 2: non-temporal
     }
   __builtin_amdgcn_s_waitcnt(0);  // the copies have landed in LDS
+  // Slots past the chunk's end read whatever the tile holds; the caller
+  // uses only blocks below c.valid.
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
-    if (64 * n < c.valid) {
-      const uint4 a = tile[128 * n + 2 * lane], b = tile[128 * n + 2 * lane + 1];
-      w[n][0] = a.x; w[n][1] = a.y; w[n][2] = a.z; w[n][3] = a.w;
-      w[n][4] = b.x; w[n][5] = b.y; w[n][6] = b.z; w[n][7] = b.w;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w[n][k] = 0u;
-    }
+    const uint4 a = tile[128 * n + 2 * lane], b = tile[128 * n + 2 * lane + 1];
+    w[n][0] = a.x; w[n][1] = a.y; w[n][2] = a.z; w[n][3] = a.w;
+    w[n][4] = b.x; w[n][5] = b.y; w[n][6] = b.z; w[n][7] = b.w;
   }
 }
 
