@@ -70,7 +70,7 @@ namespace {
 // Build-time knob: wavefronts per workgroup the split kernel aims for
 // (whole rows per workgroup).
 #ifndef FP4Q_NV_WG_WAVES
-#define FP4Q_NV_WG_WAVES 4
+#define FP4Q_NV_WG_WAVES 2
 #endif
 // Build-time knob: FP4Q_NV_LDS_LOAD = 1 copies each wave's input chunk
 // into LDS with 16-byte-per-lane contiguous loads (global_load_lds) and
