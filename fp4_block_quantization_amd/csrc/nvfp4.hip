@@ -534,10 +534,9 @@ __device__ __forceinline__ void load_block(const uint4* __restrict__ x, int64_t 
 // Split rows: a workgroup holds R rows x W wavefronts; wave c of a row owns
 // chunk c of it -- 64 * NB consecutive blocks, lane l taking blocks l and
 // l + 64 (NB = 2) -- so each lane quantizes NB blocks per pass.  The row
-// amax is combined across the W waves through LDS; waves 0 and 1 of the row
-// derive the row constants and fill the reciprocal table, which the others
-// read back.  Row and chunk are wave-uniform, so all addressing is scalar
-// base + 32-bit lane offset.
+// amax is combined across the W waves through LDS; then every wave derives
+// the row constants and fills its own reciprocal table.  Row and chunk are
+// wave-uniform, so all addressing is scalar base + 32-bit lane offset.
 // Rows of group g this wave works on: row, the blocks of its chunk that
 // exist (0 for a row outside the range or past the end), their first index.
 struct ChunkRef {
@@ -624,10 +623,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
     float neg_zero, const float* __restrict__ gscale) {
   __shared__ uint32_t wave_max[kMaxWgWaves];
-  __shared__ RowScale rowinfo[kMaxWgWaves];
-  // dynamic LDS: the reciprocal table of each row (R x 128 floats), then,
-  // with staged dequant stores, 2 KiB per wave (64 blocks x 32 bytes, reused
-  // for each group of 64 blocks)
+  // dynamic LDS: the reciprocal table of each wave (W R x 128 floats), then
+  // the waves' tiles
   extern __shared__ uint4 dyn_lds[];
   float(*recip)[128] = (float(*)[128])dyn_lds;
   constexpr bool kLdsLoad = FP4Q_NV_LDS_LOAD;
@@ -635,7 +632,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // half n, once read, stages the dequant values of block group n; else
   // 2 KiB of staging
   constexpr int kWaveLds = kLdsLoad ? 128 * NB : 128;
-  uint4* wave_lds = dyn_lds + 32 * R + kWaveLds * (threadIdx.x >> 6);
+  uint4* wave_lds = dyn_lds + 32 * W * R + kWaveLds * (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
@@ -658,20 +655,19 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   const uint32_t m = wave_max_u32(lmax);
   if (lane == 0) wave_max[wave] = m;
   wg_sync(W);
-  if (chunk < 2) {
-    uint32_t amax_bits = 0;
-    for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
-    // with gscale, one token scale for the whole tensor
-    const RowScale rs =
-        gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
-    if (chunk == 0 && lane == 0) {
-      rowinfo[rw] = rs;
-      if (c.active && tscale != nullptr) tscale[c.row] = rs.s;
-    }
-    fill_recip(recip[rw], rs.s, chunk * 64 + lane, W >= 2 ? 128 : 64);
-  }
-  wg_sync(W);
-  const RowScale rs = rowinfo[rw];
+  // every wave derives the row constants and fills its own reciprocal
+  // table, so the row needs no second workgroup barrier
+  uint32_t amax_bits = 0;
+  for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+  // with gscale, one token scale for the whole tensor
+  const RowScale rs =
+      gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
+  if (chunk == 0 && lane == 0 && c.active && tscale != nullptr) tscale[c.row] = rs.s;
+  float* tab = recip[wave];
+  fill_recip(tab, rs.s, lane, 64);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   constexpr bool kStage = FP4Q_NV_LDS_DQ && DQ;
   const bool stage = kStage && rs.fast;  // wave-uniform
 #pragma unroll
@@ -681,8 +677,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     if (64 * n < c.valid && j < c.valid) {
       float xv[16];
       unpack16(w[n], xv);
-      quantize_block<FOS, DQ>(xv, bmax[n], rs, recip[rw], neg_zero, x, c.cbase + j, codes,
-                              scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr);
+      quantize_block<FOS, DQ>(xv, bmax[n], rs, tab, neg_zero, x, c.cbase + j, codes, scales,
+                              dq, stage ? &dq_stage_n[2 * lane] : nullptr);
     }
     if (stage && 64 * n < c.valid) {
       // the group's dequant values leave as two contiguous KiB
@@ -997,11 +993,11 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   if (W <= kMaxWgWaves) {
     const int R = W >= FP4Q_NV_WG_WAVES ? 1 : FP4Q_NV_WG_WAVES / W;  // rows per workgroup
     const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * W * R) * R;  // rows per launch
-    // the rows' reciprocal tables, then per wave the input tile (NB x 2 KiB)
-    // or, without it, 2 KiB of dequant staging
+    // per wave: its reciprocal table, then its input tile (NB x 2 KiB) or,
+    // without it, 2 KiB of dequant staging
     const size_t wave_lds = FP4Q_NV_LDS_LOAD ? (size_t)NB * 128
                             : (FP4Q_NV_LDS_DQ && DQ) ? 128 : 0;
-    const size_t lds = (size_t)R * 128 * sizeof(float) + (size_t)W * R * wave_lds * sizeof(uint4);
+    const size_t lds = (size_t)W * R * (128 * sizeof(float) + wave_lds * sizeof(uint4));
     for (int64_t row0 = 0; row0 < a.rows; row0 += max_rows) {
       const int64_t row_end = a.rows - row0 < max_rows ? a.rows : row0 + max_rows;
       const dim3 grid((unsigned)((row_end - row0 + R - 1) / R)), block(64 * W * R);
