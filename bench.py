@@ -123,7 +123,7 @@ def rotating_nvfp4_sets(x, n, dequant=True):
     return sets
 
 
-def cpu_baseline(x_bits, rows_sample, repeats=3):
+def cpu_baseline(x_bits, rows_sample, repeats=7):
     """The CPU oracle as it stands (single-threaded C), over a bounded
     sample of the headline workload's rows; median of `repeats`."""
     import oracle
