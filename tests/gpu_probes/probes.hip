@@ -93,22 +93,6 @@ __global__ void k_decode_tables(float* fp4_hw, float* fp4_sw, float* fp8_hw, flo
 // Scaled conversions (MX scales).  sbits is the FP32 pattern of the scale
 // operand.  bf16 variant: out[i] = codes of BF16 patterns 2i (low) and
 // 2i+1 (high), i < 32768.
-__global__ void k_hw_fp4_bf16_scaled(uint32_t sbits, uint64_t n, uint8_t* out) {
-  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const uint32_t pair = (uint32_t)(2 * i) | ((uint32_t)(2 * i + 1) << 16);
-  const bf16x2v v = __builtin_bit_cast(bf16x2v, pair);
-  out[i] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, v, __uint_as_float(sbits), 0);
-}
-
-__global__ void k_hw_fp4_f32_scaled(uint32_t lo, uint32_t flip, uint32_t sbits, uint64_t n,
-                                    uint8_t* out) {
-  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const float a = pat(lo, 2 * i, flip), b = pat(lo, 2 * i + 1, flip);
-  out[i] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, __uint_as_float(sbits), 0);
-}
-
 // out[2b], out[2b+1]: scaled decode of byte b (256 threads)
 __global__ void k_hw_fp4_decode_scaled(uint32_t sbits, float* out) {
   const uint32_t b = threadIdx.x;
@@ -151,26 +135,11 @@ int probe_launch(int which, uint32_t lo, uint32_t flip, uint64_t n, void* out, v
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
-// which: 0 bf16 scaled encode (n <= 32768), 1 f32 scaled encode,
-// 2 scaled decode (out: 512 floats)
-int probe_launch_scaled(int which, uint32_t lo, uint32_t flip, uint32_t sbits, uint64_t n,
-                        void* out, void* stream) {
-  hipStream_t st = (hipStream_t)stream;
-  switch (which) {
-    case 0:
-      if (n == 0 || n > 32768) return 2;
-      hipLaunchKernelGGL(k_hw_fp4_bf16_scaled, grid_for(n), dim3(256), 0, st, sbits, n, (uint8_t*)out);
-      break;
-    case 1:
-      if (n == 0 || n > (1ull << 31)) return 2;
-      hipLaunchKernelGGL(k_hw_fp4_f32_scaled, grid_for(n), dim3(256), 0, st, lo, flip, sbits, n,
-                         (uint8_t*)out);
-      break;
-    case 2:
-      hipLaunchKernelGGL(k_hw_fp4_decode_scaled, dim3(1), dim3(256), 0, st, sbits, (float*)out);
-      break;
-    default: return 2;
-  }
+// out[2b], out[2b+1]: the scaled decode of byte b (256 threads) under the
+// scale operand bit pattern sbits
+int probe_decode_scaled(uint32_t sbits, void* out, void* stream) {
+  hipLaunchKernelGGL(k_hw_fp4_decode_scaled, dim3(1), dim3(256), 0, (hipStream_t)stream, sbits,
+                     (float*)out);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

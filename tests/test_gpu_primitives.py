@@ -42,6 +42,8 @@ def probes():
     L.probe_launch.restype = ctypes.c_int
     L.probe_decode_tables.argtypes = [ctypes.c_void_p] * 5
     L.probe_decode_tables.restype = ctypes.c_int
+    L.probe_decode_scaled.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    L.probe_decode_scaled.restype = ctypes.c_int
     return L
 
 
@@ -174,3 +176,24 @@ def test_decode_tables(probes):
                 assert tab[b] != tab[b]
             else:
                 assert tab[b] == want8
+
+
+def test_e2m1_scaled_decode_every_scale(probes):
+    # The MXFP4 dequant: the scaled decode of every code byte under every
+    # E8M0 scale k + 127 a finite BF16 block can give (passed as the FP32
+    # pattern (k + 127) << 23; k = -127 is the all-zero pattern; the block max
+    # is below 2^128, so k = floor(log2 b) - 2 <= 125) is +-g 2^k exactly,
+    # FP32 subnormals and -0 included.
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    b = np.arange(256)
+    codes = np.stack([b & 15, b >> 4], 1).reshape(-1)  # out[2b]: low nibble
+    out = torch.empty(512, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for k in range(-127, 126):
+        assert probes.probe_decode_scaled((k + 127) << 23, ctypes.c_void_p(out.data_ptr()), st) == 0
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint32)
+        want = (np.where(codes & 8, -1.0, 1.0) * np.ldexp(grid[codes & 7], k)).astype(np.float32)
+        bad = np.nonzero(got != want.view(np.uint32))[0]
+        assert len(bad) == 0, "k=%d: byte %d nibble %d got %#x want %#x" % (
+            k, bad[0] // 2, bad[0] % 2, got[bad[0]], want.view(np.uint32)[bad[0]])
