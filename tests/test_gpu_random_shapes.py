@@ -125,3 +125,33 @@ def test_guided_random_shapes(case):
     label = "guided case %d: %d x %d" % (case, rows, hidden)
     assert_same(host(got[0]), want[0], label + " codes")
     assert_same(bits_of(got[1]), want[1], label + " dequant")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_nvfp4_full_size_random_tensors(case):
+    """Full-size 8192 x 7168 tensors of four distributions (normal,
+    Student-t(3), per-row log-normal gains, uniform on [-6, 6]) under a
+    random power-of-two gain: about 3.7 million blocks each, of which a few
+    thousand are near-ties between the two candidates."""
+    rng = np.random.default_rng(50000 + case)
+    R, H = 8192, 7168
+    kind = case % 4
+    if kind == 0:
+        x = rng.standard_normal((R, H)).astype(np.float32)
+    elif kind == 1:
+        x = rng.standard_t(3, (R, H)).astype(np.float32)
+    elif kind == 2:
+        x = (rng.standard_normal((R, H)) * np.exp(rng.standard_normal((R, 1)) * 2)).astype(
+            np.float32)
+    else:
+        x = rng.uniform(-6, 6, (R, H)).astype(np.float32)
+    x *= np.float32(2.0 ** rng.integers(-30, 30))
+    x_bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = fq.nvfp4_quantize(to_dev(x_bits), True)
+    torch.cuda.synchronize()
+    want = oracle_nvfp4(x_bits, True)
+    label = "full-size case %d" % case
+    assert_same(host(got[0]), want[0], label + " codes")
+    assert_same(host(got[1]), want[1], label + " scales")
+    assert_same(host(got[2])[:, None], want[2][:, None], label + " token scales")
+    assert_same(bits_of(got[3]), want[3], label + " dequant")
