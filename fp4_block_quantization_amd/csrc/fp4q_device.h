@@ -31,6 +31,18 @@ __device__ __forceinline__ uint32_t cvt_e2m1x2(uint32_t acc, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, SEL);
 }
 
+// Codes of a / 2^k (low nibble) and b / 2^k into byte SEL of acc, where
+// scale2k is the FP32 pattern (k + 127) << 23: the conversion divides by
+// the power of two whose E8M0 byte is the scale's exponent field before
+// rounding.  Pinned for every k in [-127, 125] over every input with at
+// most 10 significant bits below 2^(k+3) -- each element and each residual
+// of an MX block with shared exponent k.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_e2m1x2_scaled(uint32_t acc, float a, float b,
+                                                      float scale2k) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, scale2k, SEL);
+}
+
 // The E2M1 codes of the grid points at or below a and b (a, b >= 0;
 // saturating at code 7) in bits 0-7 (a in the low nibble): the
 // stochastic-rounding conversion with a zero seed adds nothing before

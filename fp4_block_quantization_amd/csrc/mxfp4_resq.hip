@@ -148,17 +148,16 @@ __device__ __forceinline__ void resq_unit(const uint4 a, uint32_t& cw, uint32_t&
       __builtin_elementwise_max(as_u16x2(w[2] & 0x7FFF7FFFu), as_u16x2(w[3] & 0x7FFF7FFFu)));
   const uint32_t mbits = quad_max((uint32_t)max(mw.x, mw.y) << 16);
   k = mx_exponent(mbits);  // [-127, 125]
-  const float down = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k
-  const float up = __uint_as_float((uint32_t)(127 + k) << 23);    // 2^k as a scale operand
+  const float up = __uint_as_float((uint32_t)(127 + k) << 23);  // 2^k as a scale operand
 
-  // primary codes; x * 2^-k is exact (or far below the first code)
+  // primary codes of x / 2^k, the division done inside the conversion
   float v[8];
   cw = any_word();  // bytes 0-3 all written below
   static_for<0, 4>([&](auto P) {
     constexpr int p = decltype(P)::value;
     v[2 * p] = bf16_lo(w[p]);
     v[2 * p + 1] = bf16_hi(w[p]);
-    cw = cvt_e2m1x2<p>(cw, v[2 * p] * down, v[2 * p + 1] * down);
+    cw = cvt_e2m1x2_scaled<p>(cw, v[2 * p], v[2 * p + 1], up);
   });
 
   // residual x - (+-g 2^k), exact in FP32
@@ -171,11 +170,11 @@ __device__ __forceinline__ void resq_unit(const uint4 a, uint32_t& cw, uint32_t&
     rmax = fmaxf(fmaxf(rmax, fabsf(v[2 * p])), fabsf(v[2 * p + 1]));
   });
   kr = mx_exponent(quad_max(__float_as_uint(rmax)));
-  const float rdown = __uint_as_float((uint32_t)(127 - kr) << 23);
+  const float rup = __uint_as_float((uint32_t)(127 + kr) << 23);
   rw = any_word();
   static_for<0, 4>([&](auto P) {
     constexpr int p = decltype(P)::value;
-    rw = cvt_e2m1x2<p>(rw, v[2 * p] * rdown, v[2 * p + 1] * rdown);
+    rw = cvt_e2m1x2_scaled<p>(rw, v[2 * p], v[2 * p + 1], rup);
   });
 }
 

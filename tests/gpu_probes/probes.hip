@@ -101,6 +101,18 @@ __global__ void k_hw_fp4_decode_scaled(uint32_t sbits, float* out) {
   out[2 * b + 1] = d.y;
 }
 
+// out[i] = FP4 byte of the patterns (2i) << 13 (low nibble) and
+// (2i + 1) << 13 -- every binary32 value whose low 13 bits are zero, so
+// every BF16 value and every value of at most 10 significant bits -- from
+// the encode with scale operand sbits
+__global__ void k_hw_fp4_encode_scaled(uint32_t sbits, uint64_t n, uint8_t* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float a = __uint_as_float((uint32_t)(2 * i) << 13);
+  const float b = __uint_as_float((uint32_t)(2 * i + 1) << 13);
+  out[i] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, __uint_as_float(sbits), 0);
+}
+
 // out[i] = FP4 byte of patterns lo+2i (low nibble) and lo+2i+1 from the
 // stochastic-rounding conversion with seed 0 and scale 1.0 (the guided
 // quantizer's lower neighbour)
@@ -140,6 +152,15 @@ int probe_launch(int which, uint32_t lo, uint32_t flip, uint64_t n, void* out, v
 int probe_decode_scaled(uint32_t sbits, void* out, void* stream) {
   hipLaunchKernelGGL(k_hw_fp4_decode_scaled, dim3(1), dim3(256), 0, (hipStream_t)stream, sbits,
                      (float*)out);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// out[i], i < n <= 2^18: the scaled encode of the patterns (2i) << 13 and
+// (2i + 1) << 13 under the scale operand bit pattern sbits
+int probe_encode_scaled(uint32_t sbits, uint64_t n, void* out, void* stream) {
+  if (n == 0 || n > (1ull << 18)) return 2;
+  hipLaunchKernelGGL(k_hw_fp4_encode_scaled, grid_for(n), dim3(256), 0, (hipStream_t)stream, sbits,
+                     n, (uint8_t*)out);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

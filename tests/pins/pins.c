@@ -206,6 +206,36 @@ int64_t cmp_fp4(e2m1_code_fn f, uint32_t lo, uint32_t flip, uint64_t n,
   return bad;
 }
 
+/* got[i]: two codes of the patterns (2i) << 13 (low nibble) and
+ * (2i + 1) << 13 from an encode that divides by 2^k; the oracle's code of
+ * |a| * 2^-k (the product rounded to binary32, as the oracle forms it) with
+ * the sign bit kept.  Only inputs the MX kernels can feed it are compared:
+ * finite |a| < 2^(k+3), the bound every element of a block whose shared
+ * exponent is k satisfies. */
+int64_t cmp_fp4_scaled(e2m1_code_fn f, int k, uint64_t n, const uint8_t* got, uint64_t* first) {
+  int64_t bad = 0;
+  uint64_t first_bad = UINT64_MAX;
+  const float down = ldexpf(1.0f, -k);
+  const double bound = ldexp(1.0, k + 3);
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t i = 0; i < (int64_t)n; ++i) {
+    int ok = 1;
+    for (int h = 0; h < 2; ++h) {
+      uint32_t u = (uint32_t)(2 * (uint64_t)i + h) << 13;
+      float a = from_bits(u);
+      if (!(fabs((double)a) < bound)) continue; /* also skips Inf and NaN */
+      int want = f(fabsf(a) * down) | ((u >> 31) << 3);
+      if (((got[i] >> (4 * h)) & 15) != want) ok = 0;
+    }
+    if (!ok) {
+      ++bad;
+      if ((uint64_t)i < first_bad) first_bad = (uint64_t)i;
+    }
+  }
+  *first = first_bad;
+  return bad;
+}
+
 /* E2M1 code of the largest grid point at or below a >= 0 (7 above 6): the
  * number of nonzero grid points 0.5, 1, 1.5, 2, 3, 4, 6 that are <= a. */
 static int e2m1_floor_code(float a) {

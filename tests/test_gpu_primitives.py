@@ -44,6 +44,9 @@ def probes():
     L.probe_decode_tables.restype = ctypes.c_int
     L.probe_decode_scaled.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
     L.probe_decode_scaled.restype = ctypes.c_int
+    L.probe_encode_scaled.argtypes = [ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    L.probe_encode_scaled.restype = ctypes.c_int
     return L
 
 
@@ -197,3 +200,26 @@ def test_e2m1_scaled_decode_every_scale(probes):
         bad = np.nonzero(got != want.view(np.uint32))[0]
         assert len(bad) == 0, "k=%d: byte %d nibble %d got %#x want %#x" % (
             k, bad[0] // 2, bad[0] % 2, got[bad[0]], want.view(np.uint32)[bad[0]])
+
+
+def test_e2m1_scaled_encode_every_scale(probes, pins, olib):
+    # The MXFP4 encode divides by the block's power of two inside the
+    # conversion: under the scale operand (k + 127) << 23 it must give the
+    # oracle's code of |a| * 2^-k for every k in -127..125 and every input a
+    # block with that exponent can hold (|a| < 2^(k+3)).  The inputs are
+    # every binary32 pattern with its low 13 bits zero: each BF16 element,
+    # and each residual x - g 2^k (a multiple of 2^(k-9) below 2^(k+1), so
+    # of at most 10 significant bits), subnormals and -0 included.
+    n = 1 << 18
+    out = torch.empty(n, dtype=torch.uint8, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    f = fnptr(olib, "oracle_e2m1_code")
+    for k in range(-127, 126):
+        assert probes.probe_encode_scaled((k + 127) << 23, n, ctypes.c_void_p(out.data_ptr()),
+                                          st) == 0
+        torch.cuda.synchronize()
+        got = np.ascontiguousarray(out.cpu().numpy())
+        first = ctypes.c_uint64(0)
+        bad = pins.cmp_fp4_scaled(f, k, n, got.ctypes.data, ctypes.byref(first))
+        assert bad == 0, "k=%d: %d mismatches, first pair at pattern %#x" % (
+            k, bad, (2 * first.value) << 13)

@@ -137,3 +137,33 @@ def test_product_table_exact_in_fp16_and_fp32():
             if exact:
                 m, _ = math.frexp(exact)
                 assert (m * 64).is_integer()  # at most 6 significant bits
+
+
+def test_scaled_encode_comparator_cpu(pins, olib):
+    # The comparator behind the GPU pin of the scaled MX encode: it must
+    # accept the codes of |a| * 2^-k computed here independently (nearest
+    # grid value in float64, ties to the even code), skip inputs outside
+    # |a| < 2^(k+3), and report a single planted wrong nibble at its index.
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    n = 1 << 18
+    u = (np.arange(2 * n, dtype=np.uint64) << 13).astype(np.uint32)
+    with np.errstate(invalid="ignore"):  # NaN patterns, skipped below
+        a = u.view(np.float32).astype(np.float64)
+    f = fnptr(olib, "oracle_e2m1_code")
+    for k in (-127, -3, 0, 125):
+        v = np.abs(a) * 2.0 ** -k
+        inside = np.isfinite(a) & (np.abs(a) < 2.0 ** (k + 3))
+        v = np.where(inside, v, 0.0)
+        d = np.abs(v[:, None] - grid[None, :])
+        q = np.argmin(d, axis=1)
+        up = np.minimum(q + 1, 7)
+        q = np.where((q % 2 == 1) & (d[np.arange(q.size), up] == d[np.arange(q.size), q]) & (q < 7),
+                     up, q)
+        nib = (q | ((u >> 31) << 3)).astype(np.uint8)
+        got = np.ascontiguousarray(nib[0::2] | (nib[1::2] << 4))
+        first = ctypes.c_uint64(0)
+        assert pins.cmp_fp4_scaled(f, k, n, got.ctypes.data, ctypes.byref(first)) == 0, k
+        i = int(np.nonzero(inside[0::2] & (q[0::2] > 0))[0][1000])
+        got[i] ^= 1
+        assert pins.cmp_fp4_scaled(f, k, n, got.ctypes.data, ctypes.byref(first)) == 1, k
+        assert first.value == i
