@@ -99,6 +99,16 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
+// fl(1/d), the IEEE quotient, for 2^-126 <= d <= 2^126: the hardware
+// reciprocal approximation y, the residual e = 1 - d*y in one FMA, and the
+// refined y + e*y in another.  Pinned against the CPU's IEEE division over
+// every binary32 value of that range.
+__device__ __forceinline__ float recip_normal(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  const float e = __builtin_fmaf(-d, y, 1.0f);
+  return __builtin_fmaf(e, y, y);
+}
+
 // ---- portable definitions -------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -229,11 +229,19 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
   return row_scale_s<FOS>(__uint_as_float(amax_bits) / (FOS ? 1536.0f : 2688.0f));
 }
 
-// tab[byte] = 1 / fl(e(byte) s) for the E4M3 bytes this lane covers.
-__device__ __forceinline__ void fill_recip(float* tab, float s, int first, int step) {
-  for (int byte = first; byte < 128; byte += step) {
+// tab[byte] = 1 / fl(e(byte) s) for all 128 E4M3 bytes, lane l of the
+// wavefront writing bytes l and l + 64.
+__device__ __forceinline__ void fill_recip(float* tab, float s, int lane) {
+  // For s in [2^-117, 2^116] every nonzero e*s (e from 2^-9 to 448) lies in
+  // [2^-126, 2^126], where the refined hardware reciprocal is the IEEE
+  // quotient; other rows divide.  s is uniform across the wavefront.
+  const bool normal = __builtin_amdgcn_readfirstlane((s >= 0x1p-117f && s <= 0x1p116f) ? 1 : 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int byte = lane + 64 * h;
     const float d = e4m3_value<0>((uint32_t)byte) * s;
-    tab[byte] = (d != 0.0f) ? 1.0f / d : 0.0f;
+    const float r = normal ? recip_normal(d) : 1.0f / d;
+    tab[byte] = (d != 0.0f) ? r : 0.0f;
   }
 }
 
@@ -610,15 +618,25 @@ template <int NB>
 __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, const ChunkRef& c,
                                                int lane, uint4* tile, uint32_t (&w)[NB][8]) {
   const uint4* xc = x + 2 * c.cbase;
+  constexpr int kAux = FP4Q_NV_NT_LOADS ? 2 : 0;  // 2: non-temporal
+  if (c.valid == 64 * NB) {
+    // a whole chunk: one base pair, the KiB steps in the instruction's
+    // offset, which moves the global and the LDS address alike
+    static_for<0, 2 * NB>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      __builtin_amdgcn_global_load_lds(xc + lane, (lds_void*)tile, 16, 1024 * i, kAux);
+    });
+  } else {
 #pragma unroll
-  for (int n = 0; n < NB; ++n)
+    for (int n = 0; n < NB; ++n)
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int q = 128 * n + 64 * k + lane;  // 16-byte unit of the chunk
-      if (64 * n < c.valid && (q >> 1) < c.valid)
-        __builtin_amdgcn_global_load_lds(xc + q, (lds_void*)(tile + 128 * n + 64 * k), 16, 0,
-                                         FP4Q_NV_NT_LOADS ? 2 : 0);  // 2: non-temporal
-    }
+      for (int k = 0; k < 2; ++k) {
+        const int q = 128 * n + 64 * k + lane;  // 16-byte unit of the chunk
+        if (64 * n < c.valid && (q >> 1) < c.valid)
+          __builtin_amdgcn_global_load_lds(xc + q, (lds_void*)(tile + 128 * n + 64 * k), 16, 0,
+                                           kAux);
+      }
+  }
   __builtin_amdgcn_s_waitcnt(0);  // the copies have landed in LDS
   // Slots past the chunk's end read whatever the tile holds; the caller
   // uses only blocks below c.valid.
@@ -679,7 +697,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
       gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
   if (chunk == 0 && lane == 0 && c.active && tscale != nullptr) tscale[c.row] = rs.s;
   float* tab = recip[wave];
-  fill_recip(tab, rs.s, lane, 64);
+  fill_recip(tab, rs.s, lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -735,7 +753,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
   const uint32_t row_amax = wave_max_u32(lmax);
   const RowScale rs = gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(row_amax);
   if (lane == 0 && tscale != nullptr) tscale[row] = rs.s;
-  fill_recip(recip[wave], rs.s, lane, 64);
+  fill_recip(recip[wave], rs.s, lane);
   __builtin_amdgcn_wave_barrier();
   for (int j = lane; j < nblk; j += 64) {
     uint32_t w[8];
@@ -853,7 +871,11 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
     const uint32_t gwd = (FP4Q_GUIDED_NT_LOADS & 2) ? __builtin_nontemporal_load(&gin[j]) : gin[j];
     const float e = e4m3_value<0>(sin[j >> 1]);
     const float d = e * s;
-    const float r = d != 0.0f ? 1.0f / d : 0.0f;  // fl(1 / fl(e s)), IEEE
+    float r;  // fl(1 / fl(e s)), the IEEE quotient
+    if (d >= 0x1p-126f && d <= 0x1p126f)
+      r = recip_normal(d);
+    else
+      r = d != 0.0f ? 1.0f / d : 0.0f;
     // With lo <= hi adjacent (or equal) codes, the guide rule is a clamp:
     // the guide's magnitude code when the signs agree (else 0), clamped to
     // [lo, hi].

@@ -44,6 +44,8 @@ def pins():
     L.cmp_fp4_scaled.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p,
                                  u64p]
     L.cmp_fp4_scaled.restype = ctypes.c_int64
+    L.cmp_recip.argtypes = [u32, ctypes.c_uint64, ctypes.c_void_p, u64p]
+    L.cmp_recip.restype = ctypes.c_int64
     for name in ("cmp_bf16", "cmp_fp8"):
         fn = getattr(L, name)
         fn.argtypes = [ctypes.c_void_p, u32, ctypes.c_uint64, ctypes.c_void_p, u64p]

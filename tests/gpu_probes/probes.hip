@@ -123,6 +123,13 @@ __global__ void k_hw_fp4_sr0(uint32_t lo, uint64_t n, uint8_t* out) {
   out[i] = (uint8_t)fp4q::cvt_e2m1x2_floor(a, b);
 }
 
+// out[i] = the refined hardware reciprocal of pattern lo + i
+__global__ void k_recip_normal(uint32_t lo, uint64_t n, float* out) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = fp4q::recip_normal(pat(lo, i, 0u));
+}
+
 dim3 grid_for(uint64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 
 }  // namespace
@@ -130,7 +137,8 @@ dim3 grid_for(uint64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 extern "C" {
 
 // which: 0 hw fp4, 1 sw fp4, 2 hw bf16, 3 sw bf16, 4 hw fp8, 5 sw fp8,
-// 6 hw fp4 lower neighbour (flip ignored)
+// 6 hw fp4 lower neighbour (flip ignored), 7 refined reciprocal (one float
+// per pattern, flip ignored)
 int probe_launch(int which, uint32_t lo, uint32_t flip, uint64_t n, void* out, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (n == 0 || n > (1ull << 31)) return 2;
@@ -142,6 +150,7 @@ int probe_launch(int which, uint32_t lo, uint32_t flip, uint64_t n, void* out, v
     case 4: hipLaunchKernelGGL(k_hw_fp8, grid_for(n), dim3(256), 0, st, lo, n, (uint16_t*)out); break;
     case 5: hipLaunchKernelGGL(k_sw_fp8, grid_for(n), dim3(256), 0, st, lo, n, (uint16_t*)out); break;
     case 6: hipLaunchKernelGGL(k_hw_fp4_sr0, grid_for(n), dim3(256), 0, st, lo, n, (uint8_t*)out); break;
+    case 7: hipLaunchKernelGGL(k_recip_normal, grid_for(n), dim3(256), 0, st, lo, n, (float*)out); break;
     default: return 2;
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;

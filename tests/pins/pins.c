@@ -267,6 +267,23 @@ int64_t cmp_fp4_floor(uint32_t lo, uint64_t n, const uint8_t* got, uint64_t* fir
   return bad;
 }
 
+/* got[i]: a reciprocal of the pattern lo + i; it must equal the IEEE
+ * binary32 quotient 1 / d, which C's division gives. */
+int64_t cmp_recip(uint32_t lo, uint64_t n, const float* got, uint64_t* first) {
+  int64_t bad = 0;
+  uint64_t first_bad = UINT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : first_bad)
+  for (int64_t i = 0; i < (int64_t)n; ++i) {
+    float want = 1.0f / from_bits((uint32_t)(lo + (uint64_t)i));
+    if (memcmp(&want, &got[i], 4) != 0) {
+      ++bad;
+      if ((uint64_t)i < first_bad) first_bad = (uint64_t)i;
+    }
+  }
+  *first = first_bad;
+  return bad;
+}
+
 int64_t cmp_bf16(bf16_fn f, uint32_t lo, uint64_t n, const uint32_t* got,
                  uint64_t* first) {
   int64_t bad = 0;

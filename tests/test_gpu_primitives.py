@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROBES = os.path.join(ROOT, "tests", "_build", "libprobes.so")
 CHUNK = 1 << 26  # result pairs per launch
 
-HW_FP4, SW_FP4, HW_BF16, SW_BF16, HW_FP8, SW_FP8, HW_FP4_FLOOR = range(7)
+HW_FP4, SW_FP4, HW_BF16, SW_BF16, HW_FP8, SW_FP8, HW_FP4_FLOOR, RECIP = range(8)
 
 
 def bits(f):
@@ -223,3 +223,18 @@ def test_e2m1_scaled_encode_every_scale(probes, pins, olib):
         bad = pins.cmp_fp4_scaled(f, k, n, got.ctypes.data, ctypes.byref(first))
         assert bad == 0, "k=%d: %d mismatches, first pair at pattern %#x" % (
             k, bad, (2 * first.value) << 13)
+
+
+def test_reciprocal_every_normal_divisor(probes, pins):
+    # The reciprocal table of the NVFP4 quantizer: the refined hardware
+    # reciprocal equals the IEEE quotient 1/d for every binary32 d in
+    # [2^-126, 2^126] (2.1e9 values), the range the kernels use it on.
+    lo, hi = bits(2.0 ** -126), bits(2.0 ** 126)
+    start = lo
+    while start <= hi:
+        n = min(CHUNK, hi - start + 1)
+        got = np.ascontiguousarray(run(probes, RECIP, start, 0, n, torch.float32))
+        first = ctypes.c_uint64(0)
+        bad = pins.cmp_recip(start, n, got.ctypes.data, ctypes.byref(first))
+        assert bad == 0, "%d mismatches, first at pattern %#x" % (bad, start + first.value)
+        start += n

@@ -167,3 +167,17 @@ def test_scaled_encode_comparator_cpu(pins, olib):
         got[i] ^= 1
         assert pins.cmp_fp4_scaled(f, k, n, got.ctypes.data, ctypes.byref(first)) == 1, k
         assert first.value == i
+
+
+def test_reciprocal_comparator_cpu(pins):
+    # The comparator behind the GPU pin of the refined reciprocal accepts
+    # numpy's IEEE float32 quotients and reports one planted last-bit error
+    # at its index.
+    lo, n = bits(1.0) - 12345, 1 << 20
+    d = (np.arange(n, dtype=np.uint64) + lo).astype(np.uint32).view(np.float32)
+    got = np.ascontiguousarray((np.float32(1.0) / d).astype(np.float32))
+    first = ctypes.c_uint64(0)
+    assert pins.cmp_recip(lo, n, got.ctypes.data, ctypes.byref(first)) == 0
+    got.view(np.uint32)[777] ^= 1
+    assert pins.cmp_recip(lo, n, got.ctypes.data, ctypes.byref(first)) == 1
+    assert first.value == 777
