@@ -754,7 +754,9 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
   const RowScale rs = gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(row_amax);
   if (lane == 0 && tscale != nullptr) tscale[row] = rs.s;
   fill_recip(recip[wave], rs.s, lane);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   for (int j = lane; j < nblk; j += 64) {
     uint32_t w[8];
     float xv[16];
