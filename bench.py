@@ -269,11 +269,13 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
     lines = ["# Kernel durations, bench.py default run (moe_act 8192x7168 headline + secondary "
              "calls)", "", "Command (repo root, MI355X):", "", "    " + cmd_trace, "",
              "Per kernel and workload, from the kernel trace (us):", "",
-             "| kernel / workload | dispatches | mean | p50 | min | max |", "|---|---|---|---|---|---|"]
+             "| kernel / workload | dispatches | mean | p10 | p50 | p90 | min | max |",
+             "|---|---|---|---|---|---|---|---|"]
     for lab, d in sorted(dur.items()):
         a = np.array(d)
-        lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
-            lab, a.size, a.mean(), np.median(a), a.min(), a.max()))
+        lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+            lab, a.size, a.mean(), np.percentile(a, 10), np.median(a), np.percentile(a, 90),
+            a.min(), a.max()))
     lines += ["", "rocprofv3 --stats summary (all kernels of the run):", "",
               "| kernel | calls | total ns | average ns | % |", "|---|---|---|---|---|"]
     for r in srows[:12]:
