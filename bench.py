@@ -167,12 +167,45 @@ def cpu_baseline(x_bits, rows_sample, repeats=7):
                           "threads": nthr, "elements_per_s": rows_sample * hidden / tm}}
 
 
+def _code_only(text):
+    """C/C++ source without comments, blank lines or trailing blanks, so
+    that an edit of comments alone leaves the digest unchanged."""
+    out, i, n, quote = [], 0, len(text), None
+    while i < n:
+        ch = text[i]
+        if quote:
+            out.append(ch)
+            if ch == "\\" and i + 1 < n:
+                out.append(text[i + 1])
+                i += 1
+            elif ch == quote:
+                quote = None
+        elif ch in "\"'":
+            quote = ch
+            out.append(ch)
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            continue
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+            continue
+        else:
+            out.append(ch)
+        i += 1
+    lines = (ln.rstrip() for ln in "".join(out).splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest():
+    """Digest of the kernel sources' code (comments excluded)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_block_quantization_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

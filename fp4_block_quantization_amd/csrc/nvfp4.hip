@@ -25,8 +25,11 @@
 //     (within 2^-22 of t) and converts t' (1 -+ 2^-18); when both bounds
 //     give the same E4M3 byte, so does t (rounding is monotone); otherwise
 //     it divides.
-//   r = fl(1 / fl(e s)), looked up in a per-row LDS table of all E4M3 bytes
-//     (the same IEEE division, done once per row instead of per block).
+//   r = fl(1 / fl(e s)), looked up in each wavefront's LDS table of all
+//     E4M3 bytes, filled once per row instead of per block: the hardware
+//     reciprocal refined by one FMA residual step, which is the IEEE
+//     quotient for every divisor in [2^-126, 2^126] (rows with other
+//     divisors divide).
 //   v = fl(x r); q = E2M1(v) with the sign of x.
 //   c = fl(fl(g e) s): g e is exact in FP16 (<= 6 significant bits, between
 //     2^-10 and 2688), so the kernel multiplies in packed FP16 and rounds
