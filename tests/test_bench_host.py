@@ -1,0 +1,57 @@
+"""Host logic of bench.py, on the CPU: the algorithmic byte counts behind
+every GB/s figure (against the per-workload totals stated with the
+workloads: read the BF16 input, write codes, scales and optional dequant),
+the comment-blind source digest that guards the HBM traffic figures, and
+the one-GPU-only exit."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_of_the_workloads():
+    # moe_act 8192 x 7168, 4/6 + dequant: 4.5631 B per element
+    assert bench.nvfp4_bytes(8192, 7168) == 267_943_936
+    # expert weights 65536 x 7168 with dequant
+    assert bench.nvfp4_bytes(65536, 7168) == 2_143_551_488
+    # ragged routed 65536 x 2048, no dequant, 64 groups (65 int64 offsets)
+    assert bench.nvfp4_bytes(65536, 2048, dequant=False, groups=64) == 344_195_592
+    # tiny 256 x 2048, per mode
+    assert bench.nvfp4_bytes(256, 2048) == 2_393_088
+    # MXFP4 Rollout-ResQ 8192 x 7168: codes, E8M0, kept residual codes,
+    # 2:4 metadata, residual E8M0
+    assert bench.mx_bytes(8192, 7168) == 172_490_752
+    # standalone dequant reads codes, scales and token scales, writes BF16
+    assert bench.dequant_bytes(8192, 7168) == 8192 * 7168 * (2 + 0.5 + 1 / 16) + 8192 * 4
+
+
+def test_code_only_drops_comments_keeps_strings():
+    src = ('int a = 1;  // trailing\n'
+           '/* a block\n   comment */\n'
+           'const char* s = "not // a comment /* either */";\n'
+           '\n'
+           'char c = \'/\'; char q = \'"\';  int b = a / 2;\n')
+    got = bench._code_only(src)
+    lines = got.split("\n")
+    assert lines[0] == "int a = 1;"
+    assert "trailing" not in got and "block" not in got
+    assert 'const char* s = "not // a comment /* either */";' in lines
+    assert "char c = '/'; char q = '\"';  int b = a / 2;" in lines
+    # a comment-only edit keeps the text; a code edit changes it
+    assert bench._code_only(src.replace("trailing", "other words")) == got
+    assert bench._code_only(src.replace("a / 2", "a / 3")) != got
+
+
+def test_source_digest_is_stable():
+    assert bench.source_digest() == bench.source_digest()
+    assert len(bench.source_digest()) == 16
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
