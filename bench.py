@@ -386,7 +386,63 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
     print("\n".join(lines))
 
 
+SQ_COUNTERS = ("GRBM_GUI_ACTIVE SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_SALU "
+               "SQ_INSTS_LDS SQ_WAVE_CYCLES SQ_BUSY_CYCLES")
+N_SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
+N_XCDS = 8
+PEAK_CLOCK_HZ = 2.4e9
+
+
+def summarize_sq(sq_dir, out_dir):
+    """Instruction mix and VALU occupancy per kernel from one rocprofv3
+    --pmc run of SQ_COUNTERS over this script: instructions per wave, issue
+    cycles per VALU instruction (SQ_ACTIVE_INST_VALU counts in units of 4
+    cycles), and the share of the SIMDs' cycles spent issuing VALU work --
+    once against GRBM_GUI_ACTIVE (reported summed over the XCDs, so divided
+    by their number) and once against the dispatch's own duration at the
+    2.4 GHz peak clock."""
+    import glob
+    path = glob.glob(os.path.join(sq_dir, "*counter_collection.csv"))[0]
+    per = {}
+    for cname in SQ_COUNTERS.split():
+        rows, labels = _read_dispatches(path, cname)
+        for r, lab in zip(rows, labels):
+            if lab:
+                d = per.setdefault(lab, {}).setdefault(cname, [])
+                d.append((float(r["Counter_Value"]),
+                          (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9))
+    cmd = ("rocprofv3 --pmc %s -f csv -d %s -o run -- python bench.py --steps 20 --warmup 2 "
+           "--sets 2 --no-cpu" % (SQ_COUNTERS, sq_dir))
+    lines = ["# SQ instruction counters per dispatch (rocprofv3 --pmc)", "",
+             "Command (repo root, MI355X), one run:", "", "    " + cmd, "",
+             "Medians over the dispatches of each kernel (the counter run serializes "
+             "dispatches).  Cycles per VALU instruction = 4 SQ_ACTIVE_INST_VALU / "
+             "SQ_INSTS_VALU.  VALU busy = 4 SQ_ACTIVE_INST_VALU / (%d SIMDs x cycles), with "
+             "cycles = GRBM_GUI_ACTIVE / %d (the counter is summed over the XCDs), or = the "
+             "dispatch time x 2.4 GHz." % (N_SIMDS, N_XCDS), "",
+             "| kernel / workload | waves | VALU instr / wave | SALU / wave | LDS / wave | "
+             "cycles / VALU instr | VALU busy (GRBM) | VALU busy (time x 2.4 GHz) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for lab in sorted(per):
+        c = {k: np.median([v for v, _ in per[lab][k]]) for k in per[lab]}
+        t = np.median([d for _, d in per[lab]["SQ_INSTS_VALU"]])
+        waves = c["SQ_WAVES"]
+        valu_cycles = 4 * c["SQ_ACTIVE_INST_VALU"] / N_SIMDS
+        lines.append("| %s | %.0f | %.1f | %.1f | %.1f | %.2f | %.1f%% | %.1f%% |" % (
+            lab, waves, c["SQ_INSTS_VALU"] / waves, c["SQ_INSTS_SALU"] / waves,
+            c["SQ_INSTS_LDS"] / waves, 4 * c["SQ_ACTIVE_INST_VALU"] / c["SQ_INSTS_VALU"],
+            100 * valu_cycles / (c["GRBM_GUI_ACTIVE"] / N_XCDS),
+            100 * valu_cycles / (t * PEAK_CLOCK_HZ)))
+    os.makedirs(out_dir, exist_ok=True)
+    open(os.path.join(out_dir, "sq_counters_bench.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-sq":
+        # python bench.py --summarize-sq SQ_DIR
+        summarize_sq(sys.argv[2], os.path.join(ROOT, "profiles"))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
         # python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR
         summarize_profiles(*sys.argv[2:5], os.path.join(ROOT, "profiles"))

@@ -109,6 +109,18 @@ __device__ __forceinline__ float recip_normal(float d) {
   return __builtin_fmaf(e, y, y);
 }
 
+// fl(a / C) for a non-negative finite BF16 value a (a row amax) and C = 1536
+// (four_over_six) or 2688: the product with fl(1/C), corrected by one FMA
+// residual step.  Equal to the IEEE quotient for every such a and both
+// constants (pinned exhaustively on the GPU).
+__device__ __forceinline__ float amax_over_c(float a, bool four_over_six) {
+  const float c = four_over_six ? 1536.0f : 2688.0f;
+  const float c_inv = four_over_six ? 0x1.555556p-11f : 0x1.861862p-12f;  // fl(1/c)
+  const float q = a * c_inv;
+  const float r = __builtin_fmaf(-q, c, a);
+  return __builtin_fmaf(r, c_inv, q);
+}
+
 // ---- portable definitions -------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

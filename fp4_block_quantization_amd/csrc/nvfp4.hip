@@ -21,10 +21,14 @@
 //
 // Arithmetic per block and candidate k (each an IEEE binary32 operation, no
 // contraction), with the exact equivalences the kernel relies on:
-//   t = fl(b / fl(k s)); e = E4M3(t).  The kernel forms t' = b * (1/fl(k s))
-//     (within 2^-22 of t) and converts t' (1 -+ 2^-18); when both bounds
-//     give the same E4M3 byte, so does t (rounding is monotone); otherwise
-//     it divides.
+//   t = fl(b / fl(k s)); e = E4M3(t).  With y the hardware reciprocal of
+//     fl(k s) (within 2^-22 of it), the kernel forms b * fl(y (1 - 2^-18))
+//     and b * fl(y (1 + 2^-18)) -- the factors folded into per-row
+//     constants -- which lie strictly below and above t (2^-18 exceeds the
+//     2^-22 and three roundings of 2^-24 together); when both give the same
+//     E4M3 byte, so does t (rounding is monotone); otherwise it divides.
+//   s = fl(amax / C) itself comes from the product with fl(1/C) and one FMA
+//     residual correction, the IEEE quotient for every BF16 amax.
 //   r = fl(1 / fl(e s)), looked up in each wavefront's LDS table of all
 //     E4M3 bytes, filled once per row instead of per block: the hardware
 //     reciprocal refined by one FMA residual step, which is the IEEE
@@ -202,7 +206,9 @@ __device__ __forceinline__ uint32_t block_absmax_bits(const uint32_t (&w)[8]) {
 struct RowScale {
   float s;           // token scale, stored
   float ks6, ks4;    // fl(6 s), fl(4 s); 1 for a zero row (so b / ks = 0)
-  float rks6, rks4;  // approximate reciprocals for the bracketed block scale
+  // approximate reciprocals of ks6 and ks4 times 1 - 2^-18 and 1 + 2^-18:
+  // b times them brackets the block scale (see quantize_block_fast)
+  float rks6_lo, rks6_hi, rks4_lo, rks4_hi;
   bool fast;         // every decode step e s is 0 or >= 2^-127
   bool certify;      // 2^-50 <= s <= 2^40: the error enclosure applies
   float inv_s;       // fl(1 / s), for the FP16 decision (FOS == 2)
@@ -215,8 +221,11 @@ __device__ __forceinline__ RowScale row_scale_s(float s) {
   r.s = s;
   r.ks6 = (r.s != 0.0f) ? 6.0f * r.s : 1.0f;
   r.ks4 = (r.s != 0.0f) ? 4.0f * r.s : 1.0f;
-  r.rks6 = __builtin_amdgcn_rcpf(r.ks6);
-  r.rks4 = __builtin_amdgcn_rcpf(r.ks4);
+  const float rks6 = __builtin_amdgcn_rcpf(r.ks6), rks4 = __builtin_amdgcn_rcpf(r.ks4);
+  r.rks6_lo = rks6 * (1.0f - 0x1p-18f);
+  r.rks6_hi = rks6 * (1.0f + 0x1p-18f);
+  r.rks4_lo = rks4 * (1.0f - 0x1p-18f);
+  r.rks4_hi = rks4 * (1.0f + 0x1p-18f);
   // s >= 2^-118: ks >= 2^-116 so 1/ks is normal, and the smallest decode
   // step 2^-9 s >= 2^-127 has a finite reciprocal.
   r.fast = r.s >= 0x1p-118f || r.s == 0.0f;
@@ -229,7 +238,7 @@ __device__ __forceinline__ RowScale row_scale_s(float s) {
 // s = fl(amax / C).
 template <int FOS>
 __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
-  return row_scale_s<FOS>(__uint_as_float(amax_bits) / (FOS ? 1536.0f : 2688.0f));
+  return row_scale_s<FOS>(amax_over_c(__uint_as_float(amax_bits), FOS != 0));
 }
 
 // tab[byte] = 1 / fl(e(byte) s) for all 128 E4M3 bytes, lane l of the
@@ -458,9 +467,8 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
   const float b = __uint_as_float(bbits);
   // bracketed block scales for both candidates (byte 0: map to 6, byte 1:
   // map to 4)
-  const float t6 = b * rs.rks6, t4 = FOS ? b * rs.rks4 : 0.0f;
-  const uint32_t lo = cvt_e4m3x2(t6 * (1.0f - 0x1p-18f), t4 * (1.0f - 0x1p-18f));
-  uint32_t eb = cvt_e4m3x2(t6 * (1.0f + 0x1p-18f), t4 * (1.0f + 0x1p-18f));
+  const uint32_t lo = cvt_e4m3x2(b * rs.rks6_lo, FOS ? b * rs.rks4_lo : 0.0f);
+  uint32_t eb = cvt_e4m3x2(b * rs.rks6_hi, FOS ? b * rs.rks4_hi : 0.0f);
   if (__builtin_expect(lo != eb, 0))
     eb = cvt_e4m3x2(fminf(b / rs.ks6, 448.0f), FOS ? fminf(b / rs.ks4, 448.0f) : 0.0f);
   const float e6 = e4m3_value<0>(eb);

@@ -130,6 +130,14 @@ __global__ void k_recip_normal(uint32_t lo, uint64_t n, float* out) {
   out[i] = fp4q::recip_normal(pat(lo, i, 0u));
 }
 
+// out[i] = the token scale of the BF16 amax pattern i % 0x7F80 (every
+// non-negative finite BF16 value), four_over_six for i >= 0x7F80
+__global__ void k_amax_over_c(float* out) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2u * 0x7F80u) return;
+  out[i] = fp4q::amax_over_c(__uint_as_float((i % 0x7F80u) << 16), i >= 0x7F80u);
+}
+
 dim3 grid_for(uint64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 
 }  // namespace
@@ -170,6 +178,13 @@ int probe_encode_scaled(uint32_t sbits, uint64_t n, void* out, void* stream) {
   if (n == 0 || n > (1ull << 18)) return 2;
   hipLaunchKernelGGL(k_hw_fp4_encode_scaled, grid_for(n), dim3(256), 0, (hipStream_t)stream, sbits,
                      n, (uint8_t*)out);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// out[i], i < 2 * 0x7F80: see k_amax_over_c
+int probe_amax_over_c(void* out, void* stream) {
+  hipLaunchKernelGGL(k_amax_over_c, grid_for(2 * 0x7F80), dim3(256), 0, (hipStream_t)stream,
+                     (float*)out);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -47,6 +47,8 @@ def probes():
     L.probe_encode_scaled.argtypes = [ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_void_p]
     L.probe_encode_scaled.restype = ctypes.c_int
+    L.probe_amax_over_c.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    L.probe_amax_over_c.restype = ctypes.c_int
     return L
 
 
@@ -238,3 +240,20 @@ def test_reciprocal_every_normal_divisor(probes, pins):
         bad = pins.cmp_recip(start, n, got.ctypes.data, ctypes.byref(first))
         assert bad == 0, "%d mismatches, first at pattern %#x" % (bad, start + first.value)
         start += n
+
+
+def test_token_scale_every_bf16_amax(probes):
+    # The token scale s = fl(amax / C) by product and FMA correction equals
+    # the IEEE quotient (numpy's float32 division) for every non-negative
+    # finite BF16 amax, for C = 2688 (6 only) and C = 1536 (Four-Over-Six).
+    n = 0x7F80
+    out = torch.empty(2 * n, dtype=torch.float32, device="cuda")
+    assert probes.probe_amax_over_c(ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    a = (np.arange(n, dtype=np.uint32) << 16).view(np.float32)
+    for half, c in ((0, 2688.0), (1, 1536.0)):
+        want = (a / np.float32(c)).astype(np.float32).view(np.uint32)
+        bad = np.nonzero(got[half * n:(half + 1) * n] != want)[0]
+        assert len(bad) == 0, "C=%g: amax pattern %#x" % (c, int(bad[0]) << 16)
