@@ -92,11 +92,6 @@ namespace {
 #ifndef FP4Q_NV_LDS_LOAD
 #define FP4Q_NV_LDS_LOAD 1
 #endif
-// Build-time knob: FP4Q_NV_WAVE_SYNC = 1 replaces the workgroup barriers
-// by wave barriers when each row has a single wave.
-#ifndef FP4Q_NV_WAVE_SYNC
-#define FP4Q_NV_WAVE_SYNC 1
-#endif
 // Build-time knob: blocks per lane in the split kernel (1 to 4; 2 measured
 // fastest on 2048- and 7168-element rows).
 #ifndef FP4Q_NV_NB
@@ -546,6 +541,14 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
   }
 }
 
+// a < b for int64 values, from the signed high and unsigned low words, so
+// that wave-uniform operands are compared by the scalar unit
+__device__ __forceinline__ bool lt_i64(int64_t a, int64_t b) {
+  const int ah = (int)(a >> 32), bh = (int)(b >> 32);
+  const uint32_t al = (uint32_t)a, bl = (uint32_t)b;
+  return ah < bh || (ah == bh && al < bl);
+}
+
 __device__ __forceinline__ bool row_range(int64_t row, int64_t rows, const int64_t* offs,
                                           int64_t ngroups) {
   int64_t lo = 0, hi = rows;
@@ -584,7 +587,10 @@ __device__ __forceinline__ ChunkRef chunk_ref(int64_t g, int rw, int chunk, int 
                                               const int64_t* offs, int64_t ngroups) {
   ChunkRef c;
   c.row = row0 + g * R + rw;
-  c.active = c.row < row_end && row_range(c.row, rows, offs, ngroups);
+  // row < row_end <= rows, and row >= 0, so only the group range is left
+  // to check; the comparisons stay in scalar registers
+  c.active = lt_i64(c.row, row_end) &&
+             (offs == nullptr || (!lt_i64(c.row, offs[0]) && lt_i64(c.row, offs[ngroups])));
   c.valid = c.active ? min(64 * NB, nblk - chunk * 64 * NB) : 0;
   c.cbase = c.row * nblk + (int64_t)chunk * 64 * NB;
   return c;
@@ -606,20 +612,6 @@ __device__ __forceinline__ void load_chunk(const uint4* __restrict__ x, const Ch
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-// Barrier for the exchange between the waves of a row: the whole workgroup
-// when rows span several waves; with one wave per row (W == 1, uniform over
-// the workgroup) the row's own wave, so the rows of a workgroup do not wait
-// for each other.
-__device__ __forceinline__ void wg_sync(int W) {
-  if (FP4Q_NV_WAVE_SYNC && W == 1) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  } else {
-    __syncthreads();
-  }
-}
 
 // The same chunk through LDS: every lane copies 16 consecutive bytes per
 // instruction straight into the wave's LDS tile (1 KiB contiguous per
@@ -662,7 +654,7 @@ __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, cons
 template <int FOS, bool DQ, int NB, bool NTC>
 __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk, int W,
-    int R, const int64_t* __restrict__ offs, int64_t ngroups,
+    int wdiv, int R, const int64_t* __restrict__ offs, int64_t ngroups,
     uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
     float neg_zero, const float* __restrict__ gscale) {
@@ -676,10 +668,12 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // half n, once read, stages the dequant values of block group n; else
   // 2 KiB of staging
   constexpr int kWaveLds = kLdsLoad ? 128 * NB : 128;
-  uint4* wave_lds = dyn_lds + 32 * W * R + kWaveLds * (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rw = wave / W, chunk = wave - rw * W;  // wave-uniform
+  uint4* wave_lds = dyn_lds + 32 * W * R + kWaveLds * wave;
+  // wave / W as a scalar multiply and shift: wdiv = ceil(2^16 / W) is exact
+  // for every wave < 16 and W <= 16
+  const int rw = (wave * wdiv) >> 16, chunk = wave - rw * W;  // wave-uniform
 
   const ChunkRef c =
       chunk_ref<NB>(blockIdx.x, rw, chunk, R, nblk, row0, row_end, rows, offs, ngroups);
@@ -696,13 +690,17 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     lmax = max(lmax, bmax[n]);
   }
 
-  const uint32_t m = wave_max_u32(lmax);
-  if (lane == 0) wave_max[wave] = m;
-  wg_sync(W);
-  // every wave derives the row constants and fills its own reciprocal
-  // table, so the row needs no second workgroup barrier
-  uint32_t amax_bits = 0;
-  for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+  // the row amax: a one-wave row has it already; otherwise the row's waves
+  // combine theirs through LDS.  Every wave then derives the row constants
+  // and fills its own reciprocal table, so the row needs no second
+  // workgroup barrier.
+  uint32_t amax_bits = wave_max_u32(lmax);
+  if (W > 1) {  // uniform over the workgroup
+    if (lane == 0) wave_max[wave] = amax_bits;
+    __syncthreads();
+    amax_bits = 0;
+    for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+  }
   // with gscale, one token scale for the whole tensor
   const RowScale rs =
       gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
@@ -1053,7 +1051,8 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
       const int64_t row_end = a.rows - row0 < max_rows ? a.rows : row0 + max_rows;
       const dim3 grid((unsigned)((row_end - row0 + R - 1) / R)), block(64 * W * R);
       hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB, NTC>), grid, block, lds, st, x,
-                         a.rows, row0, row_end, nblk, W, R, a.offsets, a.num_groups, codes,
+                         a.rows, row0, row_end, nblk, W, (65536 + W - 1) / W, R, a.offsets,
+                         a.num_groups, codes,
                          a.block_scales, a.token_scales, dq, neg_zero, a.global_scale);
     }
   } else {
