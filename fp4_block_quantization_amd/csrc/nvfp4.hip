@@ -206,16 +206,21 @@ struct RowScale {
   float rks6_lo, rks6_hi, rks4_lo, rks4_hi;
   bool fast;         // every decode step e s is 0 or >= 2^-127
   bool certify;      // 2^-50 <= s <= 2^40: the error enclosure applies
+  bool rcp_normal;   // 2^-117 <= s <= 2^116: every nonzero e s in [2^-126, 2^126]
   float inv_s;       // fl(1 / s), for the FP16 decision (FOS == 2)
 };
 
-// Row constants from the token scale s itself.
+// Row constants from the token scale s itself (non-negative, uniform across
+// the wavefront).  Its bit pattern orders like its value, so the range
+// tests are integer compares on a scalar register.
 template <int FOS>
-__device__ __forceinline__ RowScale row_scale_s(float s) {
+__device__ __forceinline__ RowScale row_scale_s(float s_in) {
   RowScale r;
-  r.s = s;
-  r.ks6 = (r.s != 0.0f) ? 6.0f * r.s : 1.0f;
-  r.ks4 = (r.s != 0.0f) ? 4.0f * r.s : 1.0f;
+  const uint32_t sb = __builtin_amdgcn_readfirstlane(__float_as_uint(s_in));
+  r.s = __uint_as_float(sb);
+  const bool zero = sb == 0u;
+  r.ks6 = zero ? 1.0f : 6.0f * r.s;
+  r.ks4 = zero ? 1.0f : 4.0f * r.s;
   const float rks6 = __builtin_amdgcn_rcpf(r.ks6), rks4 = __builtin_amdgcn_rcpf(r.ks4);
   r.rks6_lo = rks6 * (1.0f - 0x1p-18f);
   r.rks6_hi = rks6 * (1.0f + 0x1p-18f);
@@ -223,8 +228,9 @@ __device__ __forceinline__ RowScale row_scale_s(float s) {
   r.rks4_hi = rks4 * (1.0f + 0x1p-18f);
   // s >= 2^-118: ks >= 2^-116 so 1/ks is normal, and the smallest decode
   // step 2^-9 s >= 2^-127 has a finite reciprocal.
-  r.fast = r.s >= 0x1p-118f || r.s == 0.0f;
-  r.certify = r.s >= 0x1p-50f && r.s <= 0x1p40f;
+  r.fast = (sb >= 0x04800000u && sb <= 0x7F800000u) || zero;  // 2^-118 .. inf
+  r.certify = sb >= 0x26800000u && sb <= 0x53800000u;         // 2^-50 .. 2^40
+  r.rcp_normal = sb >= 0x05000000u && sb <= 0x79800000u;      // 2^-117 .. 2^116
   r.inv_s = FOS == 2 ? 1.0f / r.s : 0.0f;
   return r;
 }
@@ -238,16 +244,15 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
 
 // tab[byte] = 1 / fl(e(byte) s) for all 128 E4M3 bytes, lane l of the
 // wavefront writing bytes l and l + 64.
-__device__ __forceinline__ void fill_recip(float* tab, float s, int lane) {
+__device__ __forceinline__ void fill_recip(float* tab, const RowScale& rs, int lane) {
   // For s in [2^-117, 2^116] every nonzero e*s (e from 2^-9 to 448) lies in
   // [2^-126, 2^126], where the refined hardware reciprocal is the IEEE
-  // quotient; other rows divide.  s is uniform across the wavefront.
-  const bool normal = __builtin_amdgcn_readfirstlane((s >= 0x1p-117f && s <= 0x1p116f) ? 1 : 0);
+  // quotient; other rows divide.
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int byte = lane + 64 * h;
-    const float d = e4m3_value<0>((uint32_t)byte) * s;
-    const float r = normal ? recip_normal(d) : 1.0f / d;
+    const float d = e4m3_value<0>((uint32_t)byte) * rs.s;
+    const float r = rs.rcp_normal ? recip_normal(d) : 1.0f / d;
     tab[byte] = (d != 0.0f) ? r : 0.0f;
   }
 }
@@ -706,7 +711,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
       gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
   if (chunk == 0 && lane == 0 && c.active && tscale != nullptr) tscale[c.row] = rs.s;
   float* tab = recip[wave];
-  fill_recip(tab, rs.s, lane);
+  fill_recip(tab, rs, lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -762,7 +767,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
   const uint32_t row_amax = wave_max_u32(lmax);
   const RowScale rs = gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(row_amax);
   if (lane == 0 && tscale != nullptr) tscale[row] = rs.s;
-  fill_recip(recip[wave], rs.s, lane);
+  fill_recip(recip[wave], rs, lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
