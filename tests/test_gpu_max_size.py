@@ -1,0 +1,98 @@
+"""GPU parity at the largest size class: a 300000 x 7168 BF16 tensor
+(2,150,400,000 elements, 4.3 GB), past 2^31 elements and 2^32 input and
+dequant bytes, so the element, byte and row indexing of every kernel runs
+beyond 32 bits.
+
+Rows are independent, so the oracle checks sampled rows bit for bit: the
+first and last, the rows around the 2^31-element boundary, the rows where
+the seeded pool below wraps, and seeded random rows.  Properties that hold
+at any size cover every element: the fused dequant equals the standalone
+dequantizer, and guided rounding toward the tensor's own codes under its
+own scales reproduces those codes (it is round-to-nearest then).
+
+The tensor is built on the device from a seeded pool of 4099 heavy-tailed
+rows (Student-t(3) times a per-row LogNormal(0, 0.5) gain): row r is pool
+row r mod 4099 times 2^((7 r mod 17) - 8), an exact BF16 scaling, so a
+kernel that read a neighbouring row would see different values.  The
+oracle's inputs are the sampled rows read back from device memory."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_block_quantization_amd as fq
+import workloads
+from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_nvfp4
+
+pytestmark = pytest.mark.gpu
+
+ROWS, HIDDEN, POOL = 300000, 7168, 4099
+
+
+@pytest.fixture(scope="module")
+def big():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fq.lib()
+    assert ROWS * HIDDEN > 2 ** 31 and 2 * ROWS * HIDDEN > 2 ** 32
+    print("max-size: building %dx%d BF16 on the device" % (ROWS, HIDDEN), flush=True)
+    pool_bits = workloads.to_bf16_bits(workloads.fill_fp32(11, 0, POOL, HIDDEN, dist=1,
+                                                           scale=1.0, row_gain_sigma=0.5))
+    pool = torch.from_numpy(pool_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    x = torch.empty((ROWS, HIDDEN), dtype=torch.bfloat16, device="cuda")
+    step = 16384
+    for r0 in range(0, ROWS, step):
+        r = torch.arange(r0, min(ROWS, r0 + step), device="cuda", dtype=torch.int64)
+        gain = torch.pow(2.0, ((7 * r) % 17 - 8).to(torch.float32)).to(torch.bfloat16)
+        x[r0:r0 + r.numel()] = pool[r % POOL] * gain[:, None]
+    del pool
+    torch.cuda.synchronize()
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+def sample_rows():
+    b = 2 ** 31 // HIDDEN  # the row holding element 2^31 (and input byte 2^32)
+    fixed = [0, 1, POOL - 1, POOL, b - 1, b, b + 1, ROWS - 2, ROWS - 1]
+    rng = np.random.default_rng(2026)
+    return np.unique(np.concatenate([fixed, rng.integers(0, ROWS, 23)])).astype(np.int64)
+
+
+def host_rows(t, idx):
+    return t[torch.from_numpy(idx).cuda()]
+
+
+def test_nvfp4_max_size_sampled_rows_and_dequant(big):
+    x = big
+    idx = sample_rows()
+    print("max-size nvfp4_quantize 4/6 + dequant, rows", idx.tolist(), flush=True)
+    codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=True, dequant=True)
+    torch.cuda.synchronize()
+    x_bits = bits_of(host_rows(x, idx))
+    want = oracle_nvfp4(x_bits, True, dequant=True)
+    assert_same(host(host_rows(codes, idx)), want[0], "max-size codes")
+    assert_same(host(host_rows(scales, idx)), want[1], "max-size block_scales")
+    assert_same(host(host_rows(ts, idx))[:, None], want[2][:, None], "max-size token_scales")
+    assert_same(bits_of(host_rows(dq, idx)), want[3], "max-size dequant")
+
+    print("max-size nvfp4_dequantize over every element", flush=True)
+    back = fq.nvfp4_dequantize(codes, scales, ts)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), dq.view(torch.int16))
+    del back, dq
+
+    print("max-size nvfp4_quantize_guided toward its own codes", flush=True)
+    gcodes, _ = fq.nvfp4_quantize_guided(x, codes, scales, ts, dequant=False)
+    torch.cuda.synchronize()
+    assert torch.equal(gcodes, codes)
+
+
+def test_mx_max_size_sampled_rows(big):
+    x = big
+    idx = sample_rows()
+    print("max-size mxfp4_resq_quantize, rows", idx.tolist(), flush=True)
+    got = fq.mxfp4_resq_quantize(x)
+    torch.cuda.synchronize()
+    want = oracle_mx(bits_of(host_rows(x, idx)))
+    for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
+        assert_same(host(host_rows(g, idx)), w, "max-size mx " + n)
