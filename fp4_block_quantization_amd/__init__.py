@@ -90,6 +90,28 @@ def _dev(t, name, dtype):
     return t
 
 
+def _same_device(x, *ts):
+    for t in ts:
+        if t is not None and t.device != x.device:
+            raise Fp4qError("all tensors must be on %s, got one on %s" % (x.device, t.device))
+
+
+def _sized(t, name, dtype, numel):
+    """A caller-supplied tensor: on a GPU, of dtype, contiguous, holding
+    exactly numel elements (the kernels write or read that many)."""
+    _dev(t, name, dtype)
+    if t.numel() != numel:
+        raise Fp4qError("%s must hold %d elements, got %d" % (name, numel, t.numel()))
+    return t
+
+
+def _rows_hidden(codes):
+    """rows and hidden of a [rows, hidden/2] code tensor."""
+    if codes.dim() != 2:
+        raise Fp4qError("codes must be 2-D [rows, hidden/2]")
+    return codes.shape[0], 2 * codes.shape[1]
+
+
 def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -121,20 +143,18 @@ def nvfp4_quantize(x, four_over_six=True, offsets=None, dequant=True, out=None):
         dq = torch.empty_like(x) if dequant else None
     else:
         codes, scales, ts, dq = out
-        _dev(codes, "codes", torch.uint8)
-        _dev(scales, "block_scales", torch.uint8)
-        _dev(ts, "token_scales", torch.float32)
+        _sized(codes, "codes", torch.uint8, rows * (hidden // 2))
+        _sized(scales, "block_scales", torch.uint8, rows * (hidden // 16))
+        _sized(ts, "token_scales", torch.float32, rows)
         if dq is not None:
-            _dev(dq, "dequant", torch.bfloat16)
-        if (codes.numel() != rows * (hidden // 2) or scales.numel() != rows * (hidden // 16)
-                or ts.numel() != rows or (dq is not None and dq.numel() != rows * hidden)):
-            raise Fp4qError("output tensor sizes do not match x")
+            _sized(dq, "dequant", torch.bfloat16, rows * hidden)
     ng = 0
     if offsets is not None:
         _dev(offsets, "offsets", torch.int64)
         ng = offsets.numel() - 1
         if ng < 1:
             raise Fp4qError("offsets needs at least two entries")
+    _same_device(x, codes, scales, ts, dq, offsets)
     st = lib().nvfp4_quantize(_p(x), rows, hidden, _p(offsets), ng, _mode(four_over_six),
                               _p(codes), _p(scales), _p(ts), _p(dq), _stream(x))
     _check(st, "nvfp4_quantize")
@@ -143,16 +163,13 @@ def nvfp4_quantize(x, four_over_six=True, offsets=None, dequant=True, out=None):
 
 def nvfp4_dequantize(codes, block_scales, token_scales, out=None):
     _dev(codes, "codes", torch.uint8)
-    _dev(block_scales, "block_scales", torch.uint8)
-    _dev(token_scales, "token_scales", torch.float32)
-    rows = codes.shape[0]
-    hidden = codes.numel() // max(rows, 1) * 2
+    rows, hidden = _rows_hidden(codes)
+    _sized(block_scales, "block_scales", torch.uint8, rows * (hidden // 16))
+    _sized(token_scales, "token_scales", torch.float32, rows)
     if out is None:
         out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=codes.device)
-    _dev(out, "out", torch.bfloat16)
-    if (block_scales.numel() != rows * (hidden // 16) or token_scales.numel() != rows
-            or out.numel() != rows * hidden):
-        raise Fp4qError("tensor sizes do not match codes")
+    _sized(out, "out", torch.bfloat16, rows * hidden)
+    _same_device(codes, block_scales, token_scales, out)
     st = lib().nvfp4_dequantize(_p(codes), _p(block_scales), _p(token_scales), rows, hidden,
                                 _p(out), _stream(codes))
     _check(st, "nvfp4_dequantize")
@@ -170,8 +187,12 @@ def mxfp4_resq_quantize(x, out=None):
         out = (torch.empty((rows, hidden // 2), **kw), torch.empty((rows, hidden // 32), **kw),
                torch.empty((rows, hidden // 4), **kw), torch.empty((rows, hidden // 8), **kw),
                torch.empty((rows, hidden // 32), **kw))
-    for t, n in zip(out, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
-        _dev(t, n, torch.uint8)
+    if len(out) != 5:
+        raise Fp4qError("out must be (codes, scales, res_codes, res_meta, res_scales)")
+    sizes = (hidden // 2, hidden // 32, hidden // 4, hidden // 8, hidden // 32)
+    for t, n, k in zip(out, ("codes", "scales", "res_codes", "res_meta", "res_scales"), sizes):
+        _sized(t, n, torch.uint8, rows * k)
+    _same_device(x, *out)
     st = lib().mxfp4_resq_quantize(_p(x), rows, hidden, *[_p(t) for t in out], _stream(x))
     _check(st, "mxfp4_resq_quantize")
     return out
@@ -187,8 +208,12 @@ def mxfp4_resq_dense_quantize(x, out=None):
         kw = dict(dtype=torch.uint8, device=x.device)
         out = (torch.empty((rows, hidden // 2), **kw), torch.empty((rows, hidden // 32), **kw),
                torch.empty((rows, hidden // 2), **kw), torch.empty((rows, hidden // 32), **kw))
-    for t, n in zip(out, ("codes", "scales", "res_codes", "res_scales")):
-        _dev(t, n, torch.uint8)
+    if len(out) != 4:
+        raise Fp4qError("out must be (codes, scales, res_codes, res_scales)")
+    sizes = (hidden // 2, hidden // 32, hidden // 2, hidden // 32)
+    for t, n, k in zip(out, ("codes", "scales", "res_codes", "res_scales"), sizes):
+        _sized(t, n, torch.uint8, rows * k)
+    _same_device(x, *out)
     st = lib().mxfp4_resq_dense_quantize(_p(x), rows, hidden, *[_p(t) for t in out], _stream(x))
     _check(st, "mxfp4_resq_dense_quantize")
     return out
@@ -199,17 +224,26 @@ def mxfp4_resq_reconstruct(codes, scales, res_codes=None, res_meta=None, res_sca
     """FP32 X_hat = DQ(Q(X)) (+ DQ(S(Q(dX))) for residual 1, + DQ(Q(dX)) for
     residual 2, from the sparse or dense quantize outputs)."""
     _dev(codes, "codes", torch.uint8)
-    _dev(scales, "scales", torch.uint8)
-    for t, n in ((res_codes, "res_codes"), (res_meta, "res_meta"), (res_scales, "res_scales")):
-        if t is not None:
-            _dev(t, n, torch.uint8)
-    rows = codes.shape[0]
-    hidden = codes.numel() // max(rows, 1) * 2
+    rows, hidden = _rows_hidden(codes)
+    _sized(scales, "scales", torch.uint8, rows * (hidden // 32))
+    # the residual tensors the mode reads: S2:4 (1) kept codes, metadata and
+    # scales; dense (2) every residual code and the scales
+    mode = int(residual)
+    if mode in (1, 2):
+        need = [("res_codes", res_codes, hidden // (4 if mode == 1 else 2)),
+                ("res_scales", res_scales, hidden // 32)]
+        if mode == 1:
+            need.append(("res_meta", res_meta, hidden // 8))
+        for n, t, k in need:
+            if t is None:
+                raise Fp4qError("%s is required for residual=%d" % (n, mode))
+            _sized(t, n, torch.uint8, rows * k)
     if out is None:
         out = torch.empty((rows, hidden), dtype=torch.float32, device=codes.device)
-    _dev(out, "out", torch.float32)
+    _sized(out, "out", torch.float32, rows * hidden)
+    _same_device(codes, scales, res_codes, res_meta, res_scales, out)
     st = lib().mxfp4_resq_reconstruct(_p(codes), _p(scales), _p(res_codes), _p(res_meta),
-                                      _p(res_scales), rows, hidden, int(residual), _p(out),
+                                      _p(res_scales), rows, hidden, mode, _p(out),
                                       _stream(codes))
     _check(st, "mxfp4_resq_reconstruct")
     return out
@@ -226,14 +260,18 @@ def nvfp4_quantize_guided(x, guide_codes, block_scales, token_scales, dequant=Tr
     if x.dim() != 2:
         raise Fp4qError("x must be 2-D [rows, hidden]")
     rows, hidden = x.shape
-    if (guide_codes.numel() != rows * (hidden // 2) or block_scales.numel() != rows * (hidden // 16)
-            or token_scales.numel() != rows):
-        raise Fp4qError("guide tensor sizes do not match x")
+    _sized(guide_codes, "guide_codes", torch.uint8, rows * (hidden // 2))
+    _sized(block_scales, "block_scales", torch.uint8, rows * (hidden // 16))
+    _sized(token_scales, "token_scales", torch.float32, rows)
     if out is None:
         codes = torch.empty((rows, hidden // 2), dtype=torch.uint8, device=x.device)
         dq = torch.empty_like(x) if dequant else None
     else:
         codes, dq = out
+        _sized(codes, "codes", torch.uint8, rows * (hidden // 2))
+        if dq is not None:
+            _sized(dq, "dequant", torch.bfloat16, rows * hidden)
+    _same_device(x, guide_codes, block_scales, token_scales, codes, dq)
     st = lib().nvfp4_quantize_guided(_p(x), rows, hidden, _p(guide_codes), _p(block_scales),
                                      _p(token_scales), _p(codes), _p(dq), _stream(x))
     _check(st, "nvfp4_quantize_guided")
@@ -254,6 +292,12 @@ def nvfp4_quantize_global(x, four_over_six=True, dequant=True, out=None):
         dq = torch.empty_like(x) if dequant else None
     else:
         codes, scales, ts, dq = out
+        _sized(codes, "codes", torch.uint8, rows * (hidden // 2))
+        _sized(scales, "block_scales", torch.uint8, rows * (hidden // 16))
+        _sized(ts, "tensor_scale", torch.float32, 1)
+        if dq is not None:
+            _sized(dq, "dequant", torch.bfloat16, rows * hidden)
+    _same_device(x, codes, scales, ts, dq)
     st = lib().nvfp4_quantize_global(_p(x), rows, hidden, _mode(four_over_six), _p(codes),
                                      _p(scales), _p(ts), _p(dq), _stream(x))
     _check(st, "nvfp4_quantize_global")

@@ -301,6 +301,62 @@ def test_empty_and_rejected_calls():
         fq.nvfp4_quantize(flat[1:1 + 64].view(4, 16))
 
 
+def test_binding_rejects_wrong_sized_buffers():
+    # caller-supplied buffers one element short, or of the wrong type, are
+    # refused before any launch (a short buffer would be written past its end)
+    R, H = 4, 64
+    x = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8, device="cuda")
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32, device="cuda")
+    bf = lambda n: torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    good = (u8(R * H // 2), u8(R * H // 16), f32(R), bf(R * H))
+    good_g = good[:2] + (f32(1),) + good[3:]  # one tensor scale
+    for k in range(4):
+        bad = tuple(t[:-1] if j == k else t for j, t in enumerate(good))
+        with pytest.raises(fq.Fp4qError):
+            fq.nvfp4_quantize(x, out=bad)
+        bad_g = tuple(t[:-1] if j == k else t for j, t in enumerate(good_g))
+        with pytest.raises(fq.Fp4qError):
+            fq.nvfp4_quantize_global(x, out=bad_g)
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_quantize(x, out=(good[0], good[1], good[2], u8(2 * R * H)))  # wrong dtype
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_quantize_global(x, out=(good[0], good[1], f32(2), good[3]))
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_dequantize(good[0].view(R, H // 2), good[1], good[2], out=bf(R * H - 1))
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_dequantize(good[0].view(R, H // 2), u8(R * H // 16 - 1), good[2])
+    with pytest.raises(fq.Fp4qError):  # codes must be [rows, hidden/2]
+        fq.nvfp4_dequantize(good[0], good[1], good[2])
+    mx = (u8(R * H // 2), u8(R * H // 32), u8(R * H // 4), u8(R * H // 8), u8(R * H // 32))
+    for k in range(5):
+        bad = tuple(u8(t.numel() - 1) if j == k else t for j, t in enumerate(mx))
+        with pytest.raises(fq.Fp4qError):
+            fq.mxfp4_resq_quantize(x, out=bad)
+    dense = (mx[0], mx[1], u8(R * H // 2), mx[4])
+    for k in range(4):
+        bad = tuple(u8(t.numel() - 1) if j == k else t for j, t in enumerate(dense))
+        with pytest.raises(fq.Fp4qError):
+            fq.mxfp4_resq_dense_quantize(x, out=bad)
+    c2 = mx[0].view(R, H // 2)
+    with pytest.raises(fq.Fp4qError):  # S2:4 reconstruction needs the metadata
+        fq.mxfp4_resq_reconstruct(c2, mx[1], mx[2], None, mx[4], residual=1)
+    with pytest.raises(fq.Fp4qError):  # dense residual codes are [R, H/2]
+        fq.mxfp4_resq_reconstruct(c2, mx[1], mx[2], None, mx[4], residual=2)
+    with pytest.raises(fq.Fp4qError):
+        fq.mxfp4_resq_reconstruct(c2, mx[1], out=f32(R * H - 1))
+    guide = (u8(R * H // 2), u8(R * H // 16), f32(R))
+    for k in range(3):
+        bad = tuple(t[:-1] if j == k else t for j, t in enumerate(guide))
+        with pytest.raises(fq.Fp4qError):
+            fq.nvfp4_quantize_guided(x, *bad)
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_quantize_guided(x, *guide, out=(u8(R * H // 2 - 1), None))
+    with pytest.raises(fq.Fp4qError):
+        fq.nvfp4_quantize_guided(x, *guide, out=(u8(R * H // 2), bf(R * H - 1)))
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------- TRACE guided rounding --
 
 def check_guided(x_rollout, x_train, label):
