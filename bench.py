@@ -438,6 +438,49 @@ def summarize_sq(sq_dir, out_dir):
     print("\n".join(lines))
 
 
+def size_sweep(x, dev):
+    """Time per call against the row count for the headline quantize
+    (4/6 + dequant), the standalone dequant, MXFP4 Rollout-ResQ and a device
+    copy of the input, on rows of moe_act (tiled past 8192 rows).  Every
+    size rotates over enough buffer sets to span about 1 GiB, so that no
+    size is served by the last-level cache and all see a similar footprint.
+    A fit of time = fixed + rows * per_row separates the per-launch cost
+    from the steady-state rate."""
+    out = {}
+    hidden = x.shape[1]
+    for rows in (1024, 2048, 4096, 8192, 16384, 32768):
+        reps = (rows + x.shape[0] - 1) // x.shape[0]
+        xr = x.repeat(reps, 1)[:rows].contiguous()
+        nsets = max(1, min(32, -(-(1 << 30) // nvfp4_bytes(rows, hidden))))
+        sets = rotating_nvfp4_sets(xr, nsets)
+        mx = [fq.mxfp4_resq_quantize(s[0]) for s in sets]
+        steps = max(100, 400 * 8192 // rows)
+        t = {}
+        t["nvfp4_quantize"], _ = time_calls(
+            lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), sets, steps, steps // 4)
+        t["nvfp4_dequantize"], _ = time_calls(
+            lambda s: fq.nvfp4_dequantize(s[1][0], s[1][1], s[1][2], out=s[1][3]), sets, steps,
+            steps // 4)
+        t["mxfp4_resq_quantize"], _ = time_calls(
+            lambda i: fq.mxfp4_resq_quantize(sets[i][0], out=mx[i]), list(range(nsets)), steps,
+            steps // 4)
+        t["device_copy"], _ = time_calls(lambda s: s[1][3].copy_(s[0]), sets, steps, steps // 4)
+        out[rows] = {k: round(v * 1e3, 3) for k, v in t.items()}
+        out[rows]["sets"] = nsets
+        print("[bench] sweep rows %d: %s" % (rows, json.dumps(out[rows])), file=sys.stderr,
+              flush=True)
+        del sets, mx, xr
+        torch.cuda.empty_cache()
+    fit = {}
+    r = np.array(sorted(out), dtype=np.float64)
+    for k in ("nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize", "device_copy"):
+        us = np.array([out[int(v)][k] for v in r])
+        big = r >= 4096  # the linear regime: several waves of workgroups per CU
+        per_row, fixed = np.polyfit(r[big], us[big], 1)
+        fit[k] = {"fixed_us": round(float(fixed), 2), "ns_per_row": round(float(per_row) * 1e3, 3)}
+    return {"hidden": hidden, "us_per_call": out, "linear_fit_rows_ge_4096": fit}
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-sq":
         # python bench.py --summarize-sq SQ_DIR
@@ -458,6 +501,8 @@ def main():
                     default="copy,dequant,resq,resq_dense,trace,global,ragged,weights,fp16",
                     help="secondary measurements to run (comma list)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--sweep", action="store_true",
+                    help="print only a row-count sweep (time per call vs rows) as JSON")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -478,6 +523,10 @@ def main():
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     print("[bench] generated moe_act %dx%d in %.1f s" % (rows, hidden, time.time() - t0),
           file=sys.stderr, flush=True)
+
+    if args.sweep:
+        print(json.dumps(size_sweep(x, dev)), flush=True)
+        return
 
     sets = rotating_nvfp4_sets(x, args.sets)
     ms, per = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), sets, args.steps,
