@@ -352,30 +352,23 @@ __device__ __forceinline__ float fp16_error(const half2v (&y)[8], const uint32_t
 // with 2^-50 <= s <= 2^40 and e != 0.  With u = 2^-24: v = x r and the
 // candidate value c carry relative rounding errors, so each x - c differs
 // from D (v - g) by at most D 2.01u (|v| + |g|) <= D 32.2u (|v| < 10,
-// |g| <= 6); summed over 16 elements, |sum (x-c)^2 - D^2 S| <= D^2 (258u
-// sqrt(S) + 0.001u) with S the exact sum of (v - g)^2, and A = S (1 +- 16.1u).
-// The FP32 error is sum (x-c)^2 (1 +- 18.1u), plus at most 2^-145 from
-// underflow.  Every coefficient below carries a factor of two or more over
-// these (which also covers the rounding of this arithmetic), and the range of
-// s keeps D^2 normal and every error finite.  sqrt(A) enters through an
-// upper bound: halving the exponent of A (adding the bias, then a right
-// shift of the bit pattern) gives 2^k (1 + f/2) for A = 4^k (1 + f) and
-// 2^k (3/2 + f/2) for A = 2 4^k (1 + f), both >= the square root (AM-GM,
-// and (3/2 + f/2)^2 - 2(1 + f) = (1 - f)^2 / 4), within a factor 1.07 of it
-// for normal A (for subnormal A it is 2^-63 or more, still >= sqrt(A)).
-// Adding one more before the shift rounds the halving up, so the dropped
-// bit cannot take the result below the square root where the two meet
-// (f -> 1).  A < 2^64 here, so the sum does not wrap.
+// |g| <= 6); summed over 16 elements (Cauchy-Schwarz on the cross term),
+// |sum (x-c)^2 - D^2 S| <= D^2 (258u sqrt(S) + 0.001u) with S the exact sum
+// of (v - g)^2, and sqrt(S) <= (S + 1) / 2 makes that at most
+// D^2 (129u S + 129.001u).  A = S (1 +- 16.1u); the FP32 error is
+// sum (x-c)^2 (1 +- 18.1u), plus at most 2^-145 from underflow.  Together:
+// |err - D^2 A| <= D^2 (163.4u A + 129.1u) + 2^-145.  The coefficients below
+// (330u, 260u, 2^-136) are at least twice these, which also covers the three
+// roundings of this arithmetic, and the range of s keeps D^2 normal and every
+// error finite.
 struct ErrBounds {
   float lo, hi;
 };
 __device__ __forceinline__ ErrBounds err_bounds(float A, float D) {
   constexpr float u = 0x1p-24f;
   const float D2 = D * D;
-  const float sq = __uint_as_float((__float_as_uint(A) + 0x3F800001u) >> 1);  // >= sqrt(A)
-  const float t = __builtin_fmaf(520.0f * u, sq, 40.0f * u);
-  const float hi = __builtin_fmaf(A, 1.0f + 80.0f * u, t);
-  const float lo = __builtin_fmaf(A, 1.0f - 80.0f * u, -t);
+  const float hi = __builtin_fmaf(A, 1.0f + 330.0f * u, 260.0f * u);
+  const float lo = __builtin_fmaf(A, 1.0f - 330.0f * u, -260.0f * u);
   return {__builtin_fmaf(D2, lo, -0x1p-136f), __builtin_fmaf(D2, hi, 0x1p-136f)};
 }
 
