@@ -356,11 +356,12 @@ __device__ __forceinline__ float fp16_error(const half2v (&y)[8], const uint32_t
 // |sum (x-c)^2 - D^2 S| <= D^2 (258u sqrt(S) + 0.001u) with S the exact sum
 // of (v - g)^2, and sqrt(S) <= (S + 1) / 2 makes that at most
 // D^2 (129u S + 129.001u).  A = S (1 +- 16.1u); the FP32 error is
-// sum (x-c)^2 (1 +- 18.1u), plus at most 2^-145 from underflow.  Together:
-// |err - D^2 A| <= D^2 (163.4u A + 129.1u) + 2^-145.  The coefficients below
-// (330u, 260u, 2^-136) are at least twice these, which also covers the three
-// roundings of this arithmetic, and the range of s keeps D^2 normal and every
-// error finite.
+// sum (x-c)^2 (1 +- 18.1u), plus at most 2^-145 from underflow, which is
+// below D^2 u / 8 because D >= 2^-9 s >= 2^-59 here.  Together:
+// |err - D^2 A| <= D^2 (163.4u A + 129.3u).  The coefficients below (330u,
+// 260u) are at least twice these, which also covers the three roundings of
+// this arithmetic, and the range of s keeps D^2 normal and every error
+// finite.
 struct ErrBounds {
   float lo, hi;
 };
@@ -369,7 +370,7 @@ __device__ __forceinline__ ErrBounds err_bounds(float A, float D) {
   const float D2 = D * D;
   const float hi = __builtin_fmaf(A, 1.0f + 330.0f * u, 260.0f * u);
   const float lo = __builtin_fmaf(A, 1.0f - 330.0f * u, -260.0f * u);
-  return {__builtin_fmaf(D2, lo, -0x1p-136f), __builtin_fmaf(D2, hi, 0x1p-136f)};
+  return {D2 * lo, D2 * hi};
 }
 
 // One element of a candidate by the portable definition: |x| r may be
