@@ -33,7 +33,8 @@
 //     E4M3 bytes, filled once per row instead of per block: the hardware
 //     reciprocal refined by one FMA residual step, which is the IEEE
 //     quotient for every divisor in [2^-126, 2^126] (rows with other
-//     divisors divide).
+//     divisors divide).  The same entry holds fl(fl(e s)^2) for the
+//     certified 4/6 comparison.
 //   v = fl(x r); q = E2M1(v) with the sign of x.
 //   c = fl(fl(g e) s): g e is exact in FP16 (<= 6 significant bits, between
 //     2^-10 and 2688), so the kernel multiplies in packed FP16 and rounds
@@ -242,9 +243,9 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
   return row_scale_s<FOS>(amax_over_c(__uint_as_float(amax_bits), FOS != 0));
 }
 
-// tab[byte] = 1 / fl(e(byte) s) for all 128 E4M3 bytes, lane l of the
-// wavefront writing bytes l and l + 64.
-__device__ __forceinline__ void fill_recip(float* tab, const RowScale& rs, int lane) {
+// tab[byte] = {1 / fl(e(byte) s), fl(e(byte) s)^2} for all 128 E4M3 bytes,
+// lane l of the wavefront writing bytes l and l + 64.
+__device__ __forceinline__ void fill_recip(float2v* tab, const RowScale& rs, int lane) {
   // For s in [2^-117, 2^116] every nonzero e*s (e from 2^-9 to 448) lies in
   // [2^-126, 2^126], where the refined hardware reciprocal is the IEEE
   // quotient; other rows divide.
@@ -253,7 +254,7 @@ __device__ __forceinline__ void fill_recip(float* tab, const RowScale& rs, int l
     const int byte = lane + 64 * h;
     const float d = e4m3_value<0>((uint32_t)byte) * rs.s;
     const float r = rs.rcp_normal ? recip_normal(d) : 1.0f / d;
-    tab[byte] = (d != 0.0f) ? r : 0.0f;
+    tab[byte] = (float2v){(d != 0.0f) ? r : 0.0f, d * d};
   }
 }
 
@@ -348,7 +349,8 @@ __device__ __forceinline__ float fp16_error(const half2v (&y)[8], const uint32_t
 }
 
 // Certified enclosure [lo, hi] of a candidate's FP32 error err (as the
-// definition computes it) from A and the decode step D = fl(e s), for rows
+// definition computes it) from A and D2 = fl(D^2), D = fl(e s) the decode
+// step, for rows
 // with 2^-50 <= s <= 2^40 and e != 0.  With u = 2^-24: v = x r and the
 // candidate value c carry relative rounding errors, so each x - c differs
 // from D (v - g) by at most D 2.01u (|v| + |g|) <= D 32.2u (|v| < 10,
@@ -365,9 +367,8 @@ __device__ __forceinline__ float fp16_error(const half2v (&y)[8], const uint32_t
 struct ErrBounds {
   float lo, hi;
 };
-__device__ __forceinline__ ErrBounds err_bounds(float A, float D) {
+__device__ __forceinline__ ErrBounds err_bounds(float A, float D2) {
   constexpr float u = 0x1p-24f;
-  const float D2 = D * D;
   const float hi = __builtin_fmaf(A, 1.0f + 330.0f * u, 260.0f * u);
   const float lo = __builtin_fmaf(A, 1.0f - 330.0f * u, -260.0f * u);
   return {D2 * lo, D2 * hi};
@@ -394,7 +395,7 @@ __device__ __forceinline__ uint32_t element_portable(float x, float e, float r, 
 // stays live across the hot path, so it costs the common case no registers.
 template <int FOS, bool DQ>
 __device__ __attribute__((noinline)) void tiny_row_block(const uint16_t* __restrict__ xb,
-                                                         float b, const float* tab, float s,
+                                                         float b, const float2v* tab, float s,
                                                          float inv_s,
                                                          uint8_t* __restrict__ code_bytes,
                                                          uint8_t* __restrict__ scale,
@@ -406,7 +407,7 @@ __device__ __attribute__((noinline)) void tiny_row_block(const uint16_t* __restr
     float e = 0.0f;
     uint32_t byte = 0u;
     if (b != 0.0f) byte = e4m3_encode(b / ((k == 0 ? 6.0f : 4.0f) * s), e);
-    const float r = tab[byte];
+    const float r = tab[byte].x;
     float err = 0.0f;
 #pragma unroll 1
     for (int i = 0; i < 16; ++i) {
@@ -456,7 +457,7 @@ struct BlockOut {
 
 template <int FOS, bool DQ>
 __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32_t bbits,
-                                                    const RowScale& rs, const float* tab,
+                                                    const RowScale& rs, const float2v* tab,
                                                     float neg_zero, BlockOut& out) {
   const float b = __uint_as_float(bbits);
   // bracketed block scales for both candidates (byte 0: map to 6, byte 1:
@@ -465,17 +466,16 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
   uint32_t eb = cvt_e4m3x2(b * rs.rks6_hi, FOS ? b * rs.rks4_hi : 0.0f);
   if (__builtin_expect(lo != eb, 0))
     eb = cvt_e4m3x2(fminf(b / rs.ks6, 448.0f), FOS ? fminf(b / rs.ks4, 448.0f) : 0.0f);
-  const float e6 = e4m3_value<0>(eb);
+  const float2v t6 = tab[eb & 0xFFu];  // {r, D^2} of the 6 candidate
   uint32_t code[2];
   float A6;
-  encode_candidate<FOS == 1>(x, tab[eb & 0xFFu], code, A6);
-  float e = e6;
+  encode_candidate<FOS == 1>(x, t6.x, code, A6);
   uint32_t ebyte = eb & 0xFFu;
   if (FOS) {
-    const float e4 = e4m3_value<1>(eb);
+    const float2v t4 = tab[eb >> 8];
     uint32_t code4[2];
     float A4;
-    encode_candidate<FOS == 1>(x, tab[eb >> 8], code4, A4);
+    encode_candidate<FOS == 1>(x, t4.x, code4, A4);
     bool four;
     if (FOS == 2) {
       half2v y[8];
@@ -484,35 +484,36 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
         y[p] = __builtin_convertvector((float2v){x[2 * p] * rs.inv_s, x[2 * p + 1] * rs.inv_s},
                                        half2v);
       });
-      four = fp16_error(y, code4, e4) < fp16_error(y, code, e6);  // ties keep 6
+      four = fp16_error(y, code4, e4m3_value<1>(eb)) <
+             fp16_error(y, code, e4m3_value<0>(eb));  // ties keep 6
     } else {
       // 4 wins only with a strictly lower error; both scales zero: the same
       // error, keep 6
       four = false;
       bool decided = eb == 0u;
-      if (rs.certify && e4 != 0.0f && e6 != 0.0f) {
-        const ErrBounds b6 = err_bounds(A6, e6 * rs.s), b4 = err_bounds(A4, e4 * rs.s);
+      if (rs.certify && (eb & 0xFFu) != 0u && (eb >> 8) != 0u) {  // both e nonzero
+        const ErrBounds b6 = err_bounds(A6, t6.y), b4 = err_bounds(A4, t4.y);
         four = b4.hi < b6.lo;
         decided = four || b4.lo >= b6.hi;
       }
       if (__builtin_expect(!decided, 0))
-        four = exact_error(x, code4, e4, rs.s, neg_zero) < exact_error(x, code, e6, rs.s, neg_zero);
+        four = exact_error(x, code4, e4m3_value<1>(eb), rs.s, neg_zero) <
+               exact_error(x, code, e4m3_value<0>(eb), rs.s, neg_zero);
     }
     code[0] = four ? code4[0] : code[0];
     code[1] = four ? code4[1] : code[1];
-    e = four ? e4 : e;
     ebyte = four ? (eb >> 8) : ebyte;
   }
   out.code0 = code[0];
   out.code1 = code[1];
   out.ebyte = ebyte;
-  if (DQ) dequant_block(code, e, rs.s, neg_zero, out.deq);
+  if (DQ) dequant_block(code, e4m3_value<0>(ebyte), rs.s, neg_zero, out.deq);
 }
 
 // One block, written directly (one lane, 32 contiguous dequant bytes).
 template <int FOS, bool DQ, bool NTC>
 __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bbits,
-                                               const RowScale& rs, const float* tab,
+                                               const RowScale& rs, const float2v* tab,
                                                float neg_zero, const uint4* __restrict__ xin,
                                                int64_t blk, uint2* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
@@ -658,10 +659,10 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
     float neg_zero, const float* __restrict__ gscale) {
   __shared__ uint32_t wave_max[kMaxWgWaves];
-  // dynamic LDS: the reciprocal table of each wave (W R x 128 floats), then
-  // the waves' tiles
+  // dynamic LDS: the reciprocal table of each wave (W R x 128 entries of
+  // two floats), then the waves' tiles
   extern __shared__ uint4 dyn_lds[];
-  float(*recip)[128] = (float(*)[128])dyn_lds;
+  float2v(*recip)[128] = (float2v(*)[128])dyn_lds;
   constexpr bool kLdsLoad = FP4Q_NV_LDS_LOAD;
   // per wave: the input tile (NB x 2 KiB) when loading through LDS, whose
   // half n, once read, stages the dequant values of block group n; else
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   constexpr int kWaveLds = kLdsLoad ? 128 * NB : 128;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint4* wave_lds = dyn_lds + 32 * W * R + kWaveLds * wave;
+  uint4* wave_lds = dyn_lds + 64 * W * R + kWaveLds * wave;
   // wave / W as a scalar multiply and shift: wdiv = ceil(2^16 / W) is exact
   // for every wave < 16 and W <= 16
   const int rw = (wave * wdiv) >> 16, chunk = wave - rw * W;  // wave-uniform
@@ -704,7 +705,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   const RowScale rs =
       gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
   if (chunk == 0 && lane == 0 && c.active && tscale != nullptr) tscale[c.row] = rs.s;
-  float* tab = recip[wave];
+  float2v* tab = recip[wave];
   fill_recip(tab, rs, lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
     float neg_zero, const float* __restrict__ gscale) {
-  __shared__ float recip[kLongWaves][128];
+  __shared__ float2v recip[kLongWaves][128];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = row0 + (int64_t)blockIdx.x * kLongWaves + wave;
@@ -1045,7 +1046,7 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
     // without it, 2 KiB of dequant staging
     const size_t wave_lds = FP4Q_NV_LDS_LOAD ? (size_t)NB * 128
                             : (FP4Q_NV_LDS_DQ && DQ) ? 128 : 0;
-    const size_t lds = (size_t)W * R * (128 * sizeof(float) + wave_lds * sizeof(uint4));
+    const size_t lds = (size_t)W * R * (128 * sizeof(float2v) + wave_lds * sizeof(uint4));
     for (int64_t row0 = 0; row0 < a.rows; row0 += max_rows) {
       const int64_t row_end = a.rows - row0 < max_rows ? a.rows : row0 + max_rows;
       const dim3 grid((unsigned)((row_end - row0 + R - 1) / R)), block(64 * W * R);
