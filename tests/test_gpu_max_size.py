@@ -5,7 +5,10 @@ beyond 32 bits.
 
 Rows are independent, so the oracle checks sampled rows bit for bit: the
 first and last, the rows around the 2^31-element boundary, the rows where
-the seeded pool below wraps, and seeded random rows.  Properties that hold
+the seeded pool below wraps, and seeded random rows -- for NVFP4 (4/6 and
+dequant), MXFP4-ResQ sparse and dense, the three reconstructions, and the
+global-scale call (whose oracle also gets the row holding the tensor max,
+found on the host from the pool, so that both use the same tensor scale).  Properties that hold
 at any size cover every element: the fused dequant equals the standalone
 dequantizer, and guided rounding toward the tensor's own codes under its
 own scales reproduces those codes (it is round-to-nearest then).
@@ -20,8 +23,9 @@ import pytest
 import torch
 
 import fp4_block_quantization_amd as fq
+import oracle
 import workloads
-from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_nvfp4
+from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +50,7 @@ def big():
         x[r0:r0 + r.numel()] = pool[r % POOL] * gain[:, None]
     del pool
     torch.cuda.synchronize()
-    yield x
+    yield x, pool_bits
     del x
     torch.cuda.empty_cache()
 
@@ -63,7 +67,7 @@ def host_rows(t, idx):
 
 
 def test_nvfp4_max_size_sampled_rows_and_dequant(big):
-    x = big
+    x = big[0]
     idx = sample_rows()
     print("max-size nvfp4_quantize 4/6 + dequant, rows", idx.tolist(), flush=True)
     codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=True, dequant=True)
@@ -88,7 +92,7 @@ def test_nvfp4_max_size_sampled_rows_and_dequant(big):
 
 
 def test_mx_max_size_sampled_rows(big):
-    x = big
+    x = big[0]
     idx = sample_rows()
     print("max-size mxfp4_resq_quantize, rows", idx.tolist(), flush=True)
     got = fq.mxfp4_resq_quantize(x)
@@ -96,3 +100,45 @@ def test_mx_max_size_sampled_rows(big):
     want = oracle_mx(bits_of(host_rows(x, idx)))
     for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
         assert_same(host(host_rows(g, idx)), w, "max-size mx " + n)
+
+
+def test_dense_reconstruct_and_global_max_size(big):
+    x, pool_bits = big
+    idx = sample_rows()
+    xs = bits_of(host_rows(x, idx))
+    print("max-size mxfp4_resq_dense_quantize and mxfp4_resq_reconstruct", flush=True)
+    sp = fq.mxfp4_resq_quantize(x)
+    de = fq.mxfp4_resq_dense_quantize(x)
+    torch.cuda.synchronize()
+    w_sp, w_de = oracle_mx(xs), oracle_mx_dense(xs)
+    for g, w, n in zip(de, w_de, ("codes", "scales", "res_codes", "res_scales")):
+        assert_same(host(host_rows(g, idx)), w, "max-size dense " + n)
+    out = torch.empty((ROWS, HIDDEN), dtype=torch.float32, device="cuda")
+    for mode, a, wa in ((0, (None, None, None), (None, None, None)),
+                        (1, sp[2:], w_sp[2:]),
+                        (2, (de[2], None, de[3]), (w_de[2], None, w_de[3]))):
+        src = sp if mode != 2 else de
+        fq.mxfp4_resq_reconstruct(src[0], src[1], *a, residual=mode, out=out)
+        torch.cuda.synchronize()
+        ws = w_sp if mode != 2 else w_de
+        want = oracle.mxfp4_resq_reconstruct(ws[0], ws[1], *wa, residual=mode)
+        assert_same(host(host_rows(out, idx)), want, "max-size reconstruct %d" % mode)
+    del out, sp, de
+    torch.cuda.empty_cache()
+
+    # the tensor max, from the pool and the row gains on the host: the
+    # oracle sees the sampled rows plus the row holding it, so its tensor
+    # scale is the whole tensor's
+    pool_amax = np.abs((pool_bits.astype(np.uint32) << 16).view(np.float32)).max(1)
+    r = np.arange(ROWS)
+    row_amax = pool_amax[r % POOL].astype(np.float64) * np.exp2((7 * r) % 17 - 8)
+    top = int(np.argmax(row_amax))
+    print("max-size nvfp4_quantize_global; tensor max in row %d" % top, flush=True)
+    got = fq.nvfp4_quantize_global(x, True, dequant=True)
+    torch.cuda.synchronize()
+    idx2 = np.unique(np.concatenate([idx, [top]]))
+    want = oracle.nvfp4_quantize_global(bits_of(host_rows(x, idx2)), True)
+    assert host(got[2]).view(np.uint32)[0] == want[2].view(np.uint32)[0], "tensor scale"
+    assert_same(host(host_rows(got[0], idx2)), want[0], "max-size global codes")
+    assert_same(host(host_rows(got[1], idx2)), want[1], "max-size global scales")
+    assert_same(bits_of(host_rows(got[3], idx2)), want[3], "max-size global dequant")
