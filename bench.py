@@ -736,7 +736,8 @@ def main():
         "config": {"workload": "moe_act: 8192x7168 BF16 MoE expert input activations, "
                                "Student-t(3) x per-token LogNormal(0,0.5); per-token NVFP4 "
                                "Four-Over-Six + BF16 dequant", "rows": rows, "hidden": hidden,
-                   "four_over_six": True, "dequant": True, "rotating_sets": args.sets},
+                   "four_over_six": True, "dequant": True, "rotating_sets": args.sets,
+                   "input_sha256": hashlib.sha256(x_bits.tobytes()).hexdigest()},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "elements_per_s": rows * hidden / (ms * 1e-3),
         "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
