@@ -66,6 +66,14 @@ def mx_bytes(rows, hidden):
 SPINUP_S = 0.2  # untimed back-to-back calls before the warm-up
 
 
+def rate(ms, nbytes):
+    """Time per call (ms) and algorithmic bytes -> µs, GB/s and the fraction
+    of the HBM peak."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def spin_up(fn, sets, seconds=SPINUP_S):
     """Back-to-back calls for `seconds` of wall time: after host-side work
     (workload generation, allocation) the GPU clocks have dropped, and the
@@ -565,7 +573,7 @@ def main():
         p, _ = time_calls(lambda d: fq.nvfp4_dequantize(d[0], d[1], d[2], out=d[3]), dsets, 200, 20)
         b = dequant_bytes(rows, hidden)
         secondary["nvfp4_dequantize moe_act 8192x7168"] = {
-            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+            **rate(p, b)}
         del dsets, c, s_, ts
         torch.cuda.empty_cache()
     if "resq" in parts:
@@ -577,7 +585,7 @@ def main():
                           list(range(4)), 200, 20)
         b = mx_bytes(*xr.shape)
         secondary["mxfp4_resq_quantize resq_act 8192x7168"] = {
-            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+            **rate(p, b)}
         del msets, mouts, xr
         torch.cuda.empty_cache()
     if "resq_dense" in parts:
@@ -591,7 +599,7 @@ def main():
         r_, h_ = xr.shape
         b = r_ * h_ * 2 + r_ * h_ // 2 * 2 + r_ * h_ // 32 * 2
         secondary["mxfp4_resq_dense_quantize resq_act 8192x7168"] = {
-            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+            **rate(p, b)}
         sp = fq.mxfp4_resq_quantize(xr)
         de = douts[0]
         xf = xr.float().double()
@@ -609,7 +617,7 @@ def main():
             sp[0], sp[1], sp[2], sp[3], sp[4], residual=1, out=xh), [0], 200, 20)
         b = r_ * h_ // 2 + r_ * h_ // 32 * 2 + r_ * h_ // 4 + r_ * h_ // 8 + r_ * h_ * 4
         secondary["mxfp4_resq_reconstruct (S2:4) resq_act 8192x7168"] = {
-            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+            **rate(p, b)}
         secondary["Rollout-ResQ reconstruction error resq_act"] = mse
         del msets, douts, sp, de, xf, xh, xr
         torch.cuda.empty_cache()
@@ -629,7 +637,7 @@ def main():
                                                               out=s_[1]), gsets, 500, 50)
         b = rows * hidden * 2 + rows * hidden // 2 * 2 + rows * hidden // 16 + rows * 4
         secondary["nvfp4_quantize_guided moe_act 8192x7168 (no dequant)"] = {
-            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+            **rate(p, b)}
 
         def nib(c):
             return torch.stack([c & 15, c >> 4], -1).reshape(c.shape[0], -1)
@@ -658,7 +666,7 @@ def main():
         p, _ = time_calls(lambda i: fq.nvfp4_quantize_global(gsets[i][0], True, out=outs[i]),
                           list(range(len(gsets))), 500, 50)
         secondary["nvfp4_quantize_global moe_act 8192x7168 (amax pass + quantize)"] = {
-            "us": round(p * 1e3, 2), "GBps": round(nbytes / (p * 1e-3) / 1e9, 1)}
+            **rate(p, nbytes)}
         del gsets, outs
         torch.cuda.empty_cache()
         full = fq.nvfp4_quantize_global(x, True, dequant=False)
@@ -685,7 +693,7 @@ def main():
                           gsets, 200, 20)
         b = nvfp4_bytes(*xg.shape, dequant=False, groups=offs.numel() - 1)
         secondary["nvfp4_quantize ragged_routed 65536x2048 (64 groups, no dequant)"] = {
-            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+            **rate(p, b)}
         del gsets, xg
         torch.cuda.empty_cache()
     if "weights" in parts:
@@ -695,7 +703,7 @@ def main():
         p, _ = time_calls(lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), wsets, 50, 5)
         b = nvfp4_bytes(*xw.shape)
         secondary["nvfp4_quantize expert_weights 65536x7168"] = {
-            "us": round(p * 1e3, 2), "GBps": round(b / (p * 1e-3) / 1e9, 1)}
+            **rate(p, b)}
         del wsets, xw
         torch.cuda.empty_cache()
     if "fp16" in parts:
@@ -704,7 +712,7 @@ def main():
         fsets = rotating_nvfp4_sets(x, args.sets)
         p, _ = time_calls(lambda s: fq.nvfp4_quantize(s[0], 2, out=s[1]), fsets, 1000, 100)
         secondary["nvfp4_quantize fp16-decision moe_act 8192x7168"] = {
-            "us": round(p * 1e3, 2), "GBps": round(nbytes / (p * 1e-3) / 1e9, 1)}
+            **rate(p, nbytes)}
         del fsets
         torch.cuda.empty_cache()
         agree = {}
