@@ -228,11 +228,12 @@ def mxfp4_resq_reconstruct(codes, scales, res_codes=None, res_meta=None, res_sca
 
 
 def nvfp4_quantize_guided(x_bits, guide_codes, block_scales, token_scales, dequant=True):
-    """TRACE rollout-guided rounding of x under the rollout's scales.
+    """TRACE rollout-guided rounding of x under the rollout's scales
+    (guide_codes None: round-to-nearest under those scales).
     Returns (codes u8 [R, H/2], dequant u16 [R, H] or None)."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     rows, hidden = x.shape
-    g = np.ascontiguousarray(guide_codes, dtype=np.uint8)
+    g = None if guide_codes is None else np.ascontiguousarray(guide_codes, dtype=np.uint8)
     bs = np.ascontiguousarray(block_scales, dtype=np.uint8)
     ts = np.ascontiguousarray(token_scales, dtype=np.float32)
     codes = np.zeros((rows, hidden // 2), np.uint8)

@@ -550,14 +550,19 @@ int mxfp4_resq_reconstruct_ref(const uint8_t* codes, const uint8_t* scales,
  *   when |sigma g(hi) - G| < |sigma g(lo) - G|, else lo.
  * The sign bit follows x, as in the quantizer; dequant (optional) is
  * BF16(+-((g * e) * s)).  Codes outside [off0, off1) of a ragged call are
- * not part of this entry point: every row is processed. */
+ * not part of this entry point: every row is processed.
+ *
+ * guide_codes NULL: the training side's own round-to-nearest under the same
+ * rollout-side scale, the rounding the page sets guided rounding against
+ * (its worked example and its count of mismatches on adjacent codewords):
+ * the code is E2M1(v), the quantizer's rounding of the same v. */
 int nvfp4_quantize_guided_ref(const uint16_t* x, int64_t rows, int64_t hidden,
                               const uint8_t* guide_codes, const uint8_t* block_scales,
                               const float* token_scales, uint8_t* codes,
                               uint16_t* dequant) {
   if (rows < 0 || hidden <= 0 || hidden % 16 != 0) return 2;
   if (rows == 0) return 0;
-  if (!x || !guide_codes || !block_scales || !token_scales || !codes) return 1;
+  if (!x || !block_scales || !token_scales || !codes) return 1;
   for (int64_t r = 0; r < rows; ++r) {
     float s = token_scales[r];
     for (int64_t i = 0; i < hidden; ++i) {
@@ -565,7 +570,7 @@ int nvfp4_quantize_guided_ref(const uint16_t* x, int64_t rows, int64_t hidden,
       float d = e * s;
       float xi = bf16_bits_to_float(x[r * hidden + i]);
       int neg = signbit(xi) ? 1 : 0;
-      int lo = 0, hi = 0;
+      int lo = 0, hi = 0, nearest = 0;
       if (d != 0.0f) {
         float rr = 1.0f / d;
         float v = fabsf(xi) * rr;
@@ -574,14 +579,19 @@ int nvfp4_quantize_guided_ref(const uint16_t* x, int64_t rows, int64_t hidden,
           if (oracle_e2m1_value(q) <= v) lo = q;
         hi = lo;
         if (oracle_e2m1_value(lo) < v && lo < 7) hi = lo + 1;
+        nearest = oracle_e2m1_code(v);
       }
-      uint8_t gb = guide_codes[r * (hidden / 2) + i / 2];
-      int gn = (i % 2) ? (gb >> 4) : (gb & 15);
-      double G = (gn & 8) ? -(double)oracle_e2m1_value(gn & 7) : (double)oracle_e2m1_value(gn & 7);
-      double sigma = neg ? -1.0 : 1.0;
-      double dlo = fabs(sigma * oracle_e2m1_value(lo) - G);
-      double dhi = fabs(sigma * oracle_e2m1_value(hi) - G);
-      int q = (dhi < dlo) ? hi : lo;
+      int q = nearest;
+      if (guide_codes) {
+        uint8_t gb = guide_codes[r * (hidden / 2) + i / 2];
+        int gn = (i % 2) ? (gb >> 4) : (gb & 15);
+        double G =
+            (gn & 8) ? -(double)oracle_e2m1_value(gn & 7) : (double)oracle_e2m1_value(gn & 7);
+        double sigma = neg ? -1.0 : 1.0;
+        double dlo = fabs(sigma * oracle_e2m1_value(lo) - G);
+        double dhi = fabs(sigma * oracle_e2m1_value(hi) - G);
+        q = (dhi < dlo) ? hi : lo;
+      }
       uint8_t nib = (uint8_t)((neg << 3) | q);
       uint8_t* cb = &codes[r * (hidden / 2) + i / 2];
       if (i % 2 == 0) *cb = (uint8_t)((*cb & 0xF0) | nib);

@@ -97,7 +97,8 @@ int nvfp4_quantize_global_ref(const uint16_t* x, int64_t rows, int64_t hidden,
                               int four_over_six, uint8_t* codes, uint8_t* block_scales,
                               float* tensor_scale, uint16_t* dequant);
 
-/* TRACE rollout-guided rounding under the rollout's scales. */
+/* TRACE rollout-guided rounding under the rollout's scales (guide_codes
+ * NULL: round-to-nearest under those scales). */
 int nvfp4_quantize_guided_ref(const uint16_t* x, int64_t rows, int64_t hidden,
                               const uint8_t* guide_codes, const uint8_t* block_scales,
                               const float* token_scales, uint8_t* codes,

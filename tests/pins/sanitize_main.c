@@ -78,6 +78,7 @@ static void run_shape(int64_t rows, int64_t hidden) {
     EXPECT(nvfp4_quantize_guided_ref(x, rows, hidden, codes, scales, ts, gcodes, back) == 0);
     for (int64_t i = 0; i < n / 2; ++i) gcodes[i] = (uint8_t)next();
     EXPECT(nvfp4_quantize_guided_ref(x, rows, hidden, gcodes, scales, ts, codes, NULL) == 0);
+    EXPECT(nvfp4_quantize_guided_ref(x, rows, hidden, NULL, scales, ts, codes, back) == 0);
     float s1;
     EXPECT(nvfp4_quantize_global_ref(x, rows, hidden, fos, codes, scales, &s1, dq) == 0);
   }

@@ -44,7 +44,8 @@ MUTANTS = {
     # bits below y's last place -- so dropping it is not an observable mistake)
     "fp16_target_not_rounded": ("double y = oracle_fp16_rne((double)scaled);",
                                 "double y = (double)scaled;"),
-    "guided_picks_farther": ("int q = (dhi < dlo) ? hi : lo;", "int q = (dhi > dlo) ? hi : lo;"),
+    "guided_picks_farther": ("q = (dhi < dlo) ? hi : lo;", "q = (dhi > dlo) ? hi : lo;"),
+    "unguided_truncates": ("nearest = oracle_e2m1_code(v);", "nearest = lo;"),
     "reconstruct_wrong_scale": ("rv = mx_value((i % 2) ? (rb >> 4) : (rb & 15), res_scales[blk]);",
                                 "rv = mx_value((i % 2) ? (rb >> 4) : (rb & 15), scales[blk]);"),
     "global_scale_constant": ("  float s = amax / (four_over_six ? 1536.0f : 2688.0f);\n  *tensor_scale = s;",

@@ -124,3 +124,58 @@ def test_guided_gap_never_larger_than_nearest():
     assert (gap_guided <= gap_rne).all()
     # and it closes most of the rounding flips
     assert (gap_guided > 0).sum() < (gap_rne > 0).sum()
+
+
+# ----------------------------------------------- no guide: round to nearest --
+# With no guide the call rounds each value to its nearest codeword under the
+# given (rollout-side) scales: the training side's plain rounding that the
+# TRACE page sets guided rounding against.
+
+def one_nearest(xv):
+    x = np.zeros((1, 16), np.uint16)
+    x[0, 0] = bf16(xv)
+    codes, _ = oracle.nvfp4_quantize_guided(x, None, np.full((1, 1), 0x38, np.uint8),
+                                            np.ones(1, np.float32))
+    return int(codes[0, 0] & 15)
+
+
+@pytest.mark.parametrize("name", sorted(cases()))
+def test_page_worked_example_round_to_nearest(name):
+    # the page's round-to-nearest outcomes: 2.49 -> 2 for training, 2.51 -> 3
+    # for the rollout (with s = e = 1, so v = |x|)
+    c = cases()[name]
+    assert one_nearest(c["training_x"]) == c["training_rne_code"]
+    assert one_nearest(c["rollout_x"]) == c["rollout_code"]
+
+
+@pytest.mark.parametrize("name,fos", [("moe_act", 1), ("tiny_ref", 1), ("tiny_ref", 0)])
+def test_nearest_under_own_scales_reproduces_the_quantizer(name, fos):
+    # the quantizer's codes are the round-to-nearest codes of the chosen
+    # candidate's scale, so rounding a tensor under its own stored scales
+    # gives back its codes and its dequant bit for bit
+    x = workloads.rows(name, 0, 48)
+    codes, scales, ts, dq = oracle.nvfp4_quantize(x, fos)
+    got, gdq = oracle.nvfp4_quantize_guided(x, None, scales, ts)
+    assert np.array_equal(got, codes)
+    assert np.array_equal(gdq, dq)
+
+
+def test_nearest_is_the_e2m1_rounding_of_v():
+    # under the rollout's scales, perturbed training values: each code is the
+    # pinned E2M1 rounding of v = |x| * fl(1/fl(e s)), with x's sign
+    rng = np.random.default_rng(5)
+    x = workloads.rows("moe_act", 0, 16)
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    _, scales, ts, _ = oracle.nvfp4_quantize(x, 1, dequant=False)
+    xt = workloads.to_bf16_bits(xf * (1 + rng.standard_normal(xf.shape).astype(np.float32)
+                                      * np.float32(2.0 ** -8)))
+    got, _ = oracle.nvfp4_quantize_guided(xt, None, scales, ts, dequant=False)
+    xtf, v, lo, hi = rne_and_neighbours(xt, scales, ts)
+    rne = np.array([[oracle.e2m1_code(float(a)) for a in row] for row in v.astype(np.float32)])
+    n = nibbles(got)
+    assert np.array_equal(n & 7, rne)
+    assert np.array_equal(n >> 3, np.signbit(xtf).astype(n.dtype))
+    # and the nearest code is one of the two neighbours, the nearer one
+    assert (((n & 7) == lo) | ((n & 7) == hi)).all()
+    dist = np.abs(GRID[n & 7] - v)
+    assert (dist <= np.minimum(np.abs(GRID[lo] - v), np.abs(GRID[hi] - v)) + 0.0).all()
