@@ -40,6 +40,30 @@ class Fp4qError(RuntimeError):
     pass
 
 
+# Bytes of device workspace nvfp4_quantize_global needs (fp4q.h)
+GLOBAL_WORKSPACE_BYTES = 1024
+
+
+def declare(L):
+    """Argument and result types of every C-ABI call on a loaded library
+    (libfp4q.so, or a build of the same sources with other knobs)."""
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.nvfp4_quantize.argtypes = [vp, i64, i64, vp, i64, ci, vp, vp, vp, vp, vp]
+    L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+    L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize_global.argtypes = [vp, i64, i64, ci, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize_guided.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.mxfp4_resq_dense_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    L.mxfp4_resq_reconstruct.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, vp, vp]
+    for name in ("nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
+                 "nvfp4_quantize_global", "nvfp4_quantize_guided", "mxfp4_resq_dense_quantize",
+                 "mxfp4_resq_reconstruct"):
+        getattr(L, name).restype = ci
+    L.fp4q_status_string.argtypes = [ci]
+    L.fp4q_status_string.restype = ctypes.c_char_p
+    return L
+
+
 def lib():
     """The loaded libfp4q.so (raises if it has not been built)."""
     global _lib
@@ -48,25 +72,7 @@ def lib():
             raise Fp4qError(
                 "libfp4q.so is not built (%s); run __graft_entry__.build() or "
                 "python fp4_block_quantization_amd/_build.py" % LIB_PATH)
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.nvfp4_quantize.argtypes = [vp, i64, i64, vp, i64, ci, vp, vp, vp, vp, vp]
-        L.nvfp4_quantize.restype = ci
-        L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
-        L.nvfp4_dequantize.restype = ci
-        L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
-        L.mxfp4_resq_quantize.restype = ci
-        L.nvfp4_quantize_global.argtypes = [vp, i64, i64, ci, vp, vp, vp, vp, vp]
-        L.nvfp4_quantize_global.restype = ci
-        L.nvfp4_quantize_guided.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
-        L.nvfp4_quantize_guided.restype = ci
-        L.mxfp4_resq_dense_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
-        L.mxfp4_resq_dense_quantize.restype = ci
-        L.mxfp4_resq_reconstruct.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, vp, vp]
-        L.mxfp4_resq_reconstruct.restype = ci
-        L.fp4q_status_string.argtypes = [ci]
-        L.fp4q_status_string.restype = ctypes.c_char_p
-        _lib = L
+        _lib = declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
 
@@ -251,16 +257,19 @@ def mxfp4_resq_reconstruct(codes, scales, res_codes=None, res_meta=None, res_sca
 
 def nvfp4_quantize_guided(x, guide_codes, block_scales, token_scales, dequant=True, out=None):
     """TRACE rollout-guided rounding of x (BF16 [rows, hidden]) under the
-    rollout's scales, toward the rollout's codes.  Returns (codes u8
-    [R, H/2], dequant bf16 [R, H] or None)."""
+    rollout's scales, toward the rollout's codes (guide_codes None: round to
+    nearest under those scales).  Returns (codes u8 [R, H/2], dequant bf16
+    [R, H] or None)."""
     _dev(x, "x", torch.bfloat16)
-    _dev(guide_codes, "guide_codes", torch.uint8)
+    if guide_codes is not None:
+        _dev(guide_codes, "guide_codes", torch.uint8)
     _dev(block_scales, "block_scales", torch.uint8)
     _dev(token_scales, "token_scales", torch.float32)
     if x.dim() != 2:
         raise Fp4qError("x must be 2-D [rows, hidden]")
     rows, hidden = x.shape
-    _sized(guide_codes, "guide_codes", torch.uint8, rows * (hidden // 2))
+    if guide_codes is not None:
+        _sized(guide_codes, "guide_codes", torch.uint8, rows * (hidden // 2))
     _sized(block_scales, "block_scales", torch.uint8, rows * (hidden // 16))
     _sized(token_scales, "token_scales", torch.float32, rows)
     if out is None:
@@ -278,9 +287,12 @@ def nvfp4_quantize_guided(x, guide_codes, block_scales, token_scales, dequant=Tr
     return codes, dq
 
 
-def nvfp4_quantize_global(x, four_over_six=True, dequant=True, out=None):
+def nvfp4_quantize_global(x, four_over_six=True, dequant=True, out=None, workspace=None):
     """NVFP4 with one FP32 scale for the whole tensor (the naive baseline).
-    Returns (codes, block_scales, tensor_scale f32 [1], dequant or None)."""
+    Returns (codes, block_scales, tensor_scale f32 [1], dequant or None).
+    workspace: optional uint8 GPU tensor of GLOBAL_WORKSPACE_BYTES (else one
+    is allocated), the partial maxima between the call's two kernels; calls
+    in flight at the same time must not share one."""
     _dev(x, "x", torch.bfloat16)
     if x.dim() != 2:
         raise Fp4qError("x must be 2-D [rows, hidden]")
@@ -297,8 +309,11 @@ def nvfp4_quantize_global(x, four_over_six=True, dequant=True, out=None):
         _sized(ts, "tensor_scale", torch.float32, 1)
         if dq is not None:
             _sized(dq, "dequant", torch.bfloat16, rows * hidden)
-    _same_device(x, codes, scales, ts, dq)
+    if workspace is None:
+        workspace = torch.empty(GLOBAL_WORKSPACE_BYTES, dtype=torch.uint8, device=x.device)
+    _sized(workspace, "workspace", torch.uint8, GLOBAL_WORKSPACE_BYTES)
+    _same_device(x, codes, scales, ts, dq, workspace)
     st = lib().nvfp4_quantize_global(_p(x), rows, hidden, _mode(four_over_six), _p(codes),
-                                     _p(scales), _p(ts), _p(dq), _stream(x))
+                                     _p(scales), _p(ts), _p(dq), _p(workspace), _stream(x))
     _check(st, "nvfp4_quantize_global")
     return codes, scales, ts, dq

@@ -17,9 +17,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libfp4q.so")
+# the same sources with the per-block arithmetic compiled out
+# (-DFP4Q_STANDIN=1): memory-pattern stand-ins, for measurement only
+STANDIN_PATH = os.path.join(BUILD_DIR, "libfp4q_standin.so")
+# K0, the HBM probes (copy, read-only, write-only)
+MEMBENCH_PATH = os.path.join(BUILD_DIR, "libfp4q_membench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["nvfp4.hip", "mxfp4_resq.hip", "fp4q_api.cpp"]
+MEMBENCH_SOURCES = ["membench.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -31,14 +37,16 @@ HIP_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=(), out_path: str = None) -> str:
-    """Compile every source and link libfp4q.so (or out_path, with
-    extra_flags such as -D launch knobs); returns the library path."""
+def build(verbose: bool = False, extra_flags=(), out_path: str = None, sources=None) -> str:
+    """Compile the sources (default: the quantizer's) and link libfp4q.so (or
+    out_path, with extra_flags such as -D build knobs); returns the library
+    path."""
     out_path = out_path or LIB_PATH
+    sources = sources or SOURCES
     obj_dir = os.path.join(os.path.dirname(out_path), "obj_" + os.path.basename(out_path))
     os.makedirs(obj_dir, exist_ok=True)
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmd = [HIPCC, *HIP_FLAGS, *extra_flags, *lang, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
@@ -56,5 +64,11 @@ def build(verbose: bool = False, extra_flags=(), out_path: str = None) -> str:
     return out_path
 
 
+def build_all(verbose: bool = False):
+    """libfp4q.so, the stand-in build and the K0 probes."""
+    return [build(verbose), build(verbose, ["-DFP4Q_STANDIN=1"], STANDIN_PATH),
+            build(verbose, out_path=MEMBENCH_PATH, sources=MEMBENCH_SOURCES)]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

@@ -118,8 +118,7 @@ fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
   fp4q_status st = check_shape(rows, hidden, 16);
   if (st != FP4Q_SUCCESS) return st;
   if (rows == 0) return FP4Q_SUCCESS;
-  if (!x || !guide_codes || !block_scales || !token_scales || !codes)
-    return FP4Q_ERROR_NULL_POINTER;
+  if (!x || !block_scales || !token_scales || !codes) return FP4Q_ERROR_NULL_POINTER;
   if (!aligned(x, 16) || !aligned(guide_codes, 4) || !aligned(codes, 4) ||
       !aligned(token_scales, 4) || (dequant && !aligned(dequant, 16)))
     return FP4Q_ERROR_MISALIGNED;
@@ -129,18 +128,21 @@ fp4q_status nvfp4_quantize_guided(const void* x, int64_t rows, int64_t hidden,
 
 fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
                                   int four_over_six, uint8_t* codes, uint8_t* block_scales,
-                                  float* tensor_scale, void* dequant, void* stream) {
+                                  float* tensor_scale, void* dequant, void* workspace,
+                                  void* stream) {
   fp4q_status st = check_shape(rows, hidden, 16);
   if (st != FP4Q_SUCCESS) return st;
   if (four_over_six < 0 || four_over_six > 2) return FP4Q_ERROR_INVALID_ARGUMENT;
   if (rows == 0) return FP4Q_SUCCESS;
-  if (!x || !codes || !block_scales || !tensor_scale) return FP4Q_ERROR_NULL_POINTER;
+  if (!x || !codes || !block_scales || !tensor_scale || !workspace)
+    return FP4Q_ERROR_NULL_POINTER;
   if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) ||
-      (dequant && !aligned(dequant, 16)))
+      !aligned(workspace, 16) || (dequant && !aligned(dequant, 16)))
     return FP4Q_ERROR_MISALIGNED;
   fp4q::NvQuantArgs a{x,     rows,         hidden,  nullptr, 0,
                       four_over_six, codes, block_scales, nullptr, dequant};
-  return launched(fp4q::nvfp4_quantize_global_launch(a, tensor_scale, (hipStream_t)stream));
+  return launched(
+      fp4q::nvfp4_quantize_global_launch(a, tensor_scale, workspace, (hipStream_t)stream));
 }
 
 const char* fp4q_status_string(fp4q_status status) {

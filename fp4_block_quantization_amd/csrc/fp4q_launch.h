@@ -2,8 +2,17 @@
 // Arguments reaching these have already been validated on the host.
 #pragma once
 
+// The memory-pattern stand-in build (-DFP4Q_STANDIN=1) puts everything in
+// its own namespace, so that its kernels carry names of their own in
+// profiles and cannot be mistaken for the quantizer's.
+#if defined(FP4Q_STANDIN) && FP4Q_STANDIN && !defined(fp4q)
+#define fp4q fp4q_standin
+#endif
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "fp4q.h"
 
 // Work-items per kernel launch at most; larger calls are split into several
 // launches over consecutive rows (or blocks).  The dispatch packet counts
@@ -25,12 +34,20 @@ struct NvQuantArgs {
   uint8_t* block_scales;
   float* token_scales;
   void* dequant;
-  const float* global_scale = nullptr;  // set: the token scale s of every row (one for the tensor)
+  // one scale for the whole tensor: the tensor-max pass's per-workgroup
+  // maxima (16-bit BF16 magnitude patterns, zero-padded; num_partials
+  // 16-byte units of them), from which every wave derives s, and where the
+  // first wave stores it
+  const uint4* global_partials = nullptr;
+  int num_partials = 0;
+  float* tensor_scale_out = nullptr;
 };
 
 hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t stream);
 hipError_t nvfp4_quantize_global_launch(const NvQuantArgs& a, float* tensor_scale,
-                                        hipStream_t stream);
+                                        void* workspace, hipStream_t stream);
+// Bytes of workspace that call uses for a tensor of rows x hidden.
+int64_t global_workspace_bytes(int64_t rows, int64_t hidden);
 hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,
                                    const float* token_scales, int64_t rows, int64_t hidden,
                                    void* out, hipStream_t stream);

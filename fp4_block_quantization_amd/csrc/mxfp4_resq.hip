@@ -139,6 +139,14 @@ __device__ __forceinline__ uint32_t select_2of4(uint32_t rw, const uint16_t* tab
 #endif
 constexpr int kUnitsPerLane = FP4Q_MX_UNITS;
 
+// Build-time knob: FP4Q_STANDIN = 1 builds a memory-pattern stand-in for
+// measurement only (libfp4q_standin.so, never the quantizer): the same
+// loads, 2:4 table copy, staging and stores, with each unit's quantization
+// and 2:4 selection replaced by XORs of its input words.
+#ifndef FP4Q_STANDIN
+#define FP4Q_STANDIN 0
+#endif
+
 __device__ __forceinline__ void resq_unit(const uint4 a, uint32_t& cw, uint32_t& rw, int& k,
                                           int& kr) {
   const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -248,14 +256,21 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
     if (64 * n < nv) {  // wave-uniform
       uint32_t cw, rw;
       int k, kr;
-      resq_unit(a[n], cw, rw, k, kr);
+      if (FP4Q_STANDIN) {
+        cw = a[n].x ^ a[n].z;
+        rw = a[n].y ^ a[n].w;
+        k = (int)(a[n].x >> 25) - 127;
+        kr = (int)(a[n].y >> 25) - 127;
+      } else {
+        resq_unit(a[n], cw, rw, k, kr);
+      }
       if (staged) {
         reinterpret_cast<uint32_t*>(sb)[j] = cw;
         if (DENSE) {
           reinterpret_cast<uint32_t*>(sb + 16 * SL::kResAt)[j] = rw;
         } else {
-          uint32_t meta;
-          const uint32_t rc = select_2of4(rw, tab, meta);
+          uint32_t meta = rw >> 24;
+          const uint32_t rc = FP4Q_STANDIN ? rw : select_2of4(rw, tab, meta);
           reinterpret_cast<uint16_t*>(sb + 16 * SL::kResAt)[j] = (uint16_t)rc;
           sb[16 * SL::kMetaAt + j] = (uint8_t)meta;
         }
@@ -268,8 +283,8 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
       if (DENSE) {
         if (j < nv) store_out(&(reinterpret_cast<uint32_t*>(res_codes) + ub)[j], rw);
       } else {
-        uint32_t meta;
-        const uint32_t rc = select_2of4(rw, tab, meta);
+        uint32_t meta = rw >> 24;
+        const uint32_t rc = FP4Q_STANDIN ? rw : select_2of4(rw, tab, meta);
         if (j < nv) {
           store_small(&(reinterpret_cast<uint16_t*>(res_codes) + ub)[j], (uint16_t)rc);
           store_small(&(res_meta + ub)[j], (uint8_t)meta);

@@ -99,6 +99,16 @@ namespace {
 #define FP4Q_NV_NB 2
 #endif
 
+// Build-time knob: FP4Q_STANDIN = 1 builds a memory-pattern stand-in of the
+// split kernel for measurement only (libfp4q_standin.so, never the
+// quantizer): the same loads, row amax, row constants, reciprocal tables
+// and stores, with each block's quantization replaced by a few XORs of its
+// input words, so its time is what this memory pattern costs without the
+// per-block arithmetic.
+#ifndef FP4Q_STANDIN
+#define FP4Q_STANDIN 0
+#endif
+
 constexpr int kMaxWgWaves = 16;  // rows of up to 16 waves use the split kernel
 constexpr int kLongWaves = 4;    // rows per workgroup of the long-row kernel
 
@@ -173,6 +183,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp<0x142, 0xA>(v));  // row_bcast:15
   v = max(v, dpp<0x143, 0xC>(v));  // row_bcast:31
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// The tensor-max pass's per-workgroup maxima, as 16-bit BF16 magnitude
+// patterns, zero-padded to whole 16-byte units: at most 512 of them, so one
+// 16-byte load per lane covers them all.  The load is issued before the
+// chunk's own loads, so its latency hides under theirs.
+__device__ __forceinline__ uint4 load_partials(const uint4* __restrict__ part, int n16,
+                                               int lane) {
+  return lane < n16 ? part[lane] : make_uint4(0u, 0u, 0u, 0u);
+}
+// The tensor amax as the bit pattern of a non-negative float.
+__device__ __forceinline__ uint32_t tensor_amax(uint4 p) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 m = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, p.x), __builtin_bit_cast(u16x2, p.y)),
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, p.z), __builtin_bit_cast(u16x2, p.w)));
+  return wave_max_u32((uint32_t)max(m.x, m.y) << 16);
 }
 
 __device__ __forceinline__ void unpack16(const uint32_t (&w)[8], float (&x)[16]) {
@@ -541,6 +568,26 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
   }
 }
 
+// The stand-in's block (FP4Q_STANDIN): the stores of quantize_block, with
+// codes, scale byte and dequant values taken from the input words.
+template <bool DQ, bool NTC>
+__device__ __forceinline__ void standin_block(const uint32_t (&w)[8], uint32_t bbits,
+                                              int64_t blk, uint2* __restrict__ codes,
+                                              uint8_t* __restrict__ scales,
+                                              uint4* __restrict__ dq, uint4* stage) {
+  store_codes<DQ, NTC>(&codes[blk], make_uint2(w[0] ^ w[2] ^ w[4] ^ w[6], w[1] ^ w[3] ^ w[5] ^ w[7]));
+  store_scale<DQ>(&scales[blk], (uint8_t)(bbits >> 24));
+  if (DQ) {
+    if (stage != nullptr) {
+      stage[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      stage[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      store_out(&dq[2 * blk], make_uint4(w[0], w[1], w[2], w[3]));
+      store_out(&dq[2 * blk + 1], make_uint4(w[4], w[5], w[6], w[7]));
+    }
+  }
+}
+
 // a < b for int64 values, from the signed high and unsigned low words, so
 // that wave-uniform operands are compared by the scalar unit
 __device__ __forceinline__ bool lt_i64(int64_t a, int64_t b) {
@@ -657,7 +704,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     int wdiv, int R, const int64_t* __restrict__ offs, int64_t ngroups,
     uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
-    float neg_zero, const float* __restrict__ gscale) {
+    float neg_zero, const uint4* __restrict__ gpart, int npart16,
+    float* __restrict__ gscale_out) {
   __shared__ uint32_t wave_max[kMaxWgWaves];
   // dynamic LDS: the reciprocal table of each wave (W R x 128 entries of
   // two floats), then the waves' tiles
@@ -677,6 +725,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
 
   const ChunkRef c =
       chunk_ref<NB>(blockIdx.x, rw, chunk, R, nblk, row0, row_end, rows, offs, ngroups);
+  uint4 gp = make_uint4(0u, 0u, 0u, 0u);
+  if (gpart != nullptr) gp = load_partials(gpart, npart16, lane);
   uint32_t w[NB][8];
   if (kLdsLoad)
     load_chunk_lds<NB>(x, c, lane, wave_lds, w);
@@ -693,18 +743,25 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // the row amax: a one-wave row has it already; otherwise the row's waves
   // combine theirs through LDS.  Every wave then derives the row constants
   // and fills its own reciprocal table, so the row needs no second
-  // workgroup barrier.
-  uint32_t amax_bits = wave_max_u32(lmax);
-  if (W > 1) {  // uniform over the workgroup
-    if (lane == 0) wave_max[wave] = amax_bits;
-    __syncthreads();
-    amax_bits = 0;
-    for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+  // workgroup barrier.  With gpart (one scale for the whole tensor) every
+  // wave reduces the tensor-max pass's partial maxima itself and the row
+  // needs no barrier at all.
+  uint32_t amax_bits;
+  if (gpart != nullptr) {  // uniform over the grid
+    amax_bits = tensor_amax(gp);
+  } else {
+    amax_bits = wave_max_u32(lmax);
+    if (W > 1) {  // uniform over the workgroup
+      if (lane == 0) wave_max[wave] = amax_bits;
+      __syncthreads();
+      amax_bits = 0;
+      for (int k = 0; k < W; ++k) amax_bits = max(amax_bits, wave_max[rw * W + k]);
+    }
   }
-  // with gscale, one token scale for the whole tensor
-  const RowScale rs =
-      gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(amax_bits);
+  const RowScale rs = row_scale<FOS>(amax_bits);
   if (chunk == 0 && lane == 0 && c.active && tscale != nullptr) tscale[c.row] = rs.s;
+  if (gscale_out != nullptr && row0 == 0 && blockIdx.x == 0 && wave == 0 && lane == 0)
+    *gscale_out = rs.s;
   float2v* tab = recip[wave];
   fill_recip(tab, rs, lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -717,10 +774,15 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     const int j = lane + 64 * n;
     uint4* dq_stage_n = wave_lds + (kLdsLoad ? 128 * n : 0);
     if (64 * n < c.valid && j < c.valid) {
-      float xv[16];
-      unpack16(w[n], xv);
-      quantize_block<FOS, DQ, NTC>(xv, bmax[n], rs, tab, neg_zero, x, c.cbase + j, codes,
-                                   scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr);
+      if (FP4Q_STANDIN) {
+        standin_block<DQ, NTC>(w[n], bmax[n], c.cbase + j, codes, scales, dq,
+                               stage ? &dq_stage_n[2 * lane] : nullptr);
+      } else {
+        float xv[16];
+        unpack16(w[n], xv);
+        quantize_block<FOS, DQ, NTC>(xv, bmax[n], rs, tab, neg_zero, x, c.cbase + j, codes,
+                                     scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr);
+      }
     }
     if (stage && 64 * n < c.valid) {
       // the group's dequant values leave as two contiguous KiB
@@ -745,7 +807,8 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     const uint4* __restrict__ x, int64_t rows, int64_t row0, int64_t row_end, int nblk,
     const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint4* __restrict__ dq,
-    float neg_zero, const float* __restrict__ gscale) {
+    float neg_zero, const uint4* __restrict__ gpart, int npart16,
+    float* __restrict__ gscale_out) {
   __shared__ float2v recip[kLongWaves][128];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -753,15 +816,22 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
   if (row >= row_end || !row_range(row, rows, offs, ngroups)) return;
   const int64_t base = row * nblk;
 
-  uint32_t lmax = 0;
-  for (int j = lane; j < nblk; j += 64) {
-    uint32_t w[8];
-    load_block(x, base + j, w);
-    lmax = max(lmax, block_absmax_bits(w));
+  uint32_t row_amax;
+  if (gpart != nullptr) {  // one scale for the whole tensor
+    row_amax = tensor_amax(load_partials(gpart, npart16, lane));
+  } else {
+    uint32_t lmax = 0;
+    for (int j = lane; j < nblk; j += 64) {
+      uint32_t w[8];
+      load_block(x, base + j, w);
+      lmax = max(lmax, block_absmax_bits(w));
+    }
+    row_amax = wave_max_u32(lmax);
   }
-  const uint32_t row_amax = wave_max_u32(lmax);
-  const RowScale rs = gscale != nullptr ? row_scale_s<FOS>(*gscale) : row_scale<FOS>(row_amax);
+  const RowScale rs = row_scale<FOS>(row_amax);
   if (lane == 0 && tscale != nullptr) tscale[row] = rs.s;
+  if (gscale_out != nullptr && row0 == 0 && blockIdx.x == 0 && wave == 0 && lane == 0)
+    *gscale_out = rs.s;
   fill_recip(recip[wave], rs, lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -848,7 +918,10 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
 // the same sign, or a zero guide, that is the upper neighbour exactly when
 // the guide's magnitude code is at least the upper one; a guide of the
 // other sign is nearer the lower neighbour.  One lane per 8-element unit,
-// mapped like the dequant kernel.
+// mapped like the dequant kernel.  RTN (no guide): each element takes its
+// nearest codeword under the same scales instead -- the training side's own
+// rounding that the page compares guided rounding with.
+template <bool RTN>
 __global__ __launch_bounds__(256) void nvfp4_guided_units(
     const uint4* __restrict__ x, const uint32_t* __restrict__ guide,
     const uint8_t* __restrict__ scales, const float* __restrict__ tscale, int64_t row0,
@@ -865,7 +938,7 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
   const int64_t base = row * h8 + first;
   const float s = tscale[row];
   const uint4* xin = x + base;
-  const uint32_t* gin = guide + base;
+  const uint32_t* gin = RTN ? nullptr : guide + base;
   const uint8_t* sin = scales + (base >> 1);
 #pragma unroll
   for (int n = 0; n < NU; ++n) {
@@ -879,7 +952,9 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
       a = xin[j];
     }
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t gwd = (FP4Q_GUIDED_NT_LOADS & 2) ? __builtin_nontemporal_load(&gin[j]) : gin[j];
+    uint32_t gwd = 0u;
+    if (!RTN)
+      gwd = (FP4Q_GUIDED_NT_LOADS & 2) ? __builtin_nontemporal_load(&gin[j]) : gin[j];
     const float e = e4m3_value<0>(sin[j >> 1]);
     const float d = e * s;
     float r;  // fl(1 / fl(e s)), the IEEE quotient
@@ -891,7 +966,18 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
     // the guide's magnitude code when the signs agree (else 0), clamped to
     // [lo, hi].
     uint32_t out = 0u;
-    if (__builtin_expect(r < __builtin_inff(), 1)) {
+    if (RTN && __builtin_expect(r < __builtin_inff(), 1)) {
+      // nearest codes of v = |x| r (+inf, from an overflowing product,
+      // saturates to code 7) with x's signs
+      uint32_t word = any_word();  // bytes 0-3 all written below
+      uint32_t sx = 0u;
+      static_for<0, 4>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        word = cvt_e2m1x2<p>(word, fabsf(bf16_lo(w[p])) * r, fabsf(bf16_hi(w[p])) * r);
+        sx |= (((w[p] >> 12) & 0x08u) | ((w[p] >> 24) & 0x80u)) << (8 * p);
+      });
+      out = word | sx;
+    } else if (!RTN && __builtin_expect(r < __builtin_inff(), 1)) {
       // r finite (v may still overflow to +inf, whose lower neighbour is
       // code 7): the lower neighbours of all eight elements from the
       // truncating conversion, the upper ones one code up where v is off the
@@ -930,13 +1016,20 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
       for (int i = 0; i < 8; ++i) {
         const float xi = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
         const float vi = fabsf(xi) * r;
-        const uint32_t lo = (vi >= 0.5f) + (vi >= 1.0f) + (vi >= 1.5f) + (vi >= 2.0f) +
-                            (vi >= 3.0f) + (vi >= 4.0f) + (vi >= 6.0f);
-        const uint32_t hi = (lo < 7u && e2m1_value(lo) < vi) ? lo + 1u : lo;
-        const uint32_t gn = (gwd >> (4 * i)) & 15u;
         const uint32_t sx = __float_as_uint(xi) >> 31;
-        const uint32_t m = (gn >> 3) == sx ? (gn & 7u) : 0u;
-        out |= ((sx << 3) | min(max(m, lo), hi)) << (4 * i);
+        uint32_t q;
+        if (RTN) {
+          float g;
+          q = e2m1_code_sw(vi, g);  // NaN (0 * inf) gives 0, +inf 7
+        } else {
+          const uint32_t lo = (vi >= 0.5f) + (vi >= 1.0f) + (vi >= 1.5f) + (vi >= 2.0f) +
+                              (vi >= 3.0f) + (vi >= 4.0f) + (vi >= 6.0f);
+          const uint32_t hi = (lo < 7u && e2m1_value(lo) < vi) ? lo + 1u : lo;
+          const uint32_t gn = (gwd >> (4 * i)) & 15u;
+          const uint32_t m = (gn >> 3) == sx ? (gn & 7u) : 0u;
+          q = min(max(m, lo), hi);
+        }
+        out |= ((sx << 3) | q) << (4 * i);
       }
     }
     store_out(&codes[base + j], out);
@@ -954,12 +1047,14 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
 }
 
 // One FP32 scale for the whole tensor: every workgroup of the max pass
-// writes the max of its share as a bit pattern (non-negative floats order
-// like their bits) to its own word of a partial array, one workgroup
-// reduces the partials and writes s = fl(amax / C) to the caller's scale,
-// and the blocks are quantized under it.  (With one atomic max per
-// workgroup on a single word instead, the atomics serialize and grow with
-// the grid.)
+// writes the max of its share -- the 16-bit pattern of a BF16 magnitude,
+// which orders like its value -- to its own slot of a partial array in the
+// caller's workspace; every wave of the quantize pass then reduces those
+// partials itself (one 16-byte load a lane, tensor_amax), derives
+// s = fl(amax / C) and quantizes its blocks under it, and the first wave
+// writes s to the caller's tensor scale.  (One atomic max per workgroup on a
+// single word instead serializes the atomics; a separate one-workgroup
+// reduction between the passes costs a dependent launch of about 4.6 us.)
 
 // Build-time knobs of the tensor max pass: workgroups (FP4Q_GAMAX_GRID),
 // 16-byte loads in flight per lane (FP4Q_GAMAX_DEPTH), non-temporal loads
@@ -967,6 +1062,10 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
 #ifndef FP4Q_GAMAX_GRID
 #define FP4Q_GAMAX_GRID 512
 #endif
+static_assert(FP4Q_GAMAX_GRID >= 1 && 2 * ((FP4Q_GAMAX_GRID + 7) / 8 * 8) <=
+                                          FP4Q_GLOBAL_WORKSPACE_BYTES &&
+                  (FP4Q_GAMAX_GRID + 7) / 8 <= 64,
+              "the padded partial maxima must fit the workspace and one 16-byte load a lane");
 #ifndef FP4Q_GAMAX_DEPTH
 #define FP4Q_GAMAX_DEPTH 4
 #endif
@@ -976,7 +1075,7 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
 
 __global__ __launch_bounds__(256) void global_amax_pass(const uint4* __restrict__ x,
                                                         int64_t n16,
-                                                        uint32_t* __restrict__ partial) {
+                                                        uint16_t* __restrict__ partial) {
   __shared__ uint32_t wmax[4];
   uint32_t m = 0u;
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -1011,23 +1110,22 @@ __global__ __launch_bounds__(256) void global_amax_pass(const uint4* __restrict_
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) partial[blockIdx.x] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-}
-
-template <int FOS>
-__global__ __launch_bounds__(256) void global_amax_reduce(const uint32_t* __restrict__ partial,
-                                                          int n, float* __restrict__ scale) {
-  __shared__ uint32_t wmax[4];
-  uint32_t m = 0u;
-  for (int i = threadIdx.x; i < n; i += 256) m = max(m, partial[i]);
-  m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
   if (threadIdx.x == 0)
-    *scale = __uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]))) /
-             (FOS ? 1536.0f : 2688.0f);
+    partial[blockIdx.x] = (uint16_t)(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) >> 16);
+  // zeros (the identity of the max) up to a whole 16-byte unit
+  const unsigned padded = (gridDim.x + 7u) & ~7u;
+  if (blockIdx.x == 0 && gridDim.x + threadIdx.x < padded) partial[gridDim.x + threadIdx.x] = 0;
 }
 
+// Rows (or row groups) per launch when one takes `items` work-items: as many
+// as the launch limit allows, and at least one, so that the row loop always
+// advances.  At the largest accepted hidden (2^30) one row is at most 2^26
+// work-items, far below the dispatch's 32-bit count, so the floor only
+// matters for builds with a tiny limit (a test build splits at 4096).
+__host__ inline int64_t rows_per_launch(int64_t items) {
+  const int64_t n = FP4Q_MAX_LAUNCH_ITEMS / items;
+  return n > 0 ? n : 1;
+}
 
 // NTC: see store_codes (the global-scale call's quantize pass).
 template <int FOS, bool DQ, bool NTC>
@@ -1041,7 +1139,7 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const int W = (nblk + 64 * NB - 1) / (64 * NB);  // waves per row
   if (W <= kMaxWgWaves) {
     const int R = W >= FP4Q_NV_WG_WAVES ? 1 : FP4Q_NV_WG_WAVES / W;  // rows per workgroup
-    const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * W * R) * R;  // rows per launch
+    const int64_t max_rows = rows_per_launch(64 * W * R) * R;         // rows per launch
     // per wave: its reciprocal table, then its input tile (NB x 2 KiB) or,
     // without it, 2 KiB of dequant staging
     const size_t wave_lds = FP4Q_NV_LDS_LOAD ? (size_t)NB * 128
@@ -1053,17 +1151,19 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((nvfp4_quantize_split<FOS, DQ, NB, NTC>), grid, block, lds, st, x,
                          a.rows, row0, row_end, nblk, W, (65536 + W - 1) / W, R, a.offsets,
                          a.num_groups, codes,
-                         a.block_scales, a.token_scales, dq, neg_zero, a.global_scale);
+                         a.block_scales, a.token_scales, dq, neg_zero, a.global_partials,
+                         a.num_partials, a.tensor_scale_out);
     }
   } else {
-    const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * kLongWaves) * kLongWaves;
+    const int64_t max_rows = rows_per_launch(64 * kLongWaves) * kLongWaves;
     for (int64_t row0 = 0; row0 < a.rows; row0 += max_rows) {
       const int64_t row_end = a.rows - row0 < max_rows ? a.rows : row0 + max_rows;
       const dim3 grid((unsigned)((row_end - row0 + kLongWaves - 1) / kLongWaves)),
           block(64 * kLongWaves);
       hipLaunchKernelGGL((nvfp4_quantize_long_rows<FOS, DQ, NTC>), grid, block, 0, st, x,
                          a.rows, row0, row_end, nblk, a.offsets, a.num_groups, codes,
-                         a.block_scales, a.token_scales, dq, neg_zero, a.global_scale);
+                         a.block_scales, a.token_scales, dq, neg_zero, a.global_partials,
+                         a.num_partials, a.tensor_scale_out);
     }
   }
   return hipGetLastError();
@@ -1071,25 +1171,31 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
 
 }  // namespace
 
+namespace {
+// Workgroups of the tensor-max pass for rows x hidden.
+int64_t global_amax_grid(int64_t rows, int64_t hidden) {
+  const int64_t n16 = rows * hidden / 8;  // 16-byte units
+  const int64_t grid = (n16 + 255) / 256;
+  return grid < FP4Q_GAMAX_GRID ? grid : FP4Q_GAMAX_GRID;
+}
+}  // namespace
+
+int64_t global_workspace_bytes(int64_t rows, int64_t hidden) {
+  return 2 * ((global_amax_grid(rows, hidden) + 7) / 8 * 8);
+}
+
 hipError_t nvfp4_quantize_global_launch(const NvQuantArgs& args, float* tensor_scale,
-                                        hipStream_t st) {
+                                        void* workspace, hipStream_t st) {
   NvQuantArgs a = args;
   const int64_t n16 = a.rows * a.hidden / 8;  // 16-byte units, >= 2
-  int64_t grid = (n16 + 255) / 256;
-  if (grid > FP4Q_GAMAX_GRID) grid = FP4Q_GAMAX_GRID;
-  // The partial maxima (4 bytes per workgroup) live in the codes output,
-  // which the quantize pass overwrites afterwards: it holds 4 n16 >= 4 grid
-  // bytes and is 8-byte aligned.
-  uint32_t* partial = reinterpret_cast<uint32_t*>(a.codes);
+  const int64_t grid = global_amax_grid(a.rows, a.hidden);
+  // grid 16-bit maxima, zero-padded to whole 16-byte units
+  uint16_t* partial = static_cast<uint16_t*>(workspace);
   hipLaunchKernelGGL(global_amax_pass, dim3((unsigned)grid), dim3(256), 0, st,
                      (const uint4*)a.x, n16, partial);
-  if (a.four_over_six)
-    hipLaunchKernelGGL(global_amax_reduce<1>, dim3(1), dim3(256), 0, st, partial, (int)grid,
-                       tensor_scale);
-  else
-    hipLaunchKernelGGL(global_amax_reduce<0>, dim3(1), dim3(256), 0, st, partial, (int)grid,
-                       tensor_scale);
-  a.global_scale = tensor_scale;
+  a.global_partials = reinterpret_cast<const uint4*>(partial);
+  a.num_partials = (int)((grid + 7) / 8);
+  a.tensor_scale_out = tensor_scale;
   a.token_scales = nullptr;
   return nvfp4_quantize_launch(a, st);
 }
@@ -1106,7 +1212,7 @@ hipError_t launch_mode(const NvQuantArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t nvfp4_quantize_launch(const NvQuantArgs& a, hipStream_t st) {
-  return a.global_scale != nullptr ? launch_mode<true>(a, st) : launch_mode<false>(a, st);
+  return a.global_partials != nullptr ? launch_mode<true>(a, st) : launch_mode<false>(a, st);
 }
 
 hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,
@@ -1115,7 +1221,7 @@ hipError_t nvfp4_dequantize_launch(const uint8_t* codes, const uint8_t* scales,
   const int h8 = (int)(hidden / 8);
   const int64_t per_wave = 64 * FP4Q_DQ_UNITS;
   const uint32_t wpr = (uint32_t)((h8 + per_wave - 1) / per_wave);  // waves per row
-  const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * (int64_t)wpr);
+  const int64_t max_rows = rows_per_launch(64 * (int64_t)wpr);
   for (int64_t row0 = 0; row0 < rows; row0 += max_rows) {
     const int64_t n = rows - row0 < max_rows ? rows - row0 : max_rows;
     const dim3 grid((unsigned)((n * wpr + 3) / 4)), block(256);
@@ -1131,13 +1237,18 @@ hipError_t nvfp4_guided_launch(const void* x, const uint8_t* guide, const uint8_
   const int h8 = (int)(hidden / 8);
   const int64_t per_wave = 64 * FP4Q_DQ_UNITS;
   const uint32_t wpr = (uint32_t)((h8 + per_wave - 1) / per_wave);  // waves per row
-  const int64_t max_rows = FP4Q_MAX_LAUNCH_ITEMS / (64 * (int64_t)wpr);
+  const int64_t max_rows = rows_per_launch(64 * (int64_t)wpr);
   for (int64_t row0 = 0; row0 < rows; row0 += max_rows) {
     const int64_t n = rows - row0 < max_rows ? rows - row0 : max_rows;
     const dim3 grid((unsigned)((n * wpr + 3) / 4)), block(256);
-    hipLaunchKernelGGL(nvfp4_guided_units, grid, block, 0, st, (const uint4*)x,
-                       (const uint32_t*)guide, scales, tscale, row0, row0 + n, h8, wpr,
-                       (uint32_t*)codes, (uint4*)dequant);
+    if (guide != nullptr)
+      hipLaunchKernelGGL(nvfp4_guided_units<false>, grid, block, 0, st, (const uint4*)x,
+                         (const uint32_t*)guide, scales, tscale, row0, row0 + n, h8, wpr,
+                         (uint32_t*)codes, (uint4*)dequant);
+    else
+      hipLaunchKernelGGL(nvfp4_guided_units<true>, grid, block, 0, st, (const uint4*)x,
+                         (const uint32_t*)nullptr, scales, tscale, row0, row0 + n, h8, wpr,
+                         (uint32_t*)codes, (uint4*)dequant);
   }
   return hipGetLastError();
 }

@@ -34,6 +34,11 @@
 /* The calls below are the library's only exported symbols. */
 #define FP4Q_API __attribute__((visibility("default")))
 
+/* Bytes of device workspace nvfp4_quantize_global needs, whatever the
+   tensor's size: one 2-byte partial maximum per workgroup of its tensor-max
+   pass, which has at most 512 workgroups. */
+#define FP4Q_GLOBAL_WORKSPACE_BYTES 1024
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -140,19 +145,24 @@ FP4Q_API fp4q_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block
  * under that s.  A row's outputs therefore depend on the other rows (the
  * batch dependency those pages warn about).
  *
+ * Two kernels: a tensor-max pass writes one partial maximum per workgroup
+ * into the workspace; the quantize pass reduces them in every wavefront,
+ * derives s and quantizes the blocks under it.
+ *
  *   x, codes, block_scales, dequant, four_over_six: as for nvfp4_quantize
  *                 (no ragged rows).
- *   tensor_scale  float [1], 4-byte aligned, device memory: receives s
- *                 before the blocks are quantized, which read it back.
- *   codes         also serves, before the blocks are quantized, as scratch
- *                 for the per-workgroup maxima of the tensor max (4 bytes
- *                 per workgroup, at most 512 workgroups and never more than
- *                 the codes hold).
- * Concurrent calls must not share tensor_scale or codes.
+ *   tensor_scale  float [1], 4-byte aligned, device memory: receives s.
+ *   workspace     device memory of FP4Q_GLOBAL_WORKSPACE_BYTES bytes,
+ *                 16-byte aligned, owned by the caller: holds the partial
+ *                 maxima between the two kernels.  Its contents on entry are
+ *                 ignored and on return unspecified; it must not overlap
+ *                 an input or output.
+ * Concurrent calls must not share tensor_scale or workspace.
  */
 FP4Q_API fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
                                   int four_over_six, uint8_t* codes, uint8_t* block_scales,
-                                  float* tensor_scale, void* dequant, void* stream);
+                                  float* tensor_scale, void* dequant, void* workspace,
+                                  void* stream);
 
 /*
  * nvfp4_quantize_guided -- TRACE rollout-guided rounding.
@@ -169,9 +179,14 @@ FP4Q_API fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t 
  *   with G the guide's signed value and sigma the sign of x_i, the code is
  *   hi if |sigma*g(hi) - G| < |sigma*g(lo) - G|, else lo; the sign bit
  *   follows x_i.  Guided by its own round-to-nearest codes it returns them.
+ *   With guide_codes NULL every element takes its nearest codeword,
+ *   E2M1_RNE(v), under the same scales: the training side's own rounding
+ *   that the page's worked example and its count of mismatches between
+ *   adjacent codewords set guided rounding against.
  *
  *   x             BF16 [rows, hidden] (training side), 16-byte aligned.
- *   guide_codes   uint8 [rows, hidden/2], 4-byte aligned: the rollout's codes.
+ *   guide_codes   uint8 [rows, hidden/2], 4-byte aligned: the rollout's
+ *                 codes; or NULL (round to nearest).
  *   block_scales  uint8 [rows, hidden/16], token_scales float [rows] (4-byte
  *                 aligned): the rollout's scales, read only.
  *   codes         uint8 [rows, hidden/2], 4-byte aligned: the guided codes.

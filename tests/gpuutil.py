@@ -73,3 +73,55 @@ def assert_same(got, want, name):
         raise AssertionError("%s: %d mismatches; first at row %d col %d: got %s want %s"
                              % (name, bad[0].size, r, c, hex(int(got.reshape(got.shape[0], -1)[r, c])),
                                 hex(int(want.reshape(want.shape[0], -1)[r, c]))))
+
+
+GUARD = 256      # bytes before and after every output
+GUARD_FILL = 0xA5
+
+
+class Guards:
+    """Output tensors placed inside 0xA5-filled uint8 allocations with GUARD
+    bytes on both sides (plus an optional extra offset in front), so that a
+    store past either end of an output is seen by check()."""
+
+    def __init__(self):
+        self._bufs = []
+
+    def empty(self, shape, dtype, offset=0):
+        shape = tuple(int(d) for d in shape)
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        buf = torch.full((n + 2 * GUARD + offset,), GUARD_FILL, dtype=torch.uint8, device="cuda")
+        o = GUARD + offset
+        self._bufs.append((buf, o, n))
+        return buf[o:o + n].view(dtype).view(shape)
+
+    def nvfp4(self, rows, hidden, dequant=True):
+        """(codes, block_scales, token_scales, dequant or None)."""
+        return (self.empty((rows, hidden // 2), torch.uint8),
+                self.empty((rows, hidden // 16), torch.uint8),
+                self.empty((rows,), torch.float32),
+                self.empty((rows, hidden), torch.bfloat16) if dequant else None)
+
+    def global_(self, rows, hidden, dequant=True):
+        """(codes, block_scales, tensor_scale, dequant or None), workspace."""
+        out = self.nvfp4(rows, hidden, dequant)
+        return (out[0], out[1], self.empty((1,), torch.float32), out[3]), \
+            self.empty((1024,), torch.uint8)
+
+    def mx(self, rows, hidden):
+        return tuple(self.empty((rows, hidden // k), torch.uint8) for k in (2, 32, 4, 8, 32))
+
+    def mx_dense(self, rows, hidden):
+        return tuple(self.empty((rows, hidden // k), torch.uint8) for k in (2, 32, 2, 32))
+
+    def guided(self, rows, hidden, dequant=True):
+        return (self.empty((rows, hidden // 2), torch.uint8),
+                self.empty((rows, hidden), torch.bfloat16) if dequant else None)
+
+    def check(self, label=""):
+        torch.cuda.synchronize()
+        for buf, o, n in self._bufs:
+            lo_ok = bool((buf[:o] == GUARD_FILL).all())
+            hi_ok = bool((buf[o + n:] == GUARD_FILL).all())
+            assert lo_ok and hi_ok, "%s: a guard byte around a %d-byte output was written (%s)" % (
+                label, n, "before" if not lo_ok else "after")

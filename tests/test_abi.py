@@ -9,24 +9,32 @@ import re
 import pytest
 
 import fp4_block_quantization_amd as fq
+from fp4_block_quantization_amd import _build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 SUCCESS, NULL, SHAPE, MISALIGNED, LAUNCH, INVALID = 0, 1, 2, 3, 4, 5
 
 
-def declared_functions():
-    names = []
-    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
-        src = open(h).read()
-        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names += re.findall(r"^\s*(?:FP4Q_API\s+)?(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
-                            r"([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
+def declared_functions(header):
+    src = open(os.path.join(ROOT, "include", header)).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:FP4Q_API\s+)?(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
+                       r"([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
+# each header under include/ and the library that exports its calls
+HEADER_LIBS = {"fp4q.h": _build.LIB_PATH, "fp4q_membench.h": _build.MEMBENCH_PATH}
+
+
+def test_every_header_has_its_library():
+    assert sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h"))) \
+        == sorted(HEADER_LIBS)
+
+
 def test_library_exports_every_declared_call():
-    names = declared_functions()
+    names = declared_functions("fp4q.h")
     assert len(names) == 8, names
     assert {"nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
             "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "nvfp4_quantize_guided",
@@ -35,6 +43,34 @@ def test_library_exports_every_declared_call():
     L = fq.lib()
     for n in names:
         assert hasattr(L, n), n
+    # the stand-in build of the same sources exports the same calls
+    S = ctypes.CDLL(_build.STANDIN_PATH)
+    for n in names:
+        assert hasattr(S, n), n
+
+
+def test_membench_library_exports_and_rejects():
+    names = declared_functions("fp4q_membench.h")
+    assert names == ["fp4q_k0_copy", "fp4q_k0_copy_stream", "fp4q_k0_read", "fp4q_k0_write"], names
+    M = ctypes.CDLL(_build.MEMBENCH_PATH)
+    P, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    M.fp4q_k0_copy.argtypes = [P, P, i64, ci, P]
+    M.fp4q_k0_read.argtypes = [P, i64, ci, ci, P, P]
+    M.fp4q_k0_write.argtypes = [P, i64, ci, P]
+    M.fp4q_k0_copy_stream.argtypes = [P, P, i64, ci, ci, P]
+    a16 = P(0x10000)
+    assert M.fp4q_k0_copy_stream(a16, a16, 32, 1, 0, None) == INVALID
+    assert M.fp4q_k0_copy_stream(a16, a16, 24, 1, 8, None) == SHAPE
+    assert M.fp4q_k0_copy(a16, a16, 24, 1, None) == SHAPE
+    assert M.fp4q_k0_copy(None, a16, 32, 1, None) == NULL
+    assert M.fp4q_k0_copy(P(0x10008), a16, 32, 1, None) == MISALIGNED
+    assert M.fp4q_k0_copy(None, None, 0, 1, None) == SUCCESS
+    assert M.fp4q_k0_read(a16, 64, 3, 0, a16, None) == INVALID
+    assert M.fp4q_k0_read(a16, 6, 4, 0, a16, None) == SHAPE
+    assert M.fp4q_k0_read(a16, 64, 4, 0, None, None) == NULL
+    assert M.fp4q_k0_read(P(0x10002), 64, 4, 0, a16, None) == MISALIGNED
+    assert M.fp4q_k0_write(a16, -16, 1, None) == SHAPE
+    assert M.fp4q_k0_write(None, 16, 1, None) == NULL
 
 
 def test_status_strings():
@@ -135,8 +171,11 @@ def test_nvfp4_quantize_guided_rejects():
         k.get("ts", A16), k.get("codes", A16), k.get("dq", A16), None)
     assert g(hidden=24) == SHAPE
     assert g(x=None) == NULL
-    assert g(guide=None) == NULL
     assert g(codes=None) == NULL
+    # no guide is a valid call (round to nearest); it is still checked in
+    # full before anything is launched
+    assert g(guide=None, codes=None) == NULL
+    assert g(guide=None, x=A8) == MISALIGNED
     assert g(x=A8) == MISALIGNED
     assert g(guide=P(0x10002)) == MISALIGNED
     assert g(dq=A8) == MISALIGNED
@@ -147,11 +186,14 @@ def test_nvfp4_quantize_global_rejects():
     L = fq.lib()
     g = lambda **k: L.nvfp4_quantize_global(
         k.get("x", A16), k.get("rows", 4), k.get("hidden", 64), k.get("fos", 1),
-        k.get("codes", A16), A16, k.get("ts", A16), k.get("dq", A16), None)
+        k.get("codes", A16), A16, k.get("ts", A16), k.get("dq", A16), k.get("ws", A16), None)
     assert g(hidden=24) == SHAPE
+    assert g(ws=None) == NULL
+    assert g(ws=P(0x10002)) == MISALIGNED
+    assert g(ws=P(0x10008)) == MISALIGNED  # 16-byte alignment
     assert g(fos=3) == INVALID
     assert g(x=None) == NULL
     assert g(ts=None) == NULL
     assert g(ts=P(0x10002)) == MISALIGNED
     assert g(dq=A8) == MISALIGNED
-    assert g(rows=0, x=None, codes=None, ts=None) == SUCCESS
+    assert g(rows=0, x=None, codes=None, ts=None, ws=None) == SUCCESS

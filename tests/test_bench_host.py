@@ -55,3 +55,48 @@ def test_more_than_one_gpu_exits_with_a_message():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_more_byte_counts():
+    n = 8192 * 7168
+    # dense residual: primary and residual codes (1/2 B each), two E8M0
+    assert bench.mx_dense_bytes(8192, 7168) == n * 2 + n + n // 16
+    # S2:4 reconstruction reads 1/2 + 1/32 + 1/4 + 1/8 + 1/32 B, writes 4 B
+    assert bench.reconstruct_bytes(8192, 7168) == n * (0.5 + 1 / 32 + 0.25 + 0.125 + 1 / 32 + 4)
+    # guided: x, guide codes, scales, token scales in; codes out
+    assert bench.guided_bytes(8192, 7168) == n * (2 + 0.5 + 1 / 16 + 0.5) + 8192 * 4
+    assert bench.guided_bytes(8192, 7168, guide=False) == n * (2 + 1 / 16 + 0.5) + 8192 * 4
+
+
+def test_rotating_sets_span_a_gib():
+    for per_set in (bench.nvfp4_bytes(8192, 7168), bench.nvfp4_bytes(256, 2048),
+                    bench.mx_bytes(8192, 7168), bench.reconstruct_bytes(8192, 7168),
+                    bench.nvfp4_bytes(65536, 2048, dequant=False, groups=64)):
+        k = bench.n_sets(per_set)
+        assert k >= 4 and k * per_set >= 1 << 30, (per_set, k)
+
+
+def test_dispatch_labels():
+    lab = bench._label
+    q = "fp4q::(anonymous namespace)::nvfp4_quantize_split<%s>(HIP_vector_type<unsigned int, 4u> const*)"
+    assert lab(q % "1, true, 2, false", 8192 * 256) == bench.HEADLINE_KEY
+    assert lab(q % "1, true, 2, true", 8192 * 256).startswith("nvfp4_quantize_global")
+    assert lab(q.replace("fp4q::", "fp4q_standin::") % "1, true, 2, false",
+               8192 * 256).startswith("stand-in")
+    assert lab(q % "1, false, 2, false", 65536 * 64).endswith("ragged_routed 65536x2048")
+    k0 = "void (anonymous namespace)::k0_read<%s, %s>(x)"
+    assert lab(k0 % ("unsigned char", "false"), 1) == "K0 read 1B 256 MiB"
+    assert lab(k0 % ("unsigned short", "false"), 1) == "K0 read 2B 256 MiB"
+    assert lab(k0 % ("unsigned int", "false"), 1) == "K0 read 4B 256 MiB"
+    assert lab(k0 % ("unsigned int __vector(2)", "false"), 1) == "K0 read 8B 256 MiB"
+    assert lab(k0 % ("unsigned int __vector(4)", "true"), 1) == "K0 read 16B nt 256 MiB"
+    assert lab("(anonymous namespace)::k0_copy<true>(x)", 1) == bench.COPY_CAL_KEY
+    # every labelled kernel has algorithmic bytes
+    algo = bench.algorithmic_rw()
+    assert bench.HEADLINE_KEY in algo and bench.COPY_CAL_KEY in algo
+
+
+def test_host_cpu_description():
+    d = bench.host_cpu()
+    assert d["cpus_usable_by_this_process"] >= 1 and d["host_logical_cpus"] >= 1
+    assert isinstance(d["cpu_model"], str)

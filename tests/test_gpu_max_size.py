@@ -25,7 +25,7 @@ import torch
 import fp4_block_quantization_amd as fq
 import oracle
 import workloads
-from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4
+from gpuutil import Guards, assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4
 
 pytestmark = pytest.mark.gpu
 
@@ -70,8 +70,10 @@ def test_nvfp4_max_size_sampled_rows_and_dequant(big):
     x = big[0]
     idx = sample_rows()
     print("max-size nvfp4_quantize 4/6 + dequant, rows", idx.tolist(), flush=True)
-    codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=True, dequant=True)
-    torch.cuda.synchronize()
+    gu = Guards()
+    codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=True, dequant=True,
+                                              out=gu.nvfp4(ROWS, HIDDEN))
+    gu.check("max-size nvfp4")
     x_bits = bits_of(host_rows(x, idx))
     want = oracle_nvfp4(x_bits, True, dequant=True)
     assert_same(host(host_rows(codes, idx)), want[0], "max-size codes")
@@ -80,14 +82,15 @@ def test_nvfp4_max_size_sampled_rows_and_dequant(big):
     assert_same(bits_of(host_rows(dq, idx)), want[3], "max-size dequant")
 
     print("max-size nvfp4_dequantize over every element", flush=True)
-    back = fq.nvfp4_dequantize(codes, scales, ts)
-    torch.cuda.synchronize()
+    back = fq.nvfp4_dequantize(codes, scales, ts, out=gu.empty((ROWS, HIDDEN), torch.bfloat16))
+    gu.check("max-size dequant")
     assert torch.equal(back.view(torch.int16), dq.view(torch.int16))
     del back, dq
 
     print("max-size nvfp4_quantize_guided toward its own codes", flush=True)
-    gcodes, _ = fq.nvfp4_quantize_guided(x, codes, scales, ts, dequant=False)
-    torch.cuda.synchronize()
+    gcodes, _ = fq.nvfp4_quantize_guided(x, codes, scales, ts, dequant=False,
+                                         out=gu.guided(ROWS, HIDDEN, dequant=False))
+    gu.check("max-size guided")
     assert torch.equal(gcodes, codes)
 
 
@@ -95,8 +98,9 @@ def test_mx_max_size_sampled_rows(big):
     x = big[0]
     idx = sample_rows()
     print("max-size mxfp4_resq_quantize, rows", idx.tolist(), flush=True)
-    got = fq.mxfp4_resq_quantize(x)
-    torch.cuda.synchronize()
+    gu = Guards()
+    got = fq.mxfp4_resq_quantize(x, out=gu.mx(ROWS, HIDDEN))
+    gu.check("max-size mx")
     want = oracle_mx(bits_of(host_rows(x, idx)))
     for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
         assert_same(host(host_rows(g, idx)), w, "max-size mx " + n)
@@ -107,23 +111,24 @@ def test_dense_reconstruct_and_global_max_size(big):
     idx = sample_rows()
     xs = bits_of(host_rows(x, idx))
     print("max-size mxfp4_resq_dense_quantize and mxfp4_resq_reconstruct", flush=True)
+    gu = Guards()
     sp = fq.mxfp4_resq_quantize(x)
-    de = fq.mxfp4_resq_dense_quantize(x)
-    torch.cuda.synchronize()
+    de = fq.mxfp4_resq_dense_quantize(x, out=gu.mx_dense(ROWS, HIDDEN))
+    gu.check("max-size dense")
     w_sp, w_de = oracle_mx(xs), oracle_mx_dense(xs)
     for g, w, n in zip(de, w_de, ("codes", "scales", "res_codes", "res_scales")):
         assert_same(host(host_rows(g, idx)), w, "max-size dense " + n)
-    out = torch.empty((ROWS, HIDDEN), dtype=torch.float32, device="cuda")
+    out = gu.empty((ROWS, HIDDEN), torch.float32)
     for mode, a, wa in ((0, (None, None, None), (None, None, None)),
                         (1, sp[2:], w_sp[2:]),
                         (2, (de[2], None, de[3]), (w_de[2], None, w_de[3]))):
         src = sp if mode != 2 else de
         fq.mxfp4_resq_reconstruct(src[0], src[1], *a, residual=mode, out=out)
-        torch.cuda.synchronize()
+        gu.check("max-size reconstruct %d" % mode)
         ws = w_sp if mode != 2 else w_de
         want = oracle.mxfp4_resq_reconstruct(ws[0], ws[1], *wa, residual=mode)
         assert_same(host(host_rows(out, idx)), want, "max-size reconstruct %d" % mode)
-    del out, sp, de
+    del out, sp, de, g
     torch.cuda.empty_cache()
 
     # the tensor max, from the pool and the row gains on the host: the
@@ -134,8 +139,10 @@ def test_dense_reconstruct_and_global_max_size(big):
     row_amax = pool_amax[r % POOL].astype(np.float64) * np.exp2((7 * r) % 17 - 8)
     top = int(np.argmax(row_amax))
     print("max-size nvfp4_quantize_global; tensor max in row %d" % top, flush=True)
-    got = fq.nvfp4_quantize_global(x, True, dequant=True)
-    torch.cuda.synchronize()
+    gu = Guards()
+    out, ws = gu.global_(ROWS, HIDDEN)
+    got = fq.nvfp4_quantize_global(x, True, dequant=True, out=out, workspace=ws)
+    gu.check("max-size global")
     idx2 = np.unique(np.concatenate([idx, [top]]))
     want = oracle.nvfp4_quantize_global(bits_of(host_rows(x, idx2)), True)
     assert host(got[2]).view(np.uint32)[0] == want[2].view(np.uint32)[0], "tensor scale"

@@ -5,7 +5,8 @@ Covers the five named workloads at their full sizes (the oracle runs over
 row chunks in threads), an edge suite over row lengths that span several
 tiles with ragged tails and the long-row path, the hand-worked golden
 blocks, ragged group ranges, the standalone dequantizer, determinism and
-argument errors."""
+argument errors.  Every output is written inside 256 guard bytes on both
+sides (gpuutil.Guards), which must be left untouched."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +15,8 @@ import fp4_block_quantization_amd as fq
 import oracle
 import workloads
 from goldens import load
-from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4, to_dev
+from gpuutil import (Guards, assert_same, bits_of, host, oracle_mx, oracle_mx_dense,
+                     oracle_nvfp4, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +35,10 @@ def f32_to_bf16_bits(a):
 
 def check_nvfp4(x_bits, fos, dequant=True, label=""):
     x = to_dev(x_bits)
-    codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=fos, dequant=dequant)
-    torch.cuda.synchronize()
+    gu = Guards()
+    codes, scales, ts, dq = fq.nvfp4_quantize(x, four_over_six=fos, dequant=dequant,
+                                              out=gu.nvfp4(*x_bits.shape, dequant))
+    gu.check(label)
     want = oracle_nvfp4(x_bits, fos, dequant=dequant)
     assert_same(host(codes), want[0], label + " codes")
     assert_same(host(scales), want[1], label + " block_scales")
@@ -46,16 +50,18 @@ def check_nvfp4(x_bits, fos, dequant=True, label=""):
 
 def check_mx(x_bits, label="", dense_and_reconstruct=True):
     x = to_dev(x_bits)
-    got = fq.mxfp4_resq_quantize(x)
-    torch.cuda.synchronize()
+    R, H = x_bits.shape
+    gu = Guards()
+    got = fq.mxfp4_resq_quantize(x, out=gu.mx(R, H))
+    gu.check(label)
     want = oracle_mx(x_bits)
     for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
         assert_same(host(g), w, label + " " + n)
     if not dense_and_reconstruct:
         return
     # Rollout-ResQ-Dense
-    gd = fq.mxfp4_resq_dense_quantize(x)
-    torch.cuda.synchronize()
+    gd = fq.mxfp4_resq_dense_quantize(x, out=gu.mx_dense(R, H))
+    gu.check(label + " dense")
     wd = oracle_mx_dense(x_bits)
     for g, w, n in zip(gd, wd, ("codes", "scales", "res_codes", "res_scales")):
         assert_same(host(g), w, label + " dense " + n)
@@ -64,8 +70,9 @@ def check_mx(x_bits, label="", dense_and_reconstruct=True):
     for mode, args, wargs in ((0, (None, None, None), (None, None, None)),
                               (1, (rc, rm, rs), (want[2], want[3], want[4])),
                               (2, (gd[2], None, gd[3]), (wd[2], None, wd[3]))):
-        xh = fq.mxfp4_resq_reconstruct(c, s, *args, residual=mode)
-        torch.cuda.synchronize()
+        xh = fq.mxfp4_resq_reconstruct(c, s, *args, residual=mode,
+                                       out=gu.empty((R, H), torch.float32))
+        gu.check(label + " reconstruct")
         wh = oracle.mxfp4_resq_reconstruct(want[0], want[1], *wargs, residual=mode)
         assert_same(host(xh), wh, label + " reconstruct residual=%d" % mode)
 
@@ -103,7 +110,11 @@ def edge_rows(H, seed):
     return np.stack(bits, 0)
 
 
-HIDDEN = [16, 32, 48, 1008, 1024, 1040, 2048, 2064, 7168, 8192, 8208, 16400, 32784]
+# row lengths: one block; a few; around one and several waves (2048 elements
+# a wave); 10, 14 and 16 waves a row (the widest split rows, with 1024-thread
+# workgroups and up to 80 KiB of LDS); past 16 waves (the long-row kernel)
+HIDDEN = [16, 32, 48, 1008, 1024, 1040, 2048, 2064, 7168, 8192, 8208, 16400, 20480, 26640,
+          32768, 32784]
 
 
 @pytest.mark.parametrize("fos", [1, 0, 2])
@@ -160,26 +171,43 @@ def test_ragged_routed_full_size():
     x_bits = workloads.rows("ragged_routed")
     offs = workloads.group_offsets()
     x = to_dev(x_bits)
+    gu = Guards()
     codes, scales, ts, _ = fq.nvfp4_quantize(x, True, offsets=torch.from_numpy(offs).cuda(),
-                                             dequant=False)
-    torch.cuda.synchronize()
+                                             dequant=False, out=gu.nvfp4(*x_bits.shape, False))
+    gu.check("ragged")
     want = oracle_nvfp4(x_bits, True, dequant=False)
     assert_same(host(codes), want[0], "ragged codes")
     assert_same(host(scales), want[1], "ragged scales")
     assert_same(host(ts)[:, None], want[2][:, None], "ragged token_scales")
 
 
-def test_ragged_subrange_leaves_other_rows():
-    x_bits = workloads.rows("ragged_routed", 0, 8192)
-    sub = workloads.group_offsets()[2:6].copy()  # groups 2..4 of the routed rows
+def sentinel_outputs(gu, R, H):
+    """Guarded nvfp4 outputs filled with sentinels (rows outside a ragged
+    range must keep them)."""
+    out = gu.nvfp4(R, H)
+    for t, f in zip(out, (0xAB, 0xCD, -7.0, 1.5)):
+        t.fill_(f)
+    return out
+
+
+@pytest.mark.parametrize("H,rows,cut", [(2048, 8192, None), (32768, 50, (3, 17, 17, 40))])
+def test_ragged_subrange_leaves_other_rows(H, rows, cut):
+    # routed rows of 2048 (groups 2..4 of the workload), and a range inside
+    # rows of 32768 (16 waves a row)
+    if cut is None:
+        x_bits = workloads.rows("ragged_routed", 0, rows)
+        sub = workloads.group_offsets()[2:6].copy()
+    else:
+        x_bits = np.ascontiguousarray(np.tile(workloads.rows("ragged_routed", 0, rows),
+                                              (1, H // 2048)))
+        x_bits[:, ::7] ^= 0x8000  # rows differ across their 16 copies of 2048
+        sub = np.array(cut, np.int64)
     x = to_dev(x_bits)
     R, H = x_bits.shape
-    out = (torch.full((R, H // 2), 0xAB, dtype=torch.uint8, device="cuda"),
-           torch.full((R, H // 16), 0xCD, dtype=torch.uint8, device="cuda"),
-           torch.full((R,), -7.0, dtype=torch.float32, device="cuda"),
-           torch.full((R, H), 1.5, dtype=torch.bfloat16, device="cuda"))
+    gu = Guards()
+    out = sentinel_outputs(gu, R, H)
     fq.nvfp4_quantize(x, True, offsets=torch.from_numpy(sub).cuda(), out=out)
-    torch.cuda.synchronize()
+    gu.check("subrange H=%d" % H)
     want = oracle_nvfp4(x_bits, True)
     lo, hi = int(sub[0]), int(sub[-1])
     assert 0 < lo < hi < R
@@ -196,22 +224,6 @@ def test_resq_act_full_size():
     check_mx(workloads.rows("resq_act"), label="resq_act")
 
 
-def _at_offset(shape, offset, bufs):
-    """A contiguous uint8 tensor whose data starts `offset` bytes past a
-    256-byte aligned allocation filled with 0xA5 (kept in bufs with the
-    view's range, to check that nothing outside it is written)."""
-    n = int(np.prod(shape))
-    buf = torch.full((n + 256,), 0xA5, dtype=torch.uint8, device="cuda")
-    bufs.append((buf, offset, n))
-    return buf[offset:offset + n].view(shape)
-
-
-def _guards_intact(bufs):
-    for buf, o, n in bufs:
-        b = buf.cpu().numpy()
-        assert (b[:o] == 0xA5).all() and (b[o + n:] == 0xA5).all(), (o, n)
-
-
 @pytest.mark.parametrize("offsets", [(0, 1, 0, 0, 3), (0, 0, 8, 4, 0), (0, 5, 8, 4, 9)])
 def test_mx_outputs_not_16_byte_aligned(offsets):
     """Outputs that are not all 16-byte aligned are written lane by lane
@@ -221,21 +233,19 @@ def test_mx_outputs_not_16_byte_aligned(offsets):
                              f32_to_bf16_bits(rng.standard_normal((48, 2048)).astype(np.float32))])
     R, H = x_bits.shape
     shapes = ((R, H // 2), (R, H // 32), (R, H // 4), (R, H // 8), (R, H // 32))
-    bufs = []
-    out = tuple(_at_offset(sh, o, bufs) for sh, o in zip(shapes, offsets))
+    gu = Guards()
+    out = tuple(gu.empty(sh, torch.uint8, o) for sh, o in zip(shapes, offsets))
     got = fq.mxfp4_resq_quantize(to_dev(x_bits), out=out)
-    torch.cuda.synchronize()
-    _guards_intact(bufs)
+    gu.check("offsets %s" % (offsets,))
     want = oracle_mx(x_bits)
     for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
         assert_same(host(g), w, "offsets %s %s" % (offsets, n))
     dshapes = ((R, H // 2), (R, H // 32), (R, H // 2), (R, H // 32))
-    dbufs = []
-    dout = tuple(_at_offset(sh, o, dbufs)
+    dg = Guards()
+    dout = tuple(dg.empty(sh, torch.uint8, o)
                  for sh, o in zip(dshapes, (0, offsets[1], 0, offsets[4])))
     gd = fq.mxfp4_resq_dense_quantize(to_dev(x_bits), out=dout)
-    torch.cuda.synchronize()
-    _guards_intact(dbufs)
+    dg.check("dense offsets %s" % (offsets,))
     wd = oracle_mx_dense(x_bits)
     for g, w, n in zip(gd, wd, ("codes", "scales", "res_codes", "res_scales")):
         assert_same(host(g), w, "dense offsets %s %s" % (offsets, n))
@@ -246,8 +256,9 @@ def test_mx_outputs_not_16_byte_aligned(offsets):
 def test_standalone_dequant_matches_fused():
     for name in ("tiny_ref", "moe_act"):
         codes, scales, ts, dq = fq.nvfp4_quantize(workloads.tensor(name, "cuda"), True)
-        out = fq.nvfp4_dequantize(codes, scales, ts)
-        torch.cuda.synchronize()
+        gu = Guards()
+        out = fq.nvfp4_dequantize(codes, scales, ts, out=gu.empty(dq.shape, torch.bfloat16))
+        gu.check(name)
         assert torch.equal(out.view(torch.int16), dq.view(torch.int16)), name
 
 
@@ -258,9 +269,10 @@ def test_standalone_dequant_random_bytes():
     scales = rng.integers(0, 0x7F, (R, H // 16), dtype=np.uint8)
     scales |= (rng.integers(0, 2, scales.shape, dtype=np.uint8) << 7)  # signed scale bytes
     ts = (rng.standard_normal(R) * 2.0 ** rng.integers(-140, 60, R)).astype(np.float32)
+    gu = Guards()
     out = fq.nvfp4_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
-                              torch.from_numpy(ts).cuda())
-    torch.cuda.synchronize()
+                              torch.from_numpy(ts).cuda(), out=gu.empty((R, H), torch.bfloat16))
+    gu.check("dequant")
     assert_same(bits_of(out), oracle.nvfp4_dequantize(codes, scales, ts), "dequant")
 
 
@@ -359,12 +371,19 @@ def test_binding_rejects_wrong_sized_buffers():
 
 # ------------------------------------------------- TRACE guided rounding --
 
-def check_guided(x_rollout, x_train, label):
-    codes, scales, ts, _ = oracle_nvfp4(x_rollout, 1, dequant=False)  # the rollout's outputs
-    got = fq.nvfp4_quantize_guided(to_dev(x_train), torch.from_numpy(codes).cuda(),
-                                   torch.from_numpy(scales).cuda(), torch.from_numpy(ts).cuda())
-    torch.cuda.synchronize()
-    want = oracle.nvfp4_quantize_guided(x_train, codes, scales, ts)
+def check_guided(x_rollout, x_train, label, guided=True):
+    """The rollout's outputs from the oracle; the training side guided by
+    its codes under its scales (or, guided False, rounded to nearest under
+    them)."""
+    codes, scales, ts, _ = oracle_nvfp4(x_rollout, 1, dequant=False)
+    guide = codes if guided else None
+    gu = Guards()
+    got = fq.nvfp4_quantize_guided(to_dev(x_train),
+                                   None if guide is None else torch.from_numpy(guide).cuda(),
+                                   torch.from_numpy(scales).cuda(), torch.from_numpy(ts).cuda(),
+                                   out=gu.guided(*x_train.shape))
+    gu.check(label)
+    want = oracle.nvfp4_quantize_guided(x_train, guide, scales, ts)
     assert_same(host(got[0]), want[0], label + " codes")
     assert_same(bits_of(got[1]), want[1], label + " dequant")
 
@@ -376,6 +395,9 @@ def test_guided_edge_rows(H):
     # a guide from unrelated values, and the tensor guided by itself
     check_guided(edge_rows(H, seed=H + 99), x, "guided cross H=%d" % H)
     check_guided(x, x, "guided self H=%d" % H)
+    # no guide: round to nearest under the rollout's scales
+    check_guided(x, workloads.perturbed(x, seed=H), "nearest edge H=%d" % H, guided=False)
+    check_guided(edge_rows(H, seed=H + 99), x, "nearest cross H=%d" % H, guided=False)
 
 
 def test_guided_random_guides_and_scales():
@@ -386,24 +408,32 @@ def test_guided_random_guides_and_scales():
     guide = rng.integers(0, 256, (rows, H // 2), dtype=np.uint8)
     scales = rng.integers(0, 0x7F, (rows, H // 16), dtype=np.uint8)
     ts = (np.abs(rng.standard_normal(rows)) * 0.01).astype(np.float32)
-    got = fq.nvfp4_quantize_guided(to_dev(x), torch.from_numpy(guide).cuda(),
-                                   torch.from_numpy(scales).cuda(), torch.from_numpy(ts).cuda())
-    torch.cuda.synchronize()
-    want = oracle.nvfp4_quantize_guided(x, guide, scales, ts)
-    assert_same(host(got[0]), want[0], "guided random codes")
-    assert_same(bits_of(got[1]), want[1], "guided random dequant")
+    ts[::5] *= np.float32(2.0 ** -120)  # rows whose decode steps are subnormal (r = inf)
+    for gd in (guide, None):
+        gu = Guards()
+        got = fq.nvfp4_quantize_guided(to_dev(x), None if gd is None else torch.from_numpy(gd).cuda(),
+                                       torch.from_numpy(scales).cuda(),
+                                       torch.from_numpy(ts).cuda(), out=gu.guided(rows, H))
+        label = "guided random" if gd is not None else "nearest random"
+        gu.check(label)
+        want = oracle.nvfp4_quantize_guided(x, gd, scales, ts)
+        assert_same(host(got[0]), want[0], label + " codes")
+        assert_same(bits_of(got[1]), want[1], label + " dequant")
 
 
 def test_guided_moe_act_full_size():
     x = workloads.rows("moe_act")
     check_guided(x, workloads.perturbed(x, seed=2), "guided moe_act")
+    check_guided(x, workloads.perturbed(x, seed=2), "nearest moe_act", guided=False)
 
 
 # ------------------------------------------------- global per-tensor scale --
 
 def check_global(x_bits, fos, label):
-    got = fq.nvfp4_quantize_global(to_dev(x_bits), fos)
-    torch.cuda.synchronize()
+    gu = Guards()
+    out, ws = gu.global_(*x_bits.shape)
+    got = fq.nvfp4_quantize_global(to_dev(x_bits), fos, out=out, workspace=ws)
+    gu.check(label)
     want = oracle.nvfp4_quantize_global(x_bits, fos)
     assert_same(host(got[0]), want[0], label + " codes")
     assert_same(host(got[1]), want[1], label + " scales")

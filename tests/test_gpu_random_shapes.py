@@ -3,14 +3,16 @@ from one block to past the one-wave-per-row limit, row counts that leave
 partial workgroups, ragged group ranges, every 4/6 mode, with and without
 the dequant, and row scales from 2^-140 to 2^100.  Every output is compared
 with the CPU oracle bit for bit; rows outside a ragged range must keep their
-sentinel bytes."""
+sentinel bytes, and the 256 guard bytes around every output must stay
+untouched."""
 import numpy as np
 import pytest
 import torch
 
 import fp4_block_quantization_amd as fq
 import oracle
-from gpuutil import assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4, to_dev
+from gpuutil import (Guards, assert_same, bits_of, host, oracle_mx, oracle_mx_dense,
+                     oracle_nvfp4, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +46,10 @@ def random_rows(rng, rows, hidden):
 
 
 def shape(rng, unit):
-    hidden = unit * int(rng.choice([1, 2, 3, 7, 64, 100, 127, 128, 129, 448, 449, 1024, 2100]))
+    # with 16-element blocks: 1280, 1665 and 2048 blocks are rows of 10, 14
+    # and 16 waves, 2100 a long row
+    hidden = unit * int(rng.choice([1, 2, 3, 7, 64, 100, 127, 128, 129, 448, 449, 1024, 1280,
+                                    1665, 2048, 2100]))
     rows = int(rng.integers(1, max(2, min(300, MAX_ELEMENTS // hidden))))
     return rows, hidden
 
@@ -63,15 +68,15 @@ def test_nvfp4_random_shapes(case):
         cuts = np.sort(rng.integers(0, rows + 1, int(rng.integers(2, 6))))
         lo, hi = int(cuts[0]), int(cuts[-1])
         offsets = torch.from_numpy(cuts.astype(np.int64)).cuda()
-    out = (torch.full((rows, hidden // 2), 0xAB, dtype=torch.uint8, device="cuda"),
-           torch.full((rows, hidden // 16), 0xCD, dtype=torch.uint8, device="cuda"),
-           torch.full((rows,), -7.0, dtype=torch.float32, device="cuda"),
-           torch.full((rows, hidden), 1.5, dtype=torch.bfloat16, device="cuda") if dequant
-           else None)
+    gu = Guards()
+    out = gu.nvfp4(rows, hidden, dequant)
+    for t, f in zip(out, (0xAB, 0xCD, -7.0, 1.5)):
+        if t is not None:
+            t.fill_(f)
     fq.nvfp4_quantize(x, fos, offsets=offsets, dequant=dequant, out=out)
-    torch.cuda.synchronize()
     label = "case %d: %d x %d fos=%d dequant=%s rows [%d, %d)" % (
         case, rows, hidden, fos, dequant, lo, hi)
+    gu.check(label)
     if hi > lo:
         want = oracle_nvfp4(x_bits[lo:hi], fos, dequant=dequant)
         assert_same(host(out[0])[lo:hi], want[0], label + " codes")
@@ -94,17 +99,18 @@ def test_mx_random_shapes(case):
     x_bits = random_rows(rng, rows, hidden)
     x = to_dev(x_bits)
     label = "mx case %d: %d x %d" % (case, rows, hidden)
-    got = fq.mxfp4_resq_quantize(x)
-    dense = fq.mxfp4_resq_dense_quantize(x)
-    torch.cuda.synchronize()
+    gu = Guards()
+    got = fq.mxfp4_resq_quantize(x, out=gu.mx(rows, hidden))
+    dense = fq.mxfp4_resq_dense_quantize(x, out=gu.mx_dense(rows, hidden))
+    gu.check(label)
     want = oracle_mx(x_bits)
     for g, w, n in zip(got, want, ("codes", "scales", "res_codes", "res_meta", "res_scales")):
         assert_same(host(g), w, label + " " + n)
     wd = oracle_mx_dense(x_bits)
     for g, w, n in zip(dense, wd, ("codes", "scales", "res_codes", "res_scales")):
         assert_same(host(g), w, label + " dense " + n)
-    xh = fq.mxfp4_resq_reconstruct(*got, residual=1)
-    torch.cuda.synchronize()
+    xh = fq.mxfp4_resq_reconstruct(*got, residual=1, out=gu.empty((rows, hidden), torch.float32))
+    gu.check(label + " reconstruct")
     assert_same(host(xh), oracle.mxfp4_resq_reconstruct(*want, residual=1),
                 label + " reconstruct")
 
@@ -118,13 +124,18 @@ def test_guided_random_shapes(case):
     scales = rng.integers(0, 0x7F, (rows, hidden // 16), dtype=np.uint8)
     ts = (np.abs(rng.standard_normal(rows)) *
           2.0 ** rng.integers(-140, 60, rows)).astype(np.float32)
-    got = fq.nvfp4_quantize_guided(to_dev(x_bits), torch.from_numpy(guide).cuda(),
-                                   torch.from_numpy(scales).cuda(), torch.from_numpy(ts).cuda())
-    torch.cuda.synchronize()
-    want = oracle.nvfp4_quantize_guided(x_bits, guide, scales, ts)
-    label = "guided case %d: %d x %d" % (case, rows, hidden)
-    assert_same(host(got[0]), want[0], label + " codes")
-    assert_same(bits_of(got[1]), want[1], label + " dequant")
+    for gd in (guide, None):  # guided, and round to nearest under the scales
+        gu = Guards()
+        got = fq.nvfp4_quantize_guided(to_dev(x_bits),
+                                       None if gd is None else torch.from_numpy(gd).cuda(),
+                                       torch.from_numpy(scales).cuda(),
+                                       torch.from_numpy(ts).cuda(), out=gu.guided(rows, hidden))
+        label = "%s case %d: %d x %d" % ("guided" if gd is not None else "nearest", case, rows,
+                                         hidden)
+        gu.check(label)
+        want = oracle.nvfp4_quantize_guided(x_bits, gd, scales, ts)
+        assert_same(host(got[0]), want[0], label + " codes")
+        assert_same(bits_of(got[1]), want[1], label + " dequant")
 
 
 @pytest.mark.parametrize("case", range(8))
@@ -147,10 +158,11 @@ def test_nvfp4_full_size_random_tensors(case):
         x = rng.uniform(-6, 6, (R, H)).astype(np.float32)
     x *= np.float32(2.0 ** rng.integers(-30, 30))
     x_bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    got = fq.nvfp4_quantize(to_dev(x_bits), True)
-    torch.cuda.synchronize()
-    want = oracle_nvfp4(x_bits, True)
+    gu = Guards()
     label = "full-size case %d" % case
+    got = fq.nvfp4_quantize(to_dev(x_bits), True, out=gu.nvfp4(R, H))
+    gu.check(label)
+    want = oracle_nvfp4(x_bits, True)
     assert_same(host(got[0]), want[0], label + " codes")
     assert_same(host(got[1]), want[1], label + " scales")
     assert_same(host(got[2])[:, None], want[2][:, None], label + " token scales")

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import fp4_block_quantization_amd as fq
 import oracle
 import workloads
 from gpuutil import (assert_same, bits_of, host, oracle_mx, oracle_mx_dense, oracle_nvfp4,
@@ -27,15 +28,7 @@ def lib():
         pytest.skip("no GPU")
     if not os.path.exists(SPLIT_LIB):
         pytest.fail("split-launch library not built: run __graft_entry__.build()")
-    L = ctypes.CDLL(SPLIT_LIB)
-    L.nvfp4_quantize.argtypes = [vp, i64, i64, vp, i64, ci, vp, vp, vp, vp, vp]
-    L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, vp]
-    L.mxfp4_resq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
-    L.mxfp4_resq_dense_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
-    L.mxfp4_resq_reconstruct.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, vp, vp]
-    L.nvfp4_quantize_guided.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
-    L.nvfp4_quantize_global.argtypes = [vp, i64, i64, ci, vp, vp, vp, vp, vp]
-    return L
+    return fq.declare(ctypes.CDLL(SPLIT_LIB))
 
 
 def ptr(t):
@@ -46,10 +39,13 @@ def stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-@pytest.mark.parametrize("H", [32, 2048, 7168, 33024])
+@pytest.mark.parametrize("H", [32, 2048, 7168, 32768, 33024, 66048])
 def test_nvfp4_split_launch(lib, H):
-    # H = 33024 takes the one-wave-per-row kernel (more than 16 waves a row)
-    rows = {32: 1000, 2048: 300, 7168: 67, 33024: 150}[H]
+    # H = 32768: 16 waves a row, 4 rows a launch; H = 33024 takes the
+    # one-wave-per-row kernel (more than 16 waves a row); H = 66048: one row
+    # of the dequantizer is more work-items than this build's launch limit,
+    # so every launch holds a single row
+    rows = {32: 1000, 2048: 300, 7168: 67, 32768: 21, 33024: 150, 66048: 9}[H]
     rng = np.random.default_rng(H)
     x_bits = workloads.to_bf16_bits(rng.standard_t(3, (rows, H)).astype(np.float32) *
                                     np.exp(rng.standard_normal((rows, 1))).astype(np.float32))
@@ -130,6 +126,13 @@ def test_next_rows_split_launch(lib):
     want = oracle.nvfp4_quantize_guided(x_bits, roll[0], roll[1], roll[2])
     assert_same(host(codes), want[0], "split guided codes")
     assert_same(bits_of(dq), want[1], "split guided dequant")
+    # the same without a guide: round to nearest under the rollout's scales
+    assert lib.nvfp4_quantize_guided(ptr(x), rows, H, None, ptr(bs), ptr(ts), ptr(codes),
+                                     ptr(dq), stream()) == 0
+    torch.cuda.synchronize()
+    want = oracle.nvfp4_quantize_guided(x_bits, None, roll[1], roll[2])
+    assert_same(host(codes), want[0], "split nearest codes")
+    assert_same(bits_of(dq), want[1], "split nearest dequant")
     # one scale for the whole tensor, 67 x 7168
     rows, H = 67, 7168
     x_bits = workloads.rows("moe_act", 100, rows)
@@ -138,8 +141,9 @@ def test_next_rows_split_launch(lib):
     scales = torch.empty((rows, H // 16), **u8)
     tsc = torch.empty(1, dtype=torch.float32, device="cuda")
     dq = torch.empty_like(x)
+    ws = torch.empty(fq.GLOBAL_WORKSPACE_BYTES, **u8)
     assert lib.nvfp4_quantize_global(ptr(x), rows, H, 1, ptr(codes), ptr(scales), ptr(tsc),
-                                     ptr(dq), stream()) == 0
+                                     ptr(dq), ptr(ws), stream()) == 0
     torch.cuda.synchronize()
     want = oracle.nvfp4_quantize_global(x_bits, True)
     assert_same(host(codes), want[0], "split global codes")

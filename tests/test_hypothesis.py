@@ -134,16 +134,20 @@ def _host(t):
 @settings(max_examples=150, **SETTINGS)
 @given(tensors(), st.sampled_from([0, 1, 2]), st.booleans())
 def test_gpu_nvfp4_calls_match_oracle(x, fos, dequant):
+    from gpuutil import Guards
     fq = _gpu()
     xd = _dev(x)
-    got = fq.nvfp4_quantize(xd, fos, dequant=dequant)
-    torch.cuda.synchronize()
+    R, H = x.shape
+    gu = Guards()
+    got = fq.nvfp4_quantize(xd, fos, dequant=dequant, out=gu.nvfp4(R, H, dequant))
+    gu.check("nvfp4")
     want = oracle.nvfp4_quantize(x, fos, dequant=dequant)
     assert _same([_host(g) for g in got], want)
-    back = fq.nvfp4_dequantize(*got[:3])
-    gd = fq.nvfp4_quantize_guided(xd, *got[:3])
-    glob = fq.nvfp4_quantize_global(xd, fos)
-    torch.cuda.synchronize()
+    back = fq.nvfp4_dequantize(*got[:3], out=gu.empty((R, H), torch.bfloat16))
+    gd = fq.nvfp4_quantize_guided(xd, *got[:3], out=gu.guided(R, H))
+    gout, ws = gu.global_(R, H)
+    glob = fq.nvfp4_quantize_global(xd, fos, out=gout, workspace=ws)
+    gu.check("dequant, guided, global")
     assert np.array_equal(_host(back).view(np.uint16), oracle.nvfp4_dequantize(*want[:3]))
     wg = oracle.nvfp4_quantize_guided(x, *want[:3])
     assert _same([_host(g) for g in gd], wg)
@@ -154,17 +158,20 @@ def test_gpu_nvfp4_calls_match_oracle(x, fos, dequant):
 @settings(max_examples=100, **SETTINGS)
 @given(tensors(block=32, max_blocks=3))
 def test_gpu_resq_calls_match_oracle(x):
+    from gpuutil import Guards
     fq = _gpu()
     xd = _dev(x)
-    sp = fq.mxfp4_resq_quantize(xd)
-    de = fq.mxfp4_resq_dense_quantize(xd)
-    torch.cuda.synchronize()
+    R, H = x.shape
+    gu = Guards()
+    sp = fq.mxfp4_resq_quantize(xd, out=gu.mx(R, H))
+    de = fq.mxfp4_resq_dense_quantize(xd, out=gu.mx_dense(R, H))
+    gu.check("resq")
     wsp, wde = oracle.mxfp4_resq_quantize(x), oracle.mxfp4_resq_dense_quantize(x)
     assert _same([_host(g) for g in sp], wsp) and _same([_host(g) for g in de], wde)
     for mode, a, w in ((0, sp[:2] + (None, None, None), wsp[:2] + (None, None, None)),
                        (1, sp, wsp), (2, (de[0], de[1], de[2], None, de[3]),
                                       (wde[0], wde[1], wde[2], None, wde[3]))):
-        xh = fq.mxfp4_resq_reconstruct(*a, residual=mode)
-        torch.cuda.synchronize()
+        xh = fq.mxfp4_resq_reconstruct(*a, residual=mode, out=gu.empty((R, H), torch.float32))
+        gu.check("reconstruct %d" % mode)
         assert np.array_equal(_host(xh).view(np.uint32),
                               oracle.mxfp4_resq_reconstruct(*w, residual=mode).view(np.uint32))
