@@ -6,6 +6,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fp4q_launch.h"
 
 namespace {
@@ -27,6 +30,38 @@ fp4q_status check_shape(int64_t rows, int64_t hidden, int64_t block) {
 }
 
 fp4q_status launched(hipError_t e) { return e == hipSuccess ? FP4Q_SUCCESS : FP4Q_ERROR_LAUNCH; }
+
+// Scratch of nvfp4_quantize_global_noalloc: the partial maxima its tensor-max
+// pass hands to its quantize pass, in place of the caller's workspace.  One
+// copy per device, held until the process ends; every call on a device
+// shares it, so calls that overlap on one device race.  Nothing in it needs
+// to start at zero: the max pass writes every slot the quantize pass reads.
+static __device__ __align__(256) uint8_t scratch[FP4Q_GLOBAL_WORKSPACE_BYTES];
+
+// Its device address per device, looked up once per device with that
+// device current (in host code the array's name is not a device address).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -143,6 +178,29 @@ fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t hidden,
                       four_over_six, codes, block_scales, nullptr, dequant};
   return launched(
       fp4q::nvfp4_quantize_global_launch(a, tensor_scale, workspace, (hipStream_t)stream));
+}
+
+fp4q_status nvfp4_quantize_global_noalloc(const void* x, int64_t rows, int64_t hidden,
+                                          int four_over_six, uint8_t* codes,
+                                          uint8_t* block_scales, float* tensor_scale,
+                                          void* dequant, void* stream) {
+  fp4q_status st = check_shape(rows, hidden, 16);
+  if (st != FP4Q_SUCCESS) return st;
+  if (four_over_six < 0 || four_over_six > 2) return FP4Q_ERROR_INVALID_ARGUMENT;
+  if (rows == 0) return FP4Q_SUCCESS;
+  if (!x || !codes || !block_scales || !tensor_scale) return FP4Q_ERROR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) ||
+      (dequant && !aligned(dequant, 16)))
+    return FP4Q_ERROR_MISALIGNED;
+  // the scratch need is fixed (at most 512 two-byte partial maxima, padded
+  // to 16-byte units), whatever the tensor's size
+  if (fp4q::global_workspace_bytes(rows, hidden) > (int64_t)sizeof(scratch))
+    return FP4Q_ERROR_INVALID_SHAPE;
+  void* ws = nullptr;
+  if (scratch_on_current_device(&ws) != hipSuccess) return FP4Q_ERROR_LAUNCH;
+  fp4q::NvQuantArgs a{x,     rows,         hidden,  nullptr, 0,
+                      four_over_six, codes, block_scales, nullptr, dequant};
+  return launched(fp4q::nvfp4_quantize_global_launch(a, tensor_scale, ws, (hipStream_t)stream));
 }
 
 const char* fp4q_status_string(fp4q_status status) {

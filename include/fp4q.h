@@ -165,6 +165,26 @@ FP4Q_API fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t 
                                   void* stream);
 
 /*
+ * nvfp4_quantize_global_noalloc -- nvfp4_quantize_global without the
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It allocates nothing: the partial maxima live in a fixed
+ * 1 KiB array of the library's own (FP4Q_GLOBAL_WORKSPACE_BYTES), one per
+ * device, held until the process ends; its address is looked up once per
+ * device on the first call there.  The scratch need does not grow with the
+ * tensor (at most 512 partial maxima), so no size within the limits of
+ * nvfp4_quantize_global is refused for it.  Every call on a device shares
+ * that device's array: calls that overlap on one device (other streams, or
+ * other host threads) race and must not be in flight together.  Arguments,
+ * outputs and results are those of nvfp4_quantize_global;
+ * FP4Q_ERROR_LAUNCH also reports a failed lookup of the array.
+ */
+FP4Q_API fp4q_status nvfp4_quantize_global_noalloc(const void* x, int64_t rows, int64_t hidden,
+                                          int four_over_six, uint8_t* codes,
+                                          uint8_t* block_scales, float* tensor_scale,
+                                          void* dequant, void* stream);
+
+/*
  * nvfp4_quantize_guided -- TRACE rollout-guided rounding.
  *
  * Definition: "TRACE FP4 RL -- Rollout-guided FP4 rounding"

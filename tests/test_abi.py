@@ -35,10 +35,10 @@ def test_every_header_has_its_library():
 
 def test_library_exports_every_declared_call():
     names = declared_functions("fp4q.h")
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert {"nvfp4_quantize", "nvfp4_dequantize", "mxfp4_resq_quantize",
             "mxfp4_resq_dense_quantize", "mxfp4_resq_reconstruct", "nvfp4_quantize_guided",
-            "nvfp4_quantize_global",
+            "nvfp4_quantize_global", "nvfp4_quantize_global_noalloc",
             "fp4q_status_string"} <= set(names)
     L = fq.lib()
     for n in names:
