@@ -109,6 +109,16 @@ namespace {
 #define FP4Q_STANDIN 0
 #endif
 
+// Build-time knob: FP4Q_NV_STREAM = 1 quantizes rows of exactly one
+// wavefront's chunk (2048 elements) without dequant, with per-token scales,
+// with the persistent streaming kernel below.  Off: on the routed-token
+// workload (65536 x 2048) it measured 66.3-66.8 us against 63.9-64.6 us for
+// the split kernel's one-shot wavefronts, at every grid from 1024 to 4096
+// workgroups, with its stores deferred (immediate stores: 68.2 us).
+#ifndef FP4Q_NV_STREAM
+#define FP4Q_NV_STREAM 0
+#endif
+
 constexpr int kMaxWgWaves = 16;  // rows of up to 16 waves use the split kernel
 constexpr int kLongWaves = 4;    // rows per workgroup of the long-row kernel
 
@@ -665,11 +675,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // instruction), then reads its own blocks back.  Lanes whose half-block
 // lies past the chunk's end copy nothing.
 template <int NB>
-__device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, const ChunkRef& c,
-                                               int lane, uint4* tile, uint32_t (&w)[NB][8]) {
-  const uint4* xc = x + 2 * c.cbase;
+__device__ __forceinline__ void issue_chunk_lds(const uint4* __restrict__ x, int64_t cbase,
+                                                int valid, int lane, uint4* tile) {
+  const uint4* xc = x + 2 * cbase;
   constexpr int kAux = FP4Q_NV_NT_LOADS ? 2 : 0;  // 2: non-temporal
-  if (c.valid == 64 * NB) {
+  if (valid == 64 * NB) {
     // a whole chunk: one base pair, the KiB steps in the instruction's
     // offset, which moves the global and the LDS address alike
     static_for<0, 2 * NB>([&](auto I) {
@@ -682,20 +692,31 @@ __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, cons
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int q = 128 * n + 64 * k + lane;  // 16-byte unit of the chunk
-        if (64 * n < c.valid && (q >> 1) < c.valid)
+        if (64 * n < valid && (q >> 1) < valid)
           __builtin_amdgcn_global_load_lds(xc + q, (lds_void*)(tile + 128 * n + 64 * k), 16, 0,
                                            kAux);
       }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the copies have landed in LDS
-  // Slots past the chunk's end read whatever the tile holds; the caller
-  // uses only blocks below c.valid.
+}
+
+// The lane's NB blocks from the wave's tile.  Slots past the chunk's end
+// read whatever the tile holds; the caller uses only blocks below valid.
+template <int NB>
+__device__ __forceinline__ void read_tile(const uint4* tile, int lane, uint32_t (&w)[NB][8]) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const uint4 a = tile[128 * n + 2 * lane], b = tile[128 * n + 2 * lane + 1];
     w[n][0] = a.x; w[n][1] = a.y; w[n][2] = a.z; w[n][3] = a.w;
     w[n][4] = b.x; w[n][5] = b.y; w[n][6] = b.z; w[n][7] = b.w;
   }
+}
+
+template <int NB>
+__device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, const ChunkRef& c,
+                                               int lane, uint4* tile, uint32_t (&w)[NB][8]) {
+  issue_chunk_lds<NB>(x, c.cbase, c.valid, lane, tile);
+  __builtin_amdgcn_s_waitcnt(0);  // the copies have landed in LDS
+  read_tile<NB>(tile, lane, w);
 }
 
 template <int FOS, bool DQ, int NB, bool NTC>
@@ -797,6 +818,142 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+  }
+}
+
+// Rows of exactly one wavefront's chunk (64 NB blocks: 2048 elements)
+// without dequant, persistent (FP4Q_NV_STREAM): wavefront g of a grid of G
+// quantizes rows lo + g, lo + g + G, ...  The
+// next row's chunk is copied into the wavefront's LDS tile as soon as the
+// current row's words are in registers, so a load is in flight while the
+// wavefront computes.  A row's codes, scales and token scale are stored
+// after the wait for the next row's chunk: that wait (which covers stores
+// too) then only ever finds the load and stores issued a whole row earlier.
+// The arithmetic is the split kernel's.
+constexpr int kStreamWaves = 4;    // wavefronts per workgroup
+#ifndef FP4Q_NV_STREAM_GRID
+#define FP4Q_NV_STREAM_GRID 2048
+#endif
+constexpr int kStreamGrid = FP4Q_NV_STREAM_GRID;  // workgroups: 8 per compute unit of 256
+
+// Build-time knob: FP4Q_NV_STREAM_DEFER = 1 stores a row's outputs after the
+// wait for the next row's chunk (0: right after its arithmetic, so that the
+// wait also covers those stores).
+#ifndef FP4Q_NV_STREAM_DEFER
+#define FP4Q_NV_STREAM_DEFER 1
+#endif
+
+// One row's outputs, held from the end of its arithmetic until its stores:
+// the lane's code words and its block-scale bytes (block n in byte n).
+template <int NB>
+struct RowOut {
+  uint32_t c[NB][2], e;
+  float s;
+  bool pending;  // wave-uniform: false when the row stored its own outputs
+};
+
+template <int NB>
+__device__ __forceinline__ void store_row(const RowOut<NB>& o, int64_t row, int nblk, int lane,
+                                          uint2* __restrict__ codes,
+                                          uint8_t* __restrict__ scales,
+                                          float* __restrict__ tscale) {
+  if (!o.pending) return;
+  const int64_t base = row * nblk;  // nblk = 64 NB: every lane's blocks exist
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int j = lane + 64 * n;
+    store_codes<false, false>(&codes[base + j], make_uint2(o.c[n][0], o.c[n][1]));
+    store_scale<false>(&scales[base + j], (uint8_t)(o.e >> (8 * n)));
+  }
+  if (lane == 0) tscale[row] = o.s;
+}
+
+template <int FOS, int NB>
+__global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_quantize_stream(
+    const uint4* __restrict__ x, int64_t row0, int64_t row_end, int nblk,
+    const int64_t* __restrict__ offs, int64_t ngroups, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, float neg_zero) {
+  __shared__ uint4 tiles[kStreamWaves][128 * NB];
+  __shared__ float2v recip[kStreamWaves][128];
+  int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t lo = row0, hi = row_end;  // this launch's rows, within the group range
+  if (offs != nullptr) {
+    lo = max(lo, offs[0]);
+    hi = min(hi, offs[ngroups]);
+  }
+  const int64_t stride = (int64_t)gridDim.x * kStreamWaves;
+  int64_t row = lo + (int64_t)blockIdx.x * kStreamWaves + wave;  // wave-uniform
+  if (!lt_i64(row, hi)) return;
+  uint4* tile = tiles[wave];
+  float2v* tab = recip[wave];
+  constexpr int valid = 64 * NB;  // blocks of a row (nblk): whole chunks only
+
+  uint32_t w[NB][8], bmax[NB], lmax;
+  // the tile holds row `row`; its block maxima are taken, then the next
+  // row's copy is started into the same tile
+  const auto take_tile = [&](int64_t next) {
+    read_tile<NB>(tile, lane, w);
+    lmax = 0;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      bmax[n] = block_absmax_bits(w[n]);
+      lmax = max(lmax, bmax[n]);
+    }
+    // lmax depends on every word read, so the reads have completed before
+    // the copy below overwrites the tile
+    asm volatile("" ::"v"(lmax) : "memory");
+    if (lt_i64(next, hi)) issue_chunk_lds<NB>(x, next * nblk, valid, lane, tile);
+  };
+  issue_chunk_lds<NB>(x, row * nblk, valid, lane, tile);
+  __builtin_amdgcn_s_waitcnt(0);
+  int64_t next = row + stride;
+  take_tile(next);
+  for (;;) {
+    // lane, redefined opaquely each row, so that addresses derived from it
+    // are formed where they are used instead of held across the loop (which
+    // would cost the occupancy of 8 wavefronts per SIMD)
+    asm volatile("" : "+v"(lane));
+    RowOut<NB> o;
+    const RowScale rs = row_scale<FOS>(wave_max_u32(lmax));
+    fill_recip(tab, rs, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t cbase = row * nblk;
+    o.s = rs.s;
+    o.pending = rs.fast;
+    o.e = 0u;
+    if (__builtin_expect(rs.fast, 1)) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {  // every lane's blocks exist (whole chunks)
+        float xv[16];
+        unpack16(w[n], xv);
+        BlockOut bo;
+        quantize_block_fast<FOS, false>(xv, bmax[n], rs, tab, neg_zero, bo);
+        o.c[n][0] = bo.code0;
+        o.c[n][1] = bo.code1;
+        o.e |= bo.ebyte << (8 * n);
+      }
+    } else {
+      // tiny rows take the out-of-line definition and store at once
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int j = lane + 64 * n;
+        tiny_row_block<FOS, false>((const uint16_t*)(x + 2 * (cbase + j)),
+                                   __uint_as_float(bmax[n]), tab, rs.s, rs.inv_s,
+                                   (uint8_t*)(codes + cbase + j), scales + cbase + j, nullptr);
+      }
+      if (lane == 0) tscale[row] = rs.s;
+    }
+    if (!FP4Q_NV_STREAM_DEFER || !lt_i64(next, hi))
+      store_row<NB>(o, row, nblk, lane, codes, scales, tscale);
+    if (!lt_i64(next, hi)) break;
+    __builtin_amdgcn_s_waitcnt(0);  // the next row's chunk has landed
+    if (FP4Q_NV_STREAM_DEFER) store_row<NB>(o, row, nblk, lane, codes, scales, tscale);
+    row = next;
+    next = row + stride;
+    take_tile(next);
   }
 }
 
@@ -1137,7 +1294,18 @@ hipError_t launch_quantize(const NvQuantArgs& a, hipStream_t st) {
   const float neg_zero = -0.0f;
   constexpr int NB = FP4Q_NV_NB;             // blocks per lane
   const int W = (nblk + 64 * NB - 1) / (64 * NB);  // waves per row
-  if (W <= kMaxWgWaves) {
+  if (FP4Q_NV_STREAM && !DQ && nblk == 64 * NB && a.global_partials == nullptr &&
+      !FP4Q_STANDIN) {
+    // a fixed grid (fewer workgroups if there are fewer rows, and within the
+    // launch limit) walks all rows
+    int64_t grid = (a.rows + kStreamWaves - 1) / kStreamWaves;
+    if (grid > kStreamGrid) grid = kStreamGrid;
+    const int64_t max_grid = rows_per_launch(64 * kStreamWaves);
+    if (grid > max_grid) grid = max_grid;
+    hipLaunchKernelGGL((nvfp4_quantize_stream<FOS, NB>), dim3((unsigned)grid),
+                       dim3(64 * kStreamWaves), 0, st, x, (int64_t)0, a.rows, nblk, a.offsets,
+                       a.num_groups, codes, a.block_scales, a.token_scales, neg_zero);
+  } else if (W <= kMaxWgWaves) {
     const int R = W >= FP4Q_NV_WG_WAVES ? 1 : FP4Q_NV_WG_WAVES / W;  // rows per workgroup
     const int64_t max_rows = rows_per_launch(64 * W * R) * R;         // rows per launch
     // per wave: its reciprocal table, then its input tile (NB x 2 KiB) or,

@@ -123,6 +123,19 @@ def test_nvfp4_edge_suite(H, fos):
     check_nvfp4(edge_rows(H, seed=H), fos, label="edge H=%d" % H)
 
 
+@pytest.mark.parametrize("fos", [1, 0, 2])
+@pytest.mark.parametrize("H,reps", [(2048, 1), (2048, 300), (2064, 1), (16, 1)])
+def test_nvfp4_edge_suite_no_dequant(H, reps, fos):
+    # without the dequant, rows of exactly 2048 elements take the persistent
+    # streaming kernel (a wavefront walks many rows; with 300 copies of the
+    # edge rows every wavefront of its grid gets several, tiny rows among
+    # them); other lengths take the split kernel
+    x = np.ascontiguousarray(np.tile(edge_rows(H, seed=H + 5), (reps, 1)))
+    if reps > 1:
+        x[::3] ^= 0x8000  # the copies differ
+    check_nvfp4(x, fos, dequant=False, label="edge no-dequant H=%d x%d" % (H, reps))
+
+
 @pytest.mark.parametrize("H", [32, 64, 96, 2048, 7200])
 def test_mx_edge_suite(H):
     check_mx(edge_rows(H, seed=H + 1), label="mx edge H=%d" % H)
