@@ -83,9 +83,12 @@ namespace {
 #define FP4Q_NV_LDS_DQ 1
 #endif
 // Build-time knob: wavefronts per workgroup the split kernel aims for
-// (whole rows per workgroup).
+// (whole rows per workgroup).  4: rows of one wavefront go four to a
+// workgroup (the routed-token workload, 65536 x 2048 without dequant:
+// 64.4 us against 65.1 us with two, median of three side by side); longer
+// rows are unaffected.
 #ifndef FP4Q_NV_WG_WAVES
-#define FP4Q_NV_WG_WAVES 2
+#define FP4Q_NV_WG_WAVES 4
 #endif
 // Build-time knob: FP4Q_NV_LDS_LOAD = 1 copies each wave's input chunk
 // into LDS with 16-byte-per-lane contiguous loads (global_load_lds) and
@@ -548,11 +551,14 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
 }
 
 // One block, written directly (one lane, 32 contiguous dequant bytes).
+// xin, codes, scales and dq point at block 0 of the wavefront's chunk
+// (wave-uniform, so the stores take a scalar base and a 32-bit lane
+// offset); blk is the block within it.
 template <int FOS, bool DQ, bool NTC>
 __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bbits,
                                                const RowScale& rs, const float2v* tab,
                                                float neg_zero, const uint4* __restrict__ xin,
-                                               int64_t blk, uint2* __restrict__ codes,
+                                               int blk, uint2* __restrict__ codes,
                                                uint8_t* __restrict__ scales,
                                                uint4* __restrict__ dq,
                                                uint4* stage = nullptr) {
@@ -801,8 +807,10 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
       } else {
         float xv[16];
         unpack16(w[n], xv);
-        quantize_block<FOS, DQ, NTC>(xv, bmax[n], rs, tab, neg_zero, x, c.cbase + j, codes,
-                                     scales, dq, stage ? &dq_stage_n[2 * lane] : nullptr);
+        quantize_block<FOS, DQ, NTC>(xv, bmax[n], rs, tab, neg_zero, x + 2 * c.cbase, j,
+                                     codes + c.cbase, scales + c.cbase,
+                                     DQ ? dq + 2 * c.cbase : nullptr,
+                                     stage ? &dq_stage_n[2 * lane] : nullptr);
       }
     }
     if (stage && 64 * n < c.valid) {
@@ -998,8 +1006,9 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
     float xv[16];
     load_block(x, base + j, w);
     unpack16(w, xv);
-    quantize_block<FOS, DQ, NTC>(xv, block_absmax_bits(w), rs, recip[wave], neg_zero, x,
-                                 base + j, codes, scales, dq);
+    quantize_block<FOS, DQ, NTC>(xv, block_absmax_bits(w), rs, recip[wave], neg_zero,
+                                 x + 2 * base, j, codes + base, scales + base,
+                                 DQ ? dq + 2 * base : nullptr);
   }
 }
 

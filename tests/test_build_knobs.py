@@ -14,7 +14,7 @@ from fp4_block_quantization_amd import _build
 KNOBS = {
     "nvfp4.hip": ["FP4Q_NV_NT_STORES=0", "FP4Q_NV_NT_BYTES=0", "FP4Q_NV_NT_BYTES=1",
                   "FP4Q_NV_NT_CODES=0", "FP4Q_NV_NT_CODES=1", "FP4Q_NV_NT_LOADS=0",
-                  "FP4Q_NV_LDS_DQ=0", "FP4Q_NV_WG_WAVES=4", "FP4Q_NV_LDS_LOAD=0",
+                  "FP4Q_NV_LDS_DQ=0", "FP4Q_NV_WG_WAVES=2", "FP4Q_NV_LDS_LOAD=0",
                   "FP4Q_NV_NB=1", "FP4Q_NV_NB=3", "FP4Q_NV_NB=4", "FP4Q_DQ_UNITS=1",
                   "FP4Q_DQ_UNITS=4", "FP4Q_DQ_NT_STORES=0", "FP4Q_DQ_NT_LOADS=3",
                   "FP4Q_GUIDED_NT_LOADS=0", "FP4Q_GUIDED_NT_LOADS=3", "FP4Q_GAMAX_NT=1",
