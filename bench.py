@@ -113,10 +113,11 @@ def rate(ms, nbytes, elements=None):
     return out
 
 
-def spin_up(fn, sets, seconds=SPINUP_S):
+def spin_up(fn, sets, seconds=None):
     """Back-to-back calls for `seconds` of wall time: after host-side work
     (workload generation, allocation) the GPU clocks have dropped, and the
     first tens of milliseconds of calls run several % slower."""
+    seconds = SPINUP_S if seconds is None else seconds
     t0 = time.perf_counter()
     i = 0
     while time.perf_counter() - t0 < seconds:
@@ -463,9 +464,9 @@ def algorithmic_rw():
               (n * 2 + n // 2 + n // 16 + R * 4, n // 2),
           "nvfp4_quantize_guided (no guide: nearest) moe_act 8192x7168":
               (n * 2 + n // 16 + R * 4, n // 2),
-          "nvfp4_quantize_global (amax pass) moe_act 8192x7168": (n * 2, 4 * 512),
+          "nvfp4_quantize_global (amax pass) moe_act 8192x7168": (n * 2, 2 * 512),
           "nvfp4_quantize_global (quantize pass) moe_act 8192x7168":
-              (n * 2 + 4 * 512, nvfp4_bytes(R, H) - n * 2 - R * 4 + 4),
+              (n * 2 + 2 * 512, nvfp4_bytes(R, H) - n * 2 - R * 4 + 4),
           "mxfp4_resq_quantize resq_act 8192x7168": (n * 2, mx_bytes(R, H) - n * 2),
           "mxfp4_resq_dense_quantize resq_act 8192x7168": (n * 2, mx_dense_bytes(R, H) - n * 2),
           "mxfp4_resq_reconstruct (S2:4) resq_act 8192x7168":
@@ -484,7 +485,7 @@ def algorithmic_rw():
 
 
 PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python bench.py --no-cpu "
-           "--secondary-steps 8 --steps 20 --warmup 2 --sets 2")
+           "--secondary-steps 8 --steps 20 --warmup 2 --sets 2 --spinup 0")
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
@@ -713,6 +714,7 @@ def write_sweep_summary(sw, path, cmd):
 # ------------------------------------------------------------------ main --
 
 def main():
+    global SPINUP_S
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-sq":
         # python bench.py --summarize-sq SQ_DIR
         summarize_sq(sys.argv[2], os.path.join(ROOT, "profiles"))
@@ -739,7 +741,10 @@ def main():
                     help="print only a row-count sweep (time per call vs rows) as JSON")
     ap.add_argument("--sweep-summary", default=None,
                     help="with --sweep: also write a markdown summary to this path")
+    ap.add_argument("--spinup", type=float, default=SPINUP_S,
+                    help="seconds of untimed calls before each measurement's warm-up")
     args = ap.parse_args()
+    SPINUP_S = args.spinup
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: the quantizer is row-local and needs no "
