@@ -209,6 +209,7 @@ def membench():
     M.fp4q_k0_copy.argtypes = [vp, vp, i64, ci, vp]
     M.fp4q_k0_read.argtypes = [vp, i64, ci, ci, vp, vp]
     M.fp4q_k0_write.argtypes = [vp, i64, ci, vp]
+    M.fp4q_k0_mix.argtypes = [vp, vp, i64, ci, ci, vp]
     return M
 
 
@@ -379,12 +380,21 @@ R, H, RG, HG = 8192, 7168, 65536, 2048
 def _label(name, grid):
     """Name one dispatch (kernel name, total work-items) of a bench run."""
     standin = "fp4q_standin" in name
-    if "k0_copy<true>" in name:
+    if "k0_copy<1>" in name:
         return COPY_CAL_KEY
-    if "k0_copy<false>" in name:
+    if "k0_copy<0>" in name:
         return "K0 copy 256 MiB"
-    if "k0_write<true>" in name:
+    if "k0_copy<2>" in name:
+        return "K0 copy nt sc1 256 MiB"
+    if "k0_mix<" in name:
+        import re
+        m = re.search(r"k0_mix<(\d), (\d)>", name)
+        return None if not m else "K0 mix read 4 KiB, write 4/%s KiB%s 256 MiB" % (
+            m.group(1), ("", " nt", " nt sc1")[int(m.group(2))])
+    if "k0_write<1>" in name:
         return "K0 write nt 256 MiB"
+    if "k0_write<2>" in name:
+        return "K0 write nt sc1 256 MiB"
     if "k0_read<" in name:
         import re
         m = re.search(r"k0_read<(.+?),\s*(true|false)>", name)
@@ -477,7 +487,11 @@ def algorithmic_rw():
               (ng * 2 + 65 * 8, nvfp4_bytes(RG, HG, dequant=False) - ng * 2),
           "stand-in mxfp4_resq_quantize resq_act 8192x7168": (n * 2, mx_bytes(R, H) - n * 2),
           COPY_CAL_KEY: (mib256, mib256), "K0 copy 256 MiB": (mib256, mib256),
-          "K0 write nt 256 MiB": (0.0, mib256)}
+          "K0 copy nt sc1 256 MiB": (mib256, mib256),
+          "K0 write nt 256 MiB": (0.0, mib256), "K0 write nt sc1 256 MiB": (0.0, mib256)}
+    for d in (2, 4):
+        for m in ("", " nt", " nt sc1"):
+            rw["K0 mix read 4 KiB, write 4/%d KiB%s 256 MiB" % (d, m)] = (mib256, mib256 / d)
     for w in (1, 2, 4, 8, 16):
         rw["K0 read %dB 256 MiB" % w] = (mib256, 0.0)
     rw["K0 read 16B nt 256 MiB"] = (mib256, 0.0)
@@ -666,8 +680,8 @@ def size_sweep(x, dev):
         t["mxfp4_resq_quantize"], _ = time_calls(
             lambda i: fq.mxfp4_resq_quantize(sets[i][0], out=mx[i]), list(range(nsets)), steps,
             steps // 4)
-        t["K0 copy nt (same bytes)"], _ = time_calls(
-            lambda c: M.fp4q_k0_copy(ptr(c[0]), ptr(c[1]), half, 1, stream_ptr()), cp, steps,
+        t["K0 copy nt sc1 (same bytes)"], _ = time_calls(
+            lambda c: M.fp4q_k0_copy(ptr(c[0]), ptr(c[1]), half, 2, stream_ptr()), cp, steps,
             steps // 4)
         out[rows] = {k: round(v * 1e3, 3) for k, v in t.items()}
         out[rows]["sets"] = nsets
@@ -707,7 +721,8 @@ def write_sweep_summary(sw, path, cmd):
               "compiled out (-DFP4Q_STANDIN=1): the same loads, row amax, row constants, "
               "reciprocal tables and stores.  The K0 copy moves the same number of bytes "
               "(half read, half written) in 4 KiB per wavefront with non-temporal loads and "
-              "stores; its steady-state column counts the quantize call's bytes per row."]
+              "non-temporal sc1 stores (the quantizer's dequant stream); its steady-state "
+              "column counts the quantize call's bytes per row."]
     open(path, "w").write("\n".join(lines) + "\n")
 
 
@@ -807,9 +822,11 @@ def main():
     n_el = rows * hidden
     if "k0" in parts:
         # K0: the copy ceiling in the quantizer's access pattern (4 KiB per
-        # wavefront, 1 KiB per instruction), non-temporal and plain, on
+        # wavefront, 1 KiB per instruction) -- non-temporal with sc1 stores
+        # (the quantizer's dequant stream), non-temporal and plain -- on
         # 256 MiB per call rotating over 4 x 512 MiB; then reads at every
-        # load width (the counter calibration) and a non-temporal write
+        # load width (the counter calibration) and the two non-temporal
+        # writes
         M = membench()
         sz = 1 << 28
         bufs = [(torch.empty(sz, dtype=torch.uint8, device=dev),
@@ -817,8 +834,8 @@ def main():
         for b in bufs:
             b[0].fill_(0x5A)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        for nt in (1, 0):
-            name = "K0 copy%s 256 MiB" % (" nt" if nt else "")
+        for nt in (2, 1, 0):
+            name = "K0 copy%s 256 MiB" % ("", " nt", " nt sc1")[nt]
             secondary[name] = measure(
                 lambda b: _ok(M.fp4q_k0_copy(ptr(b[0]), ptr(b[1]), sz, nt, stream_ptr()), name),
                 bufs, 2 * sz, None, steps(100))
@@ -829,12 +846,23 @@ def main():
                 lambda b: _ok(M.fp4q_k0_read(ptr(b[0]), sz, w, nt, ptr(sink), stream_ptr()),
                               name), bufs, sz, None, steps(50))
             log(name)
-        name = "K0 write nt 256 MiB"
-        secondary[name] = measure(
-            lambda b: _ok(M.fp4q_k0_write(ptr(b[1]), sz, 1, stream_ptr()), name), bufs, sz,
-            None, steps(100))
-        log(name)
-        secondary["device_copy_GBps"] = secondary["K0 copy nt 256 MiB"]["GBps"]
+        for nt in (1, 2):
+            name = "K0 write%s 256 MiB" % ("", " nt", " nt sc1")[nt]
+            secondary[name] = measure(
+                lambda b: _ok(M.fp4q_k0_write(ptr(b[1]), sz, nt, stream_ptr()), name), bufs, sz,
+                None, steps(100))
+            log(name)
+        # the read/write mixes: 4 KiB read and 2 or 1 KiB written per
+        # wavefront (the routed-token call's mix is about 1 KiB)
+        for d, nt in ((4, 1), (4, 2), (2, 1)):
+            name = "K0 mix read 4 KiB, write 4/%d KiB%s 256 MiB" % (d, ("", " nt", " nt sc1")[nt])
+            secondary[name] = measure(
+                lambda b: _ok(M.fp4q_k0_mix(ptr(b[0]), ptr(b[1]), sz, d, nt, stream_ptr()), name),
+                bufs, sz + sz // d, None, steps(100))
+            log(name)
+        # the copy ceiling: the faster of the K0 copies
+        secondary["device_copy_GBps"] = max(secondary["K0 copy%s 256 MiB" % m]["GBps"]
+                                            for m in ("", " nt", " nt sc1"))
         del bufs, sink
         torch.cuda.empty_cache()
     if "standin" in parts:

@@ -212,4 +212,65 @@ __device__ __forceinline__ int mx_exponent(uint32_t bits) {
   return max((int)(bits >> 23) - 129, -127);
 }
 
+// ---- output stores with a cache policy ----------------------------------
+// POL holds the cache-policy bits of the gfx950 memory instructions (1 sc0,
+// 2 nt, 16 sc1; -1: none).  One lane stores element idx of an array whose
+// base is uniform over the wavefront: no bits and nt alone as global stores
+// (scalar base, lane offset), other bits as a buffer store through a
+// descriptor at base, whose 32-bit byte offset idx * sizeof(T) every caller
+// keeps far below 2^32 (one chunk or row of a wavefront).
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, -1, 0x20000);
+}
+template <int POL>
+__device__ __forceinline__ void put(uint4* base, uint32_t idx, uint4 v) {
+  const u32x4v w = {v.x, v.y, v.z, v.w};
+  if constexpr (POL < 0)
+    base[idx] = v;
+  else if constexpr (POL == 2)
+    __builtin_nontemporal_store(w, (u32x4v*)&base[idx]);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(w, rsrc_at(base), idx * 16u, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void put(uint2* base, uint32_t idx, uint2 v) {
+  const u32x2v w = {v.x, v.y};
+  if constexpr (POL < 0)
+    base[idx] = v;
+  else if constexpr (POL == 2)
+    __builtin_nontemporal_store(w, (u32x2v*)&base[idx]);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(w, rsrc_at(base), idx * 8u, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void put(uint32_t* base, uint32_t idx, uint32_t v) {
+  if constexpr (POL < 0)
+    base[idx] = v;
+  else if constexpr (POL == 2)
+    __builtin_nontemporal_store(v, &base[idx]);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(v, rsrc_at(base), idx * 4u, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void put(uint16_t* base, uint32_t idx, uint16_t v) {
+  if constexpr (POL < 0)
+    base[idx] = v;
+  else if constexpr (POL == 2)
+    __builtin_nontemporal_store(v, &base[idx]);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16(v, rsrc_at(base), idx * 2u, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void put(uint8_t* base, uint32_t idx, uint8_t v) {
+  if constexpr (POL < 0)
+    base[idx] = v;
+  else if constexpr (POL == 2)
+    __builtin_nontemporal_store(v, &base[idx]);
+  else
+    __builtin_amdgcn_raw_buffer_store_b8(v, rsrc_at(base), idx, 0, POL);
+}
+
 }  // namespace fp4q

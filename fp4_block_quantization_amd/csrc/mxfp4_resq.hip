@@ -41,27 +41,21 @@ __device__ __forceinline__ void static_for(F&& f) {
 #ifndef FP4Q_MX_NT_SMALL
 #define FP4Q_MX_NT_SMALL 0
 #endif
+// Build-time knobs: the cache-policy bits (see put) of the 16- and 4-byte
+// outputs, and of the narrow ones (2 bytes or less per lane).
+#ifndef FP4Q_MX_POLICY
+#define FP4Q_MX_POLICY (FP4Q_MX_NT_STORES ? 2 : -1)
+#endif
+#ifndef FP4Q_MX_SMALL_POLICY
+#define FP4Q_MX_SMALL_POLICY (FP4Q_MX_NT_STORES && FP4Q_MX_NT_SMALL ? 2 : -1)
+#endif
 template <typename T>
-__device__ __forceinline__ void store_out(T* p, T v) {
-  if (FP4Q_MX_NT_STORES)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
+__device__ __forceinline__ void store_out(T* base, uint32_t idx, T v) {
+  put<FP4Q_MX_POLICY>(base, idx, v);
 }
-__device__ __forceinline__ void store_out(uint4* p, uint4 v) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  if (FP4Q_MX_NT_STORES)
-    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, (u32x4*)p);
-  else
-    *p = v;
-}
-// the narrow outputs (2 bytes or less per lane)
 template <typename T>
-__device__ __forceinline__ void store_small(T* p, T v) {
-  if (FP4Q_MX_NT_STORES && FP4Q_MX_NT_SMALL)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
+__device__ __forceinline__ void store_small(T* base, uint32_t idx, T v) {
+  put<FP4Q_MX_SMALL_POLICY>(base, idx, v);
 }
 
 template <int CTRL>
@@ -281,20 +275,20 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
         continue;
       }
       if (DENSE) {
-        if (j < nv) store_out(&(reinterpret_cast<uint32_t*>(res_codes) + ub)[j], rw);
+        if (j < nv) store_out(reinterpret_cast<uint32_t*>(res_codes) + ub, j, rw);
       } else {
         uint32_t meta = rw >> 24;
         const uint32_t rc = FP4Q_STANDIN ? rw : select_2of4(rw, tab, meta);
         if (j < nv) {
-          store_small(&(reinterpret_cast<uint16_t*>(res_codes) + ub)[j], (uint16_t)rc);
-          store_small(&(res_meta + ub)[j], (uint8_t)meta);
+          store_small(reinterpret_cast<uint16_t*>(res_codes) + ub, j, (uint16_t)rc);
+          store_small(res_meta + ub, j, (uint8_t)meta);
         }
       }
       if (j < nv) {
-        store_out(&cw_out[j], cw);
+        store_out(cw_out, j, cw);
         if ((lane & 3) == 0) {
-          store_small(&sc_out[j >> 2], (uint8_t)(k + 127));
-          store_small(&rs_out[j >> 2], (uint8_t)(kr + 127));
+          store_small(sc_out, j >> 2, (uint8_t)(k + 127));
+          store_small(rs_out, j >> 2, (uint8_t)(kr + 127));
         }
       }
     }
@@ -304,24 +298,26 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint4* st = stage_lds + wave * SL::kPieces;
+    // each output's first piece (wave-uniform)
+    uint4* const o_code = reinterpret_cast<uint4*>(cw_out);
+    uint4* const o_res =
+        reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(res_codes) + ub * (DENSE ? 4 : 2));
+    uint4* const o_meta = reinterpret_cast<uint4*>(DENSE ? nullptr : res_meta + ub);
+    uint4* const o_sc = reinterpret_cast<uint4*>(sc_out);
+    uint4* const o_rs = reinterpret_cast<uint4*>(rs_out);
 #pragma unroll
     for (int p0 = 0; p0 < SL::kPieces; p0 += 64) {
       const int p = p0 + lane;
-      if (p < SL::kPieces) {
-        uint4* dst;
-        if (p < SL::kResAt)
-          dst = reinterpret_cast<uint4*>(cw_out) + p;
-        else if (p < SL::kMetaAt)
-          dst = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(res_codes) +
-                                         ub * (DENSE ? 4 : 2)) + (p - SL::kResAt);
-        else if (p < SL::kScAt)
-          dst = reinterpret_cast<uint4*>(res_meta + ub) + (p - SL::kMetaAt);
-        else if (p < SL::kRscAt)
-          dst = reinterpret_cast<uint4*>(sc_out) + (p - SL::kScAt);
-        else
-          dst = reinterpret_cast<uint4*>(rs_out) + (p - SL::kRscAt);
-        store_out(dst, st[p]);
-      }
+      if (p < SL::kResAt)
+        store_out(o_code, p, st[p]);
+      else if (p < SL::kMetaAt)
+        store_out(o_res, p - SL::kResAt, st[p]);
+      else if (p < SL::kScAt)
+        store_out(o_meta, p - SL::kMetaAt, st[p]);
+      else if (p < SL::kRscAt)
+        store_out(o_sc, p - SL::kScAt, st[p]);
+      else if (p < SL::kPieces)
+        store_out(o_rs, p - SL::kRscAt, st[p]);
     }
   }
 }
@@ -350,12 +346,14 @@ __device__ __forceinline__ uint32_t expand_2of4(uint32_t rc, uint32_t meta) {
 #ifndef FP4Q_MX_REC_NT
 #define FP4Q_MX_REC_NT 1
 #endif
-__device__ __forceinline__ void store_rec(uint4* p, uint4 v) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  if (FP4Q_MX_REC_NT)
-    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, (u32x4*)p);
-  else
-    *p = v;
+// Build-time knob: the cache-policy bits (see put) of the FP32 output: nt
+// with sc1 measured 41.0 against 41.4 us for nt alone on the 8192 x 7168
+// S2:4 reconstruction (sc1 gained nothing on the quantizer's outputs).
+#ifndef FP4Q_MX_REC_POLICY
+#define FP4Q_MX_REC_POLICY (FP4Q_MX_REC_NT ? 18 : -1)
+#endif
+__device__ __forceinline__ void store_rec(uint4* base, uint32_t idx, uint4 v) {
+  put<FP4Q_MX_REC_POLICY>(base, idx, v);
 }
 template <int RES>
 __global__ __launch_bounds__(256) void mxfp4_reconstruct_units(
@@ -364,9 +362,10 @@ __global__ __launch_bounds__(256) void mxfp4_reconstruct_units(
     const uint8_t* __restrict__ res_scales, int64_t u0, int64_t u_end,
     uint4* __restrict__ out) {
   __shared__ uint4 stage_lds[FP4Q_MX_REC_STAGE ? 512 : 1];
-  const int64_t u = u0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x & 63;
-  const int64_t uw = u - lane;  // the wave's first unit (uniform)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t uw = u0 + (int64_t)blockIdx.x * 256 + 64 * wave;  // the wave's first unit
+  const int64_t u = uw + lane;
   const bool staged = FP4Q_MX_REC_STAGE && uw + 64 <= u_end;
   if (u >= u_end) return;
   const uint32_t cw = codes[u];
@@ -391,11 +390,11 @@ __global__ __launch_bounds__(256) void mxfp4_reconstruct_units(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    store_rec(&out[2 * uw + lane], st[lane]);
-    store_rec(&out[2 * uw + 64 + lane], st[64 + lane]);
+    store_rec(out + 2 * uw, lane, st[lane]);
+    store_rec(out + 2 * uw, 64 + lane, st[64 + lane]);
   } else {
-    store_rec(&out[2 * u], make_uint4(o[0], o[1], o[2], o[3]));
-    store_rec(&out[2 * u + 1], make_uint4(o[4], o[5], o[6], o[7]));
+    store_rec(out + 2 * uw, 2 * lane, make_uint4(o[0], o[1], o[2], o[3]));
+    store_rec(out + 2 * uw, 2 * lane + 1, make_uint4(o[4], o[5], o[6], o[7]));
   }
 }
 

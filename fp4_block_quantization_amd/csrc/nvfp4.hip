@@ -66,6 +66,24 @@ namespace {
 #ifndef FP4Q_NV_NT_CODES
 #define FP4Q_NV_NT_CODES 2
 #endif
+// Build-time knobs: the cache-policy bits of the output stores, as the
+// gfx950 memory instructions encode them (1 sc0, 2 nt, 16 sc1; -1 none):
+//   FP4Q_NV_DQ_POLICY     the BF16 dequant stream;
+//   FP4Q_NV_NT_POLICY     the non-temporal code and block-scale stores;
+//   FP4Q_NV_PLAIN_POLICY  the other code and block-scale stores.
+// nt with sc1 on the dequant stream measured faster than nt alone on MI355X
+// (the dequant call 19.8 against 22.1 us, the headline 42.8 against 43.3 us;
+// writes of 256 MiB 43.0 against 44.1 us); on the code stores of the
+// routed-token workload it gained nothing.
+#ifndef FP4Q_NV_DQ_POLICY
+#define FP4Q_NV_DQ_POLICY (FP4Q_NV_NT_STORES ? 18 : -1)
+#endif
+#ifndef FP4Q_NV_NT_POLICY
+#define FP4Q_NV_NT_POLICY (FP4Q_NV_NT_STORES ? 2 : -1)
+#endif
+#ifndef FP4Q_NV_PLAIN_POLICY
+#define FP4Q_NV_PLAIN_POLICY -1
+#endif
 
 // Build-time knob: FP4Q_NV_NT_LOADS = 1 makes the contiguous input copies
 // into LDS (FP4Q_NV_LDS_LOAD) non-temporal: the input is read once, and each
@@ -74,6 +92,11 @@ namespace {
 // apart, so every line is read by two instructions.
 #ifndef FP4Q_NV_NT_LOADS
 #define FP4Q_NV_NT_LOADS 1
+#endif
+// Build-time knob: the cache-policy bits of those copies (1 sc0, 2 nt,
+// 16 sc1).
+#ifndef FP4Q_NV_LOAD_AUX
+#define FP4Q_NV_LOAD_AUX (FP4Q_NV_NT_LOADS ? 2 : 0)
 #endif
 
 // Build-time knob: FP4Q_NV_LDS_DQ = 1 stages each wave's dequant chunk
@@ -128,49 +151,33 @@ constexpr int kLongWaves = 4;    // rows per workgroup of the long-row kernel
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void store_out(uint4* p, uint4 v) {
-  if (FP4Q_NV_NT_STORES)
-    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, (u32x4*)p);
-  else
-    *p = v;
+// The stores of each output stream, by the policies above.
+__device__ __forceinline__ void store_dq(uint4* base, uint32_t idx, uint4 v) {
+  put<FP4Q_NV_DQ_POLICY>(base, idx, v);
 }
-__device__ __forceinline__ void store_out(uint2* p, uint2 v) {
-  if (FP4Q_NV_NT_STORES)
-    __builtin_nontemporal_store((u32x2){v.x, v.y}, (u32x2*)p);
-  else
-    *p = v;
-}
-__device__ __forceinline__ void store_out(uint32_t* p, uint32_t v) {
-  if (FP4Q_NV_NT_STORES)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
-}
-__device__ __forceinline__ void store_out(uint8_t* p, uint8_t v) {
-  if (FP4Q_NV_NT_STORES)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
-}
-// A block scale byte and a block's code word: non-temporal per
+// A block-scale byte and a block's code word: non-temporal per
 // FP4Q_NV_NT_BYTES and FP4Q_NV_NT_CODES (DQ: the call also writes the
 // dequant).
 template <bool DQ>
-__device__ __forceinline__ void store_scale(uint8_t* p, uint8_t v) {
-  if (FP4Q_NV_NT_BYTES == 1 || (FP4Q_NV_NT_BYTES == 2 && !DQ))
-    store_out(p, v);
+__device__ __forceinline__ void store_scale(uint8_t* base, uint32_t idx, uint8_t v) {
+  if constexpr (FP4Q_NV_NT_BYTES == 1 || (FP4Q_NV_NT_BYTES == 2 && !DQ))
+    put<FP4Q_NV_NT_POLICY>(base, idx, v);
   else
-    *p = v;
+    put<FP4Q_NV_PLAIN_POLICY>(base, idx, v);
 }
 // NTC: non-temporal whatever the knob says -- the quantize pass of the
 // global-scale call, whose plain code stores would leave dirty lines for the
 // next call's tensor-max pass to write back (62 vs 68 us on moe_act).
 template <bool DQ, bool NTC>
-__device__ __forceinline__ void store_codes(uint2* p, uint2 v) {
-  if (NTC || FP4Q_NV_NT_CODES == 1 || (FP4Q_NV_NT_CODES == 2 && !DQ))
-    store_out(p, v);
+__device__ __forceinline__ void store_codes(uint2* base, uint32_t idx, uint2 v) {
+  if constexpr (NTC || FP4Q_NV_NT_CODES == 1 || (FP4Q_NV_NT_CODES == 2 && !DQ))
+    put<FP4Q_NV_NT_POLICY < 0 ? 2 : FP4Q_NV_NT_POLICY>(base, idx, v);
   else
-    *p = v;
+    put<FP4Q_NV_PLAIN_POLICY>(base, idx, v);
+}
+// Code words of the guided call (one lane per 8 elements).
+__device__ __forceinline__ void store_words(uint32_t* base, uint32_t idx, uint32_t v) {
+  put<FP4Q_NV_NT_POLICY>(base, idx, v);
 }
 
 template <int I, int N, typename F>
@@ -571,15 +578,15 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
   }
   BlockOut o;
   quantize_block_fast<FOS, DQ>(x, bbits, rs, tab, neg_zero, o);
-  store_codes<DQ, NTC>(&codes[blk], make_uint2(o.code0, o.code1));
-  store_scale<DQ>(&scales[blk], (uint8_t)o.ebyte);
+  store_codes<DQ, NTC>(codes, blk, make_uint2(o.code0, o.code1));
+  store_scale<DQ>(scales, blk, (uint8_t)o.ebyte);
   if (DQ) {
     if (stage != nullptr) {  // the caller writes the chunk out contiguously
       stage[0] = make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]);
       stage[1] = make_uint4(o.deq[4], o.deq[5], o.deq[6], o.deq[7]);
     } else {
-      store_out(&dq[2 * blk], make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]));
-      store_out(&dq[2 * blk + 1], make_uint4(o.deq[4], o.deq[5], o.deq[6], o.deq[7]));
+      store_dq(dq, 2 * blk, make_uint4(o.deq[0], o.deq[1], o.deq[2], o.deq[3]));
+      store_dq(dq, 2 * blk + 1, make_uint4(o.deq[4], o.deq[5], o.deq[6], o.deq[7]));
     }
   }
 }
@@ -588,18 +595,18 @@ __device__ __forceinline__ void quantize_block(const float (&x)[16], uint32_t bb
 // codes, scale byte and dequant values taken from the input words.
 template <bool DQ, bool NTC>
 __device__ __forceinline__ void standin_block(const uint32_t (&w)[8], uint32_t bbits,
-                                              int64_t blk, uint2* __restrict__ codes,
+                                              int blk, uint2* __restrict__ codes,
                                               uint8_t* __restrict__ scales,
                                               uint4* __restrict__ dq, uint4* stage) {
-  store_codes<DQ, NTC>(&codes[blk], make_uint2(w[0] ^ w[2] ^ w[4] ^ w[6], w[1] ^ w[3] ^ w[5] ^ w[7]));
-  store_scale<DQ>(&scales[blk], (uint8_t)(bbits >> 24));
+  store_codes<DQ, NTC>(codes, blk, make_uint2(w[0] ^ w[2] ^ w[4] ^ w[6], w[1] ^ w[3] ^ w[5] ^ w[7]));
+  store_scale<DQ>(scales, blk, (uint8_t)(bbits >> 24));
   if (DQ) {
     if (stage != nullptr) {
       stage[0] = make_uint4(w[0], w[1], w[2], w[3]);
       stage[1] = make_uint4(w[4], w[5], w[6], w[7]);
     } else {
-      store_out(&dq[2 * blk], make_uint4(w[0], w[1], w[2], w[3]));
-      store_out(&dq[2 * blk + 1], make_uint4(w[4], w[5], w[6], w[7]));
+      store_dq(dq, 2 * blk, make_uint4(w[0], w[1], w[2], w[3]));
+      store_dq(dq, 2 * blk + 1, make_uint4(w[4], w[5], w[6], w[7]));
     }
   }
 }
@@ -684,7 +691,7 @@ template <int NB>
 __device__ __forceinline__ void issue_chunk_lds(const uint4* __restrict__ x, int64_t cbase,
                                                 int valid, int lane, uint4* tile) {
   const uint4* xc = x + 2 * cbase;
-  constexpr int kAux = FP4Q_NV_NT_LOADS ? 2 : 0;  // 2: non-temporal
+  constexpr int kAux = FP4Q_NV_LOAD_AUX;
   if (valid == 64 * NB) {
     // a whole chunk: one base pair, the KiB steps in the instruction's
     // offset, which moves the global and the LDS address alike
@@ -802,7 +809,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
     uint4* dq_stage_n = wave_lds + (kLdsLoad ? 128 * n : 0);
     if (64 * n < c.valid && j < c.valid) {
       if (FP4Q_STANDIN) {
-        standin_block<DQ, NTC>(w[n], bmax[n], c.cbase + j, codes, scales, dq,
+        standin_block<DQ, NTC>(w[n], bmax[n], j, codes + c.cbase, scales + c.cbase,
+                               DQ ? dq + 2 * c.cbase : nullptr,
                                stage ? &dq_stage_n[2 * lane] : nullptr);
       } else {
         float xv[16];
@@ -820,8 +828,8 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       uint4* dqc = dq + 2 * (c.cbase + 64 * n);
-      if (lane < 2 * nv) store_out(&dqc[lane], dq_stage_n[lane]);
-      if (64 + lane < 2 * nv) store_out(&dqc[64 + lane], dq_stage_n[64 + lane]);
+      if (lane < 2 * nv) store_dq(dqc, lane, dq_stage_n[lane]);
+      if (64 + lane < 2 * nv) store_dq(dqc, 64 + lane, dq_stage_n[64 + lane]);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -870,8 +878,8 @@ __device__ __forceinline__ void store_row(const RowOut<NB>& o, int64_t row, int 
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const int j = lane + 64 * n;
-    store_codes<false, false>(&codes[base + j], make_uint2(o.c[n][0], o.c[n][1]));
-    store_scale<false>(&scales[base + j], (uint8_t)(o.e >> (8 * n)));
+    store_codes<false, false>(codes + base, j, make_uint2(o.c[n][0], o.c[n][1]));
+    store_scale<false>(scales + base, j, (uint8_t)(o.e >> (8 * n)));
   }
   if (lane == 0) tscale[row] = o.s;
 }
@@ -1023,6 +1031,10 @@ __global__ __launch_bounds__(64 * kLongWaves) void nvfp4_quantize_long_rows(
 #ifndef FP4Q_DQ_NT_STORES
 #define FP4Q_DQ_NT_STORES 1
 #endif
+// Build-time knob: the cache-policy bits of K2's BF16 stores (see put).
+#ifndef FP4Q_DQ_POLICY
+#define FP4Q_DQ_POLICY FP4Q_NV_DQ_POLICY
+#endif
 // Build-time knob: FP4Q_DQ_NT_LOADS reads the codes (bit 0) and the block
 // scales (bit 1) of the dequantizer with non-temporal loads.
 #ifndef FP4Q_DQ_NT_LOADS
@@ -1070,7 +1082,8 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
     });
     if (lane + 64 * n < nv) {
       if (FP4Q_DQ_NT_STORES)
-        __builtin_nontemporal_store((u32x4){q[0], q[1], q[2], q[3]}, (u32x4*)&o[lane + 64 * n]);
+        put<FP4Q_DQ_POLICY < 0 ? 2 : FP4Q_DQ_POLICY>(o, lane + 64 * n,
+                                                     make_uint4(q[0], q[1], q[2], q[3]));
       else
         o[lane + 64 * n] = make_uint4(q[0], q[1], q[2], q[3]);
     }
@@ -1198,7 +1211,7 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
         out |= ((sx << 3) | q) << (4 * i);
       }
     }
-    store_out(&codes[base + j], out);
+    store_words(codes + base, j, out);
     if (dq != nullptr) {
       uint32_t o[4];
       static_for<0, 4>([&](auto P) {
@@ -1207,7 +1220,7 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
         const float ge0 = g.x * e, ge1 = g.y * e;  // exact
         o[k] = cvt_bf16x2(ge0 * s, ge1 * s);
       });
-      store_out(&dq[base + j], make_uint4(o[0], o[1], o[2], o[3]));
+      store_dq(dq + base, j, make_uint4(o[0], o[1], o[2], o[3]));
     }
   }
 }

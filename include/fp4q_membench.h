@@ -26,8 +26,10 @@ extern "C" {
  * fp4q_k0_copy -- copy `bytes` bytes from src to dst (the copy ceiling).
  *   src, dst     16-byte aligned, non-overlapping; bytes a multiple of 16,
  *                at most 2^40.
- *   nontemporal  1: non-temporal loads and stores (as the quantizer's input
- *                and dequant streams), 0: ordinary ones.
+ *   nontemporal  0: ordinary loads and stores; 1: non-temporal ones (nt);
+ *                2: non-temporal loads and stores with nt and sc1, as the
+ *                quantizer's input and BF16 dequant streams.  Other values:
+ *                FP4Q_ERROR_INVALID_ARGUMENT.
  */
 FP4Q_API fp4q_status fp4q_k0_copy(const void* src, void* dst, int64_t bytes, int nontemporal,
                                   void* stream);
@@ -44,6 +46,7 @@ FP4Q_API fp4q_status fp4q_k0_copy_stream(const void* src, void* dst, int64_t byt
 /*
  * fp4q_k0_read -- read `bytes` bytes of src with loads of `width` bytes per
  * lane (1, 2, 4, 8 or 16; other widths: FP4Q_ERROR_INVALID_ARGUMENT),
+ * non-temporal when `nontemporal` is nonzero,
  * writing nothing in practice: the XOR of everything read goes to sink[0]
  * only if it equals 0xFFFFFFFF.  The reference kernel for the HBM read
  * counters at each load width.
@@ -54,9 +57,24 @@ FP4Q_API fp4q_status fp4q_k0_read(const void* src, int64_t bytes, int width, int
                                   uint32_t* sink, void* stream);
 
 /*
+ * fp4q_k0_mix -- read `bytes` bytes of src and write bytes / divisor bytes
+ * to dst: each wavefront reads its 4 KiB and writes 4 KiB / divisor, the
+ * XOR of `divisor` of its 16-byte units, contiguously (divisor 4 is the
+ * routed-token quantizer's mix: 4 KiB of input and 1 KiB of codes per
+ * wavefront; 1 is the copy).
+ *   src, dst     16-byte aligned, non-overlapping; dst holds bytes / divisor.
+ *   bytes        a multiple of 4096 (whole wavefront chunks), at most 2^40.
+ *   divisor      1, 2 or 4 (else FP4Q_ERROR_INVALID_ARGUMENT).
+ *   nontemporal  store mode as for fp4q_k0_copy (0, 1 or 2).
+ */
+FP4Q_API fp4q_status fp4q_k0_mix(const void* src, void* dst, int64_t bytes, int divisor,
+                                 int nontemporal, void* stream);
+
+/*
  * fp4q_k0_write -- write `bytes` bytes of an index-derived pattern to dst
  * (the write ceiling, and the reference kernel for the HBM write counter).
  *   dst          16-byte aligned; bytes a multiple of 16, at most 2^40.
+ *   nontemporal  store mode as for fp4q_k0_copy (0, 1 or 2).
  */
 FP4Q_API fp4q_status fp4q_k0_write(void* dst, int64_t bytes, int nontemporal, void* stream);
 

@@ -51,14 +51,22 @@ def test_library_exports_every_declared_call():
 
 def test_membench_library_exports_and_rejects():
     names = declared_functions("fp4q_membench.h")
-    assert names == ["fp4q_k0_copy", "fp4q_k0_copy_stream", "fp4q_k0_read", "fp4q_k0_write"], names
+    assert names == ["fp4q_k0_copy", "fp4q_k0_copy_stream", "fp4q_k0_mix", "fp4q_k0_read",
+                     "fp4q_k0_write"], names
     M = ctypes.CDLL(_build.MEMBENCH_PATH)
     P, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     M.fp4q_k0_copy.argtypes = [P, P, i64, ci, P]
     M.fp4q_k0_read.argtypes = [P, i64, ci, ci, P, P]
     M.fp4q_k0_write.argtypes = [P, i64, ci, P]
     M.fp4q_k0_copy_stream.argtypes = [P, P, i64, ci, ci, P]
+    M.fp4q_k0_mix.argtypes = [P, P, i64, ci, ci, P]
     a16 = P(0x10000)
+    assert M.fp4q_k0_mix(a16, a16, 4096, 3, 1, None) == INVALID
+    assert M.fp4q_k0_mix(a16, a16, 4096, 4, 3, None) == INVALID
+    assert M.fp4q_k0_mix(a16, a16, 2048, 4, 1, None) == SHAPE
+    assert M.fp4q_k0_mix(None, a16, 4096, 4, 1, None) == NULL
+    assert M.fp4q_k0_mix(a16, P(0x10004), 4096, 4, 1, None) == MISALIGNED
+    assert M.fp4q_k0_mix(None, None, 0, 4, 1, None) == SUCCESS
     assert M.fp4q_k0_copy_stream(a16, a16, 32, 1, 0, None) == INVALID
     assert M.fp4q_k0_copy_stream(a16, a16, 24, 1, 8, None) == SHAPE
     assert M.fp4q_k0_copy(a16, a16, 24, 1, None) == SHAPE
@@ -71,6 +79,10 @@ def test_membench_library_exports_and_rejects():
     assert M.fp4q_k0_read(P(0x10002), 64, 4, 0, a16, None) == MISALIGNED
     assert M.fp4q_k0_write(a16, -16, 1, None) == SHAPE
     assert M.fp4q_k0_write(None, 16, 1, None) == NULL
+    # store modes 0, 1 and 2 only
+    assert M.fp4q_k0_write(a16, 16, 3, None) == INVALID
+    assert M.fp4q_k0_copy(a16, a16, 32, -1, None) == INVALID
+    assert M.fp4q_k0_copy_stream(a16, a16, 32, 3, 8, None) == INVALID
 
 
 def test_status_strings():

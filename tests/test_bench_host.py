@@ -90,7 +90,13 @@ def test_dispatch_labels():
     assert lab(k0 % ("unsigned int", "false"), 1) == "K0 read 4B 256 MiB"
     assert lab(k0 % ("unsigned int __vector(2)", "false"), 1) == "K0 read 8B 256 MiB"
     assert lab(k0 % ("unsigned int __vector(4)", "true"), 1) == "K0 read 16B nt 256 MiB"
-    assert lab("(anonymous namespace)::k0_copy<true>(x)", 1) == bench.COPY_CAL_KEY
+    assert lab("(anonymous namespace)::k0_copy<1>(x)", 1) == bench.COPY_CAL_KEY
+    assert lab("(anonymous namespace)::k0_copy<0>(x)", 1) == "K0 copy 256 MiB"
+    assert lab("(anonymous namespace)::k0_copy<2>(x)", 1) == "K0 copy nt sc1 256 MiB"
+    assert lab("(anonymous namespace)::k0_write<2>(x)", 1) == "K0 write nt sc1 256 MiB"
+    assert lab("(anonymous namespace)::k0_copy_stream<1>(x)", 1) is None
+    assert lab("void (anonymous namespace)::k0_mix<4, 1>(x)", 1) == \
+        "K0 mix read 4 KiB, write 4/4 KiB nt 256 MiB"
     # every labelled kernel has algorithmic bytes
     algo = bench.algorithmic_rw()
     assert bench.HEADLINE_KEY in algo and bench.COPY_CAL_KEY in algo
