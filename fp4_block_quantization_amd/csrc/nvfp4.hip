@@ -395,30 +395,38 @@ __device__ __forceinline__ float fp16_error(const half2v (&y)[8], const uint32_t
   return err;
 }
 
-// Certified enclosure [lo, hi] of a candidate's FP32 error err (as the
-// definition computes it) from A and D2 = fl(D^2), D = fl(e s) the decode
-// step, for rows
-// with 2^-50 <= s <= 2^40 and e != 0.  With u = 2^-24: v = x r and the
-// candidate value c carry relative rounding errors, so each x - c differs
-// from D (v - g) by at most D 2.01u (|v| + |g|) <= D 32.2u (|v| < 10,
-// |g| <= 6); summed over 16 elements (Cauchy-Schwarz on the cross term),
+// Certified 4/6 decision from each candidate's A and D2 = fl(D^2), D =
+// fl(e s) the decode step, for rows with 2^-50 <= s <= 2^40 and both e != 0.
+// Each candidate's FP32 error err (as the definition computes it) is close
+// to D^2 A.  With u = 2^-24: v = x r and the candidate value c carry relative
+// rounding errors, so each x - c differs from D (v - g) by at most
+// D 2.01u (|v| + |g|) <= D 32.2u (|v| < 10, |g| <= 6); summed over 16
+// elements (Cauchy-Schwarz on the cross term),
 // |sum (x-c)^2 - D^2 S| <= D^2 (258u sqrt(S) + 0.001u) with S the exact sum
 // of (v - g)^2, and sqrt(S) <= (S + 1) / 2 makes that at most
 // D^2 (129u S + 129.001u).  A = S (1 +- 16.1u); the FP32 error is
 // sum (x-c)^2 (1 +- 18.1u), plus at most 2^-145 from underflow, which is
 // below D^2 u / 8 because D >= 2^-9 s >= 2^-59 here.  Together:
-// |err - D^2 A| <= D^2 (163.4u A + 129.3u).  The coefficients below (330u,
-// 260u) are at least twice these, which also covers the three roundings of
-// this arithmetic, and the range of s keeps D^2 normal and every error
-// finite.
-struct ErrBounds {
-  float lo, hi;
-};
-__device__ __forceinline__ ErrBounds err_bounds(float A, float D2) {
+//   |err - D^2 A| <= D^2 (163.4u A + 129.3u).
+// So with P = D4^2 A4 and Q = D6^2 A6, the 4 candidate's error is certainly
+// lower when Q - P > 163.4u (P + Q) + 129.3u (D4^2 + D6^2), and certainly
+// not lower (6 kept, ties included) when P - Q exceeds the same margin.
+// Below, P, Q, their difference and sum, D4^2 + D6^2 and the margin M are
+// each one FP32 rounding (relative u each, D2 = fl(D^2) one more), so the
+// computed Q - P is within 2.01u (P + Q) of the exact one and the computed
+// M is at least 329.9u (P + Q) + 259.9u (D4^2 + D6^2): a computed
+// |Q - P| > M implies the exact difference exceeds 327u (P + Q) +
+// 259u (D4^2 + D6^2), twice the margin needed.  The range of s keeps every
+// D^2 normal and every product finite.  Returns whether the decision is
+// certified; four says which.
+__device__ __forceinline__ bool certified_four(float A6, float D2_6, float A4, float D2_4,
+                                               bool& four) {
   constexpr float u = 0x1p-24f;
-  const float hi = __builtin_fmaf(A, 1.0f + 330.0f * u, 260.0f * u);
-  const float lo = __builtin_fmaf(A, 1.0f - 330.0f * u, -260.0f * u);
-  return {D2 * lo, D2 * hi};
+  const float P = D2_4 * A4, Q = D2_6 * A6;
+  const float diff = Q - P;
+  const float M = __builtin_fmaf(P + Q, 330.0f * u, (D2_4 + D2_6) * (260.0f * u));
+  four = diff > M;
+  return fabsf(diff) > M;
 }
 
 // One element of a candidate by the portable definition: |x| r may be
@@ -538,11 +546,11 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
       // error, keep 6
       four = false;
       bool decided = eb == 0u;
-      if (rs.certify && (eb & 0xFFu) != 0u && (eb >> 8) != 0u) {  // both e nonzero
-        const ErrBounds b6 = err_bounds(A6, t6.y), b4 = err_bounds(A4, t4.y);
-        four = b4.hi < b6.lo;
-        decided = four || b4.lo >= b6.hi;
-      }
+      // both e nonzero: the 4 candidate's byte is never below the 6
+      // candidate's (both round b / (k s) to nearest, monotonically, and
+      // b / (6 s) < b / (4 s)), so a nonzero 6 byte is enough
+      if (rs.certify && (eb & 0xFFu) != 0u)
+        decided = certified_four(A6, t6.y, A4, t4.y, four);
       if (__builtin_expect(!decided, 0))
         four = exact_error(x, code4, e4m3_value<1>(eb), rs.s, neg_zero) <
                exact_error(x, code, e4m3_value<0>(eb), rs.s, neg_zero);
