@@ -145,6 +145,19 @@ namespace {
 #define FP4Q_NV_STREAM 0
 #endif
 
+// Build-time knob: FP4Q_GLOBAL_REVERSE = 1 quantizes the row groups of the
+// global-scale call's second pass from last to first, starting with the
+// rows the tensor-max pass read last (60.3 against 60.5 us on moe_act).
+#ifndef FP4Q_GLOBAL_REVERSE
+#define FP4Q_GLOBAL_REVERSE 1
+#endif
+// Build-time knob: the cache-policy bits of the global-scale call's second
+// pass's input copies (the tensor the max pass has just read): ordinary or
+// sc1 copies measured 62.4 us against 60.3 for non-temporal ones.
+#ifndef FP4Q_GLOBAL_LOAD_AUX
+#define FP4Q_GLOBAL_LOAD_AUX FP4Q_NV_LOAD_AUX
+#endif
+
 constexpr int kMaxWgWaves = 16;  // rows of up to 16 waves use the split kernel
 constexpr int kLongWaves = 4;    // rows per workgroup of the long-row kernel
 
@@ -695,11 +708,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // instruction straight into the wave's LDS tile (1 KiB contiguous per
 // instruction), then reads its own blocks back.  Lanes whose half-block
 // lies past the chunk's end copy nothing.
-template <int NB>
+template <int NB, int kAux = FP4Q_NV_LOAD_AUX>
 __device__ __forceinline__ void issue_chunk_lds(const uint4* __restrict__ x, int64_t cbase,
                                                 int valid, int lane, uint4* tile) {
   const uint4* xc = x + 2 * cbase;
-  constexpr int kAux = FP4Q_NV_LOAD_AUX;
   if (valid == 64 * NB) {
     // a whole chunk: one base pair, the KiB steps in the instruction's
     // offset, which moves the global and the LDS address alike
@@ -732,10 +744,10 @@ __device__ __forceinline__ void read_tile(const uint4* tile, int lane, uint32_t 
   }
 }
 
-template <int NB>
+template <int NB, int kAux = FP4Q_NV_LOAD_AUX>
 __device__ __forceinline__ void load_chunk_lds(const uint4* __restrict__ x, const ChunkRef& c,
                                                int lane, uint4* tile, uint32_t (&w)[NB][8]) {
-  issue_chunk_lds<NB>(x, c.cbase, c.valid, lane, tile);
+  issue_chunk_lds<NB, kAux>(x, c.cbase, c.valid, lane, tile);
   __builtin_amdgcn_s_waitcnt(0);  // the copies have landed in LDS
   read_tile<NB>(tile, lane, w);
 }
@@ -765,13 +777,17 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   // for every wave < 16 and W <= 16
   const int rw = (wave * wdiv) >> 16, chunk = wave - rw * W;  // wave-uniform
 
-  const ChunkRef c =
-      chunk_ref<NB>(blockIdx.x, rw, chunk, R, nblk, row0, row_end, rows, offs, ngroups);
+  // with one scale for the whole tensor (FP4Q_GLOBAL_REVERSE) the row
+  // groups go last to first, so that the rows the tensor-max pass read last
+  // -- the likeliest still in the last-level cache -- are read first
+  const int64_t g = (FP4Q_GLOBAL_REVERSE && gpart != nullptr) ? gridDim.x - 1 - blockIdx.x
+                                                               : blockIdx.x;
+  const ChunkRef c = chunk_ref<NB>(g, rw, chunk, R, nblk, row0, row_end, rows, offs, ngroups);
   uint4 gp = make_uint4(0u, 0u, 0u, 0u);
   if (gpart != nullptr) gp = load_partials(gpart, npart16, lane);
   uint32_t w[NB][8];
   if (kLdsLoad)
-    load_chunk_lds<NB>(x, c, lane, wave_lds, w);
+    load_chunk_lds<NB, NTC ? FP4Q_GLOBAL_LOAD_AUX : FP4Q_NV_LOAD_AUX>(x, c, lane, wave_lds, w);
   else
     load_chunk<NB>(x, c, lane, w);
   uint32_t bmax[NB];
@@ -1259,14 +1275,24 @@ static_assert(FP4Q_GAMAX_GRID >= 1 && 2 * ((FP4Q_GAMAX_GRID + 7) / 8 * 8) <=
 #ifndef FP4Q_GAMAX_NT
 #define FP4Q_GAMAX_NT 0
 #endif
+// Build-time knob: threads per workgroup of the tensor max pass (256, 512
+// or 1024; one partial maximum per workgroup either way).  More waves in
+// flight made the whole call slower on moe_act: 61.5 us with 1024 threads,
+// 62.3 with 512, against 60.5 with 256.  (Loads with the sc0 or sc1 bits,
+// through buffer instructions, made no difference: 60.4-60.5 us.)
+#ifndef FP4Q_GAMAX_THREADS
+#define FP4Q_GAMAX_THREADS 256
+#endif
+static_assert(FP4Q_GAMAX_THREADS == 256 || FP4Q_GAMAX_THREADS == 512 ||
+                  FP4Q_GAMAX_THREADS == 1024, "whole wavefronts, at most 1024 threads");
 
-__global__ __launch_bounds__(256) void global_amax_pass(const uint4* __restrict__ x,
-                                                        int64_t n16,
-                                                        uint16_t* __restrict__ partial) {
-  __shared__ uint32_t wmax[4];
+__global__ __launch_bounds__(FP4Q_GAMAX_THREADS) void global_amax_pass(
+    const uint4* __restrict__ x, int64_t n16, uint16_t* __restrict__ partial) {
+  constexpr int T = FP4Q_GAMAX_THREADS;
+  __shared__ uint32_t wmax[T / 64];
   uint32_t m = 0u;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * T;
+  int64_t i = (int64_t)blockIdx.x * T + threadIdx.x;
   constexpr int D = FP4Q_GAMAX_DEPTH;
   for (; i + (D - 1) * stride < n16; i += D * stride) {  // D loads in flight per lane
     uint4 a[D];
@@ -1297,8 +1323,12 @@ __global__ __launch_bounds__(256) void global_amax_pass(const uint4* __restrict_
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0)
-    partial[blockIdx.x] = (uint16_t)(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) >> 16);
+  if (threadIdx.x == 0) {
+    uint32_t b = 0u;
+#pragma unroll
+    for (int k = 0; k < T / 64; ++k) b = max(b, wmax[k]);
+    partial[blockIdx.x] = (uint16_t)(b >> 16);
+  }
   // zeros (the identity of the max) up to a whole 16-byte unit
   const unsigned padded = (gridDim.x + 7u) & ~7u;
   if (blockIdx.x == 0 && gridDim.x + threadIdx.x < padded) partial[gridDim.x + threadIdx.x] = 0;
@@ -1373,7 +1403,7 @@ namespace {
 // Workgroups of the tensor-max pass for rows x hidden.
 int64_t global_amax_grid(int64_t rows, int64_t hidden) {
   const int64_t n16 = rows * hidden / 8;  // 16-byte units
-  const int64_t grid = (n16 + 255) / 256;
+  const int64_t grid = (n16 + FP4Q_GAMAX_THREADS - 1) / FP4Q_GAMAX_THREADS;
   return grid < FP4Q_GAMAX_GRID ? grid : FP4Q_GAMAX_GRID;
 }
 }  // namespace
@@ -1389,7 +1419,7 @@ hipError_t nvfp4_quantize_global_launch(const NvQuantArgs& args, float* tensor_s
   const int64_t grid = global_amax_grid(a.rows, a.hidden);
   // grid 16-bit maxima, zero-padded to whole 16-byte units
   uint16_t* partial = static_cast<uint16_t*>(workspace);
-  hipLaunchKernelGGL(global_amax_pass, dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL(global_amax_pass, dim3((unsigned)grid), dim3(FP4Q_GAMAX_THREADS), 0, st,
                      (const uint4*)a.x, n16, partial);
   a.global_partials = reinterpret_cast<const uint4*>(partial);
   a.num_partials = (int)((grid + 7) / 8);
