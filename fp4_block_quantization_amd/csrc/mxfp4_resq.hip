@@ -207,14 +207,7 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
     uint8_t* __restrict__ res_meta, uint8_t* __restrict__ res_scales, int stage) {
   typedef StageLayout<DENSE> SL;
   __shared__ uint4 stage_lds[FP4Q_MX_LDS_STAGE ? 4 * SL::kPieces : 1];
-  // the 2:4 table (8 KiB) into LDS
   __shared__ uint4 tab_lds[DENSE ? 1 : 512];
-  if (!DENSE) {
-    const uint4* tab_src = reinterpret_cast<const uint4*>(kSelTable.e);
-    tab_lds[threadIdx.x] = tab_src[threadIdx.x];
-    tab_lds[threadIdx.x + 256] = tab_src[threadIdx.x + 256];
-    __syncthreads();
-  }
   const uint16_t* tab = reinterpret_cast<const uint16_t*>(tab_lds);
 
   const int lane = threadIdx.x & 63;
@@ -223,8 +216,9 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   // quads are whole
   const int64_t ub = u0 + ((int64_t)blockIdx.x * 4 + wave) * 64 * kUnitsPerLane;
   const int64_t left = u_end - ub;  // units of this wave that exist (may be <= 0)
-  if (left <= 0) return;
-  const int nv = left < 64 * kUnitsPerLane ? (int)left : 64 * kUnitsPerLane;
+  // a wave past the end loads nothing but still writes its share of the
+  // table and meets the barrier below before it leaves
+  const int nv = left <= 0 ? 0 : left < 64 * kUnitsPerLane ? (int)left : 64 * kUnitsPerLane;
   const uint4* xw = x + ub;  // wave-uniform bases, 32-bit lane offsets
   uint32_t* cw_out = codes + ub;
   uint8_t* sc_out = scales + (ub >> 2);
@@ -244,6 +238,17 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
         a[n] = *src;
       }
     }
+  // the 2:4 table (8 KiB) into LDS, its loads issued after the wave's own so
+  // that the two latencies overlap (loading it first and waiting for it
+  // before the input loads cost a second memory round trip per workgroup)
+  if (!DENSE) {
+    const uint4* tab_src = reinterpret_cast<const uint4*>(kSelTable.e);
+    const uint4 t0 = tab_src[threadIdx.x], t1 = tab_src[threadIdx.x + 256];
+    tab_lds[threadIdx.x] = t0;
+    tab_lds[threadIdx.x + 256] = t1;
+    __syncthreads();
+  }
+  if (nv == 0) return;
 #pragma unroll
   for (int n = 0; n < kUnitsPerLane; ++n) {
     const int j = lane + 64 * n;
