@@ -251,8 +251,11 @@ def standin_nvfp4(S, s, offs=None, fos=1):
 
 def host_cpu():
     """CPU model, logical CPUs and physical cores the host reports, and the
-    CPUs this process may run on."""
+    CPUs this process may run on.  A virtual machine may show a generic
+    model name; the CPUID family/model/stepping and the widest vector
+    extensions then still place the CPU's generation."""
     model, phys = "unknown", set()
+    cpuid, vec = None, []
     cur = {}
     try:
         for line in open("/proc/cpuinfo"):
@@ -265,6 +268,12 @@ def host_cpu():
             cur[k] = v
             if k == "model name" and model == "unknown":
                 model = v
+            if k == "stepping" and cpuid is None:
+                cpuid = "family %s model %s stepping %s" % (cur.get("cpu family"),
+                                                              cur.get("model"), v)
+            if k == "flags" and not vec:
+                f = set(v.split())
+                vec = [e for e in ("avx2", "avx512f", "avx512_bf16", "avx512_vnni") if e in f]
         if cur:
             phys.add((cur.get("physical id"), cur.get("core id")))
     except OSError:
@@ -273,7 +282,8 @@ def host_cpu():
         usable = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
         usable = os.cpu_count()
-    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(),
+    return {"cpu_model": model, "cpuid": cpuid, "vector_extensions": vec,
+            "host_logical_cpus": os.cpu_count(),
             "host_physical_cores": len(phys) if phys and None not in next(iter(phys)) else None,
             "cpus_usable_by_this_process": usable}
 

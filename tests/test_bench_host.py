@@ -106,3 +106,5 @@ def test_host_cpu_description():
     d = bench.host_cpu()
     assert d["cpus_usable_by_this_process"] >= 1 and d["host_logical_cpus"] >= 1
     assert isinstance(d["cpu_model"], str)
+    assert d["cpuid"] is None or d["cpuid"].startswith("family ")
+    assert isinstance(d["vector_extensions"], list)
