@@ -1160,6 +1160,10 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
   const uint4* xin = x + base;
   const uint32_t* gin = RTN ? nullptr : guide + base;
   const uint8_t* sin = scales + (base >> 1);
+  // Unit by unit: each unit's loads are issued after the previous unit's
+  // stores.  Requesting every unit's inputs before using the first (so that
+  // the wave has them all in flight) measured slower: 31.3 against 28.7 us
+  // guided, 27.6 against 26.3 us to nearest, on moe_act.
 #pragma unroll
   for (int n = 0; n < NU; ++n) {
     const int j = lane + 64 * n;
