@@ -16,7 +16,7 @@ KNOBS = {
                   "FP4Q_NV_NT_CODES=0", "FP4Q_NV_NT_CODES=1", "FP4Q_NV_NT_LOADS=0",
                   "FP4Q_NV_LDS_DQ=0", "FP4Q_NV_WG_WAVES=2", "FP4Q_NV_LDS_LOAD=0",
                   "FP4Q_NV_NB=1", "FP4Q_NV_NB=3", "FP4Q_NV_NB=4", "FP4Q_DQ_UNITS=1",
-                  "FP4Q_DQ_UNITS=4", "FP4Q_DQ_NT_STORES=0", "FP4Q_DQ_NT_LOADS=3",
+                  "FP4Q_DQ_UNITS=2", "FP4Q_GUIDED_UNITS=2", "FP4Q_DQ_NT_STORES=0", "FP4Q_DQ_NT_LOADS=3",
                   "FP4Q_GUIDED_NT_LOADS=0", "FP4Q_GUIDED_NT_LOADS=3", "FP4Q_GAMAX_NT=1",
                   "FP4Q_GAMAX_DEPTH=2", "FP4Q_GAMAX_GRID=256", "FP4Q_NV_STREAM=1",
                   "FP4Q_NV_STREAM_DEFER=0", "FP4Q_NV_STREAM_GRID=4096", "FP4Q_STANDIN=1",
