@@ -72,9 +72,10 @@ namespace {
 //   FP4Q_NV_NT_POLICY     the non-temporal code and block-scale stores;
 //   FP4Q_NV_PLAIN_POLICY  the other code and block-scale stores.
 // nt with sc1 on the dequant stream measured faster than nt alone on MI355X
-// (the dequant call 19.8 against 22.1 us, the headline 42.8 against 43.3 us;
-// writes of 256 MiB 43.0 against 44.1 us); on the code stores of the
-// routed-token workload it gained nothing.
+// (the headline 42.6 against 43.6 us and 43.5 against 43.8 us on two boxes,
+// the dequant call 23.6 against 23.8 us with distinct codes per call; K0
+// writes of 256 MiB 42.1 against 43.5 us); on the code stores of the
+// routed-token workload it gained nothing, and sc1 without nt was slower.
 #ifndef FP4Q_NV_DQ_POLICY
 #define FP4Q_NV_DQ_POLICY (FP4Q_NV_NT_STORES ? 18 : -1)
 #endif
