@@ -132,6 +132,15 @@ __device__ __forceinline__ uint32_t select_2of4(uint32_t rw, const uint16_t* tab
 #define FP4Q_MX_UNITS 4
 #endif
 constexpr int kUnitsPerLane = FP4Q_MX_UNITS;
+// Build-time knob: wavefronts per workgroup of the quantize kernels (4, 8 or
+// 16); each workgroup copies the 8 KiB 2:4 table into LDS once.  Fewer
+// table copies did not pay: resq_act 8192 x 7168 took 31.0 us with 8 and
+// 33.9 us with 16 against 29.9 us with 4.
+#ifndef FP4Q_MX_WG_WAVES
+#define FP4Q_MX_WG_WAVES 4
+#endif
+constexpr int kMxWaves = FP4Q_MX_WG_WAVES;
+static_assert(kMxWaves == 4 || kMxWaves == 8 || kMxWaves == 16, "4, 8 or 16 wavefronts");
 
 // Build-time knob: FP4Q_STANDIN = 1 builds a memory-pattern stand-in for
 // measurement only (libfp4q_standin.so, never the quantizer): the same
@@ -201,12 +210,12 @@ struct StageLayout {
 };
 
 template <bool DENSE>
-__global__ __launch_bounds__(256) void mxfp4_resq_units(
+__global__ __launch_bounds__(64 * kMxWaves) void mxfp4_resq_units(
     const uint4* __restrict__ x, int64_t u0, int64_t u_end, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, void* __restrict__ res_codes,
     uint8_t* __restrict__ res_meta, uint8_t* __restrict__ res_scales, int stage) {
   typedef StageLayout<DENSE> SL;
-  __shared__ uint4 stage_lds[FP4Q_MX_LDS_STAGE ? 4 * SL::kPieces : 1];
+  __shared__ uint4 stage_lds[FP4Q_MX_LDS_STAGE ? kMxWaves * SL::kPieces : 1];
   __shared__ uint4 tab_lds[DENSE ? 1 : 512];
   const uint16_t* tab = reinterpret_cast<const uint16_t*>(tab_lds);
 
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // first unit of this wave (uniform); u0 and u_end are multiples of 4, so
   // quads are whole
-  const int64_t ub = u0 + ((int64_t)blockIdx.x * 4 + wave) * 64 * kUnitsPerLane;
+  const int64_t ub = u0 + ((int64_t)blockIdx.x * kMxWaves + wave) * 64 * kUnitsPerLane;
   const int64_t left = u_end - ub;  // units of this wave that exist (may be <= 0)
   // a wave past the end loads nothing but still writes its share of the
   // table and meets the barrier below before it leaves
@@ -243,9 +252,14 @@ __global__ __launch_bounds__(256) void mxfp4_resq_units(
   // before the input loads cost a second memory round trip per workgroup)
   if (!DENSE) {
     const uint4* tab_src = reinterpret_cast<const uint4*>(kSelTable.e);
-    const uint4 t0 = tab_src[threadIdx.x], t1 = tab_src[threadIdx.x + 256];
-    tab_lds[threadIdx.x] = t0;
-    tab_lds[threadIdx.x + 256] = t1;
+    constexpr int kPer = 512 / (64 * kMxWaves);  // 16-byte table pieces per thread
+    uint4 t[kPer > 0 ? kPer : 1];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) t[k] = tab_src[threadIdx.x + 64 * kMxWaves * k];
+    if (kPer == 0 && threadIdx.x < 512) t[0] = tab_src[threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) tab_lds[threadIdx.x + 64 * kMxWaves * k] = t[k];
+    if (kPer == 0 && threadIdx.x < 512) tab_lds[threadIdx.x] = t[0];
     __syncthreads();
   }
   if (nv == 0) return;
@@ -416,8 +430,8 @@ hipError_t resq_launch(const void* x, int64_t rows, int64_t hidden, uint8_t* cod
                     (DENSE || a16(res_meta));
   for (int64_t u0 = 0; u0 < nunits; u0 += max_units) {
     const int64_t n = nunits - u0 < max_units ? nunits - u0 : max_units;
-    constexpr int64_t per_wg = 256 * kUnitsPerLane;
-    const dim3 grid((unsigned)((n + per_wg - 1) / per_wg)), block(256);
+    constexpr int64_t per_wg = 64 * kMxWaves * kUnitsPerLane;
+    const dim3 grid((unsigned)((n + per_wg - 1) / per_wg)), block(64 * kMxWaves);
     hipLaunchKernelGGL(mxfp4_resq_units<DENSE>, grid, block, 0, st, (const uint4*)x, u0, u0 + n,
                        (uint32_t*)codes, scales, res_codes, res_meta, res_scales, stage);
   }
