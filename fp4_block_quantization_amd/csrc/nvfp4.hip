@@ -1305,6 +1305,15 @@ static_assert(FP4Q_GAMAX_GRID >= 1 && 2 * ((FP4Q_GAMAX_GRID + 7) / 8 * 8) <=
 #ifndef FP4Q_GAMAX_NT
 #define FP4Q_GAMAX_NT 0
 #endif
+// Build-time knob: FP4Q_GAMAX_CHUNKED = 1 gives each wavefront of the max
+// pass whole chunks of D contiguous KiB (the grid striding over chunks, as
+// K0 reads); 0 strides every lane over single 16-byte units, so that a
+// wavefront's D loads in flight lie a whole grid apart.  Chunks: max pass
+// 18.8 against 19.7 us on moe_act (2 KiB chunks 21.6 us, 8 KiB 19.1 us;
+// 512 or 1024 threads per workgroup 19.5 and 20.7 us).
+#ifndef FP4Q_GAMAX_CHUNKED
+#define FP4Q_GAMAX_CHUNKED 1
+#endif
 // Build-time knob: threads per workgroup of the tensor max pass (256, 512
 // or 1024; one partial maximum per workgroup either way).  More waves in
 // flight made the whole call slower on moe_act: 61.5 us with 1024 threads,
@@ -1321,9 +1330,44 @@ __global__ __launch_bounds__(FP4Q_GAMAX_THREADS) void global_amax_pass(
   constexpr int T = FP4Q_GAMAX_THREADS;
   __shared__ uint32_t wmax[T / 64];
   uint32_t m = 0u;
-  const int64_t stride = (int64_t)gridDim.x * T;
-  int64_t i = (int64_t)blockIdx.x * T + threadIdx.x;
   constexpr int D = FP4Q_GAMAX_DEPTH;
+  if (FP4Q_GAMAX_CHUNKED) {
+    // each wavefront reads whole chunks of 64 D consecutive units (D
+    // contiguous KiB), chunk k going to wavefront k mod (all wavefronts), so
+    // a step of the grid covers one contiguous stretch of the tensor
+    const int lane = threadIdx.x & 63;
+    constexpr int64_t CH = 64 * D;
+    const int64_t nwaves = (int64_t)gridDim.x * (T / 64);
+    int64_t base =
+        ((int64_t)blockIdx.x * (T / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * CH;
+    for (; base + CH <= n16; base += nwaves * CH) {  // whole chunks
+      uint4 a[D];
+#pragma unroll
+      for (int u = 0; u < D; ++u) a[u] = x[base + 64 * u + lane];
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const uint32_t w[4] = {a[u].x & 0x7FFF7FFFu, a[u].y & 0x7FFF7FFFu, a[u].z & 0x7FFF7FFFu,
+                               a[u].w & 0x7FFF7FFFu};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max(w[k] << 16, w[k] & 0xFFFF0000u));
+      }
+    }
+    if (base < n16) {  // the one partial chunk at the end of the tensor
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int64_t idx = base + 64 * u + lane;
+        if (idx < n16) {
+          const uint4 a = x[idx];
+          const uint32_t w[4] = {a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu, a.z & 0x7FFF7FFFu,
+                                 a.w & 0x7FFF7FFFu};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) m = max(m, max(w[k] << 16, w[k] & 0xFFFF0000u));
+        }
+      }
+    }
+  }
+  const int64_t stride = (int64_t)gridDim.x * T;
+  int64_t i = FP4Q_GAMAX_CHUNKED ? n16 : (int64_t)blockIdx.x * T + threadIdx.x;
   for (; i + (D - 1) * stride < n16; i += D * stride) {  // D loads in flight per lane
     uint4 a[D];
 #pragma unroll
