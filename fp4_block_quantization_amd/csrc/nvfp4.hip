@@ -1211,7 +1211,10 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
   // Unit by unit: each unit's loads are issued after the previous unit's
   // stores.  Requesting every unit's inputs before using the first (so that
   // the wave has them all in flight) measured slower: 31.3 against 28.7 us
-  // guided, 27.6 against 26.3 us to nearest, on moe_act.
+  // guided, 27.6 against 26.3 us to nearest, on moe_act; so did copying the
+  // wave's 4 KiB of input into LDS with global_load_lds and its guide words
+  // and scale bytes into registers before one wait (35.1 against 28.0 us
+  // guided, 28.0 against 25.4 us to nearest).
 #pragma unroll
   for (int n = 0; n < NU; ++n) {
     const int j = lane + 64 * n;

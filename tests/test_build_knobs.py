@@ -28,7 +28,8 @@ KNOBS = {
                        "FP4Q_MX_NT_SMALL=1", "FP4Q_MX_UNITS=1", "FP4Q_MX_UNITS=2",
                        "FP4Q_MX_UNITS=8", "FP4Q_MX_REC_STAGE=0", "FP4Q_MX_REC_NT=0",
                        "FP4Q_STANDIN=1", "FP4Q_MX_POLICY=18", "FP4Q_MX_SMALL_POLICY=18",
-                       "FP4Q_MX_REC_POLICY=2", "FP4Q_MX_WG_WAVES=8", "FP4Q_MX_WG_WAVES=16"],
+                       "FP4Q_MX_REC_POLICY=2", "FP4Q_MX_WG_WAVES=8", "FP4Q_MX_WG_WAVES=16",
+                       "FP4Q_MX_FLOAT_MAX=0"],
     "membench.hip": ["FP4Q_K0_UNITS=8", "FP4Q_K0_UNITS=16"],
 }
 
