@@ -136,6 +136,38 @@ def test_nvfp4_edge_suite_no_dequant(H, reps, fos):
     check_nvfp4(x, fos, dequant=False, label="edge no-dequant H=%d x%d" % (H, reps))
 
 
+def every_bf16_rows(H, seed):
+    """Every finite BF16 pattern once (both signs, subnormals and zeros
+    included), ordered by magnitude and cut into rows of H (the last padded
+    with zeros), so that each row spans a few binades; the elements of every
+    other row are shuffled, so its blocks mix those magnitudes."""
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    pats = pats[(pats & 0x7F80) != 0x7F80]  # no infinities or NaNs (outside the domain)
+    pats = pats[np.lexsort((pats >> 15, pats & 0x7FFF))].astype(np.uint16)
+    rows = -(-pats.size // H)
+    x = np.zeros(rows * H, np.uint16)
+    x[:pats.size] = pats
+    x = x.reshape(rows, H)
+    rng = np.random.default_rng(seed)
+    for r in range(1, rows, 2):
+        x[r] = x[r, rng.permutation(H)]
+    return x
+
+
+# the split kernel's one-wave rows without dequant (the FP32 block maximum)
+# and its four-wave rows with dequant (the packed one), in every mode
+@pytest.mark.parametrize("fos", [1, 0, 2])
+@pytest.mark.parametrize("H,dequant", [(2048, False), (2048, True), (7168, True), (7168, False)])
+def test_nvfp4_every_bf16_value(H, dequant, fos):
+    check_nvfp4(every_bf16_rows(H, seed=H), fos, dequant=dequant,
+                label="every BF16 value H=%d dq=%d" % (H, dequant))
+
+
+@pytest.mark.parametrize("H", [2048, 7168])
+def test_mx_every_bf16_value(H):
+    check_mx(every_bf16_rows(H, seed=H + 3), label="mx every BF16 value H=%d" % H)
+
+
 @pytest.mark.parametrize("H", [32, 64, 96, 2048, 7200])
 def test_mx_edge_suite(H):
     check_mx(edge_rows(H, seed=H + 1), label="mx edge H=%d" % H)
