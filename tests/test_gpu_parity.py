@@ -445,6 +445,15 @@ def test_guided_edge_rows(H):
     check_guided(edge_rows(H, seed=H + 99), x, "nearest cross H=%d" % H, guided=False)
 
 
+@pytest.mark.parametrize("H", [2048, 7168])
+def test_guided_every_bf16_value(H):
+    x = every_bf16_rows(H, seed=H + 11)
+    check_guided(x, workloads.perturbed(x, seed=H + 1), "guided every BF16 value H=%d" % H)
+    check_guided(x, x, "guided self every BF16 value H=%d" % H)
+    check_guided(x, workloads.perturbed(x, seed=H + 1), "nearest every BF16 value H=%d" % H,
+                 guided=False)
+
+
 def test_guided_random_guides_and_scales():
     # arbitrary guide bytes and block scales (every branch of the rule)
     rng = np.random.default_rng(77)
