@@ -1189,7 +1189,7 @@ __global__ __launch_bounds__(256) void nvfp4_dequantize_rows(
 // mapped like the dequant kernel.  RTN (no guide): each element takes its
 // nearest codeword under the same scales instead -- the training side's own
 // rounding that the page compares guided rounding with.
-template <bool RTN>
+template <bool RTN, bool DQ>
 __global__ __launch_bounds__(256) void nvfp4_guided_units(
     const uint4* __restrict__ x, const uint32_t* __restrict__ guide,
     const uint8_t* __restrict__ scales, const float* __restrict__ tscale, int64_t row0,
@@ -1214,7 +1214,12 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
   // guided, 27.6 against 26.3 us to nearest, on moe_act; so did copying the
   // wave's 4 KiB of input into LDS with global_load_lds and its guide words
   // and scale bytes into registers before one wait (35.1 against 28.0 us
-  // guided, 28.0 against 25.4 us to nearest).
+  // guided, 28.0 against 25.4 us to nearest), and so did issuing unit
+  // n + 1's loads before unit n's arithmetic, with one wait ahead of unit
+  // n's stores (28.9 against 28.0 us guided; to nearest 25.1 either way).
+  // The dequant output is a template argument, so that an instance issues
+  // the same memory operations for every unit (28.3 -> 28.0 us guided, 25.4
+  // -> 25.2 us to nearest, without the dequant).
 #pragma unroll
   for (int n = 0; n < NU; ++n) {
     const int j = lane + 64 * n;
@@ -1308,7 +1313,7 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
       }
     }
     store_words(codes + base, j, out);
-    if (dq != nullptr) {
+    if (DQ) {
       uint32_t o[4];
       static_for<0, 4>([&](auto P) {
         constexpr int k = decltype(P)::value;
@@ -1585,14 +1590,19 @@ hipError_t nvfp4_guided_launch(const void* x, const uint8_t* guide, const uint8_
   for (int64_t row0 = 0; row0 < rows; row0 += max_rows) {
     const int64_t n = rows - row0 < max_rows ? rows - row0 : max_rows;
     const dim3 grid((unsigned)((n * wpr + 3) / 4)), block(256);
+    // the guide's presence and the dequant output are template arguments, so
+    // that each instance issues a fixed run of memory operations per unit
+    auto launch = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, block, 0, st, (const uint4*)x, (const uint32_t*)guide,
+                         scales, tscale, row0, row0 + n, h8, wpr, (uint32_t*)codes,
+                         (uint4*)dequant);
+    };
     if (guide != nullptr)
-      hipLaunchKernelGGL(nvfp4_guided_units<false>, grid, block, 0, st, (const uint4*)x,
-                         (const uint32_t*)guide, scales, tscale, row0, row0 + n, h8, wpr,
-                         (uint32_t*)codes, (uint4*)dequant);
+      dequant != nullptr ? launch(nvfp4_guided_units<false, true>)
+                         : launch(nvfp4_guided_units<false, false>);
     else
-      hipLaunchKernelGGL(nvfp4_guided_units<true>, grid, block, 0, st, (const uint4*)x,
-                         (const uint32_t*)nullptr, scales, tscale, row0, row0 + n, h8, wpr,
-                         (uint32_t*)codes, (uint4*)dequant);
+      dequant != nullptr ? launch(nvfp4_guided_units<true, true>)
+                         : launch(nvfp4_guided_units<true, false>);
   }
   return hipGetLastError();
 }
