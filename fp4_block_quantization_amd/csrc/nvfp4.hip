@@ -125,16 +125,15 @@ namespace {
 #ifndef FP4Q_NV_NB
 #define FP4Q_NV_NB 2
 #endif
-// Build-time knob: how the split kernel takes its block maxima.  0: a
-// packed 16-bit integer maximum of the sign-cleared BF16 words, before
-// unpacking.  1: three-input maxima of the magnitudes of the unpacked FP32
-// values, which the quantization then reuses (8 fewer VALU instructions per
-// block, 16 more live registers; 65536 x 2048 routed rows without dequant
-// 60.4 -> 56.8 us).  2: 1 in every instance but the per-token
-// FP32-decision one with dequant, where 0 is kept (the two forms measured
-// alike there, 0.2 us apart at most).
+// Build-time knob: how the split kernel takes its block maxima.  1:
+// three-input maxima of the magnitudes of the unpacked FP32 values, which
+// the quantization then reuses (8 fewer VALU instructions per block, 16
+// more live registers; 65536 x 2048 routed rows without dequant 60.4 ->
+// 56.8 us, 65536 x 7168 with dequant 318.6 -> 316.2 us, 8192 x 7168 with
+// dequant the same).  0: a packed 16-bit integer maximum of the
+// sign-cleared BF16 words, before unpacking.
 #ifndef FP4Q_NV_FLOAT_MAX
-#define FP4Q_NV_FLOAT_MAX 2
+#define FP4Q_NV_FLOAT_MAX 1
 #endif
 
 // Build-time knob: FP4Q_STANDIN = 1 builds a memory-pattern stand-in of the
@@ -839,9 +838,7 @@ __global__ __launch_bounds__(64 * kMaxWgWaves) void nvfp4_quantize_split(
   }
   // the blocks' values (FP32), unpacked once for the block maxima and the
   // quantization (FP4Q_NV_FLOAT_MAX)
-  constexpr bool kFloatMax =
-      !FP4Q_STANDIN && (FP4Q_NV_FLOAT_MAX == 1 ||
-                        (FP4Q_NV_FLOAT_MAX == 2 && !(FOS == 1 && DQ && !kGlobal)));
+  constexpr bool kFloatMax = FP4Q_NV_FLOAT_MAX && !FP4Q_STANDIN;
   float xv[NB][16];
   uint32_t bmax[NB];
   uint32_t lmax = 0;

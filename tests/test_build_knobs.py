@@ -23,7 +23,7 @@ KNOBS = {
                   "FP4Q_NV_DQ_POLICY=2", "FP4Q_NV_DQ_POLICY=-1", "FP4Q_NV_NT_POLICY=18",
                   "FP4Q_NV_PLAIN_POLICY=16", "FP4Q_DQ_POLICY=19", "FP4Q_NV_LOAD_AUX=18",
                   "FP4Q_GLOBAL_REVERSE=0", "FP4Q_GLOBAL_LOAD_AUX=0", "FP4Q_GAMAX_THREADS=1024",
-                  "FP4Q_GAMAX_CHUNKED=0", "FP4Q_NV_FLOAT_MAX=0", "FP4Q_NV_FLOAT_MAX=1"],
+                  "FP4Q_GAMAX_CHUNKED=0", "FP4Q_NV_FLOAT_MAX=0"],
     "mxfp4_resq.hip": ["FP4Q_MX_LDS_STAGE=0", "FP4Q_MX_NT_LOADS=0", "FP4Q_MX_NT_STORES=0",
                        "FP4Q_MX_NT_SMALL=1", "FP4Q_MX_UNITS=1", "FP4Q_MX_UNITS=2",
                        "FP4Q_MX_UNITS=8", "FP4Q_MX_REC_STAGE=0", "FP4Q_MX_REC_NT=0",
