@@ -46,6 +46,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 #ifndef FP4Q_MX_POLICY
 #define FP4Q_MX_POLICY (FP4Q_MX_NT_STORES ? 2 : -1)
 #endif
+// Build-time knob: the cache-policy bits of the staged 16-byte pieces of
+// the metadata and both scale outputs (256 and 64 bytes a wave).  sc1
+// measured fastest on resq_act (29.2 us, dense 30.45) against nt (30.0,
+// 30.7), none (29.3, 30.8) and nt with sc1 (30.0, 31.0); sc1 on the code
+// and residual-code pieces as well was slower (30.6, 31.0).
+#ifndef FP4Q_MX_STAGED_SMALL_POLICY
+#define FP4Q_MX_STAGED_SMALL_POLICY 16
+#endif
 #ifndef FP4Q_MX_SMALL_POLICY
 #define FP4Q_MX_SMALL_POLICY (FP4Q_MX_NT_STORES && FP4Q_MX_NT_SMALL ? 2 : -1)
 #endif
@@ -358,11 +366,11 @@ __global__ __launch_bounds__(64 * kMxWaves) void mxfp4_resq_units(
       else if (p < SL::kMetaAt)
         store_out(o_res, p - SL::kResAt, st[p]);
       else if (p < SL::kScAt)
-        store_out(o_meta, p - SL::kMetaAt, st[p]);
+        put<FP4Q_MX_STAGED_SMALL_POLICY>(o_meta, p - SL::kMetaAt, st[p]);
       else if (p < SL::kRscAt)
-        store_out(o_sc, p - SL::kScAt, st[p]);
+        put<FP4Q_MX_STAGED_SMALL_POLICY>(o_sc, p - SL::kScAt, st[p]);
       else if (p < SL::kPieces)
-        store_out(o_rs, p - SL::kRscAt, st[p]);
+        put<FP4Q_MX_STAGED_SMALL_POLICY>(o_rs, p - SL::kRscAt, st[p]);
     }
   }
 }

@@ -182,12 +182,31 @@ __device__ __forceinline__ void store_dq(uint4* base, uint32_t idx, uint4 v) {
 // A block-scale byte and a block's code word: non-temporal per
 // FP4Q_NV_NT_BYTES and FP4Q_NV_NT_CODES (DQ: the call also writes the
 // dequant).
+// Build-time knobs: the block-scale stores' own policies (by default those
+// of the code stores); sc1 measured slower on the routed-token call (58.3
+// against 58.0 us) and the same on the headline.
+#ifndef FP4Q_NV_SCALE_NT_POLICY
+#define FP4Q_NV_SCALE_NT_POLICY FP4Q_NV_NT_POLICY
+#endif
+#ifndef FP4Q_NV_SCALE_PLAIN_POLICY
+#define FP4Q_NV_SCALE_PLAIN_POLICY FP4Q_NV_PLAIN_POLICY
+#endif
+// Build-time knobs: the cache-policy bits of the guided call's code stores
+// (4 bytes per lane) with a guide, and without one (round to nearest).
+// Measured on moe_act (guided / to nearest, us): nt 28.1 / 25.2; sc1
+// 32.3 / 24.2; none 33.5 / 25.2; sc0 33.5 / 25.2; nt with sc1 28.1 / 25.2.
+#ifndef FP4Q_GUIDED_CODE_POLICY
+#define FP4Q_GUIDED_CODE_POLICY 2
+#endif
+#ifndef FP4Q_RTN_CODE_POLICY
+#define FP4Q_RTN_CODE_POLICY 16
+#endif
 template <bool DQ>
 __device__ __forceinline__ void store_scale(uint8_t* base, uint32_t idx, uint8_t v) {
   if constexpr (FP4Q_NV_NT_BYTES == 1 || (FP4Q_NV_NT_BYTES == 2 && !DQ))
-    put<FP4Q_NV_NT_POLICY>(base, idx, v);
+    put<FP4Q_NV_SCALE_NT_POLICY>(base, idx, v);
   else
-    put<FP4Q_NV_PLAIN_POLICY>(base, idx, v);
+    put<FP4Q_NV_SCALE_PLAIN_POLICY>(base, idx, v);
 }
 // NTC: non-temporal whatever the knob says -- the quantize pass of the
 // global-scale call, whose plain code stores would leave dirty lines for the
@@ -199,9 +218,11 @@ __device__ __forceinline__ void store_codes(uint2* base, uint32_t idx, uint2 v) 
   else
     put<FP4Q_NV_PLAIN_POLICY>(base, idx, v);
 }
-// Code words of the guided call (one lane per 8 elements).
+// Code words of the guided call (one lane per 8 elements); RTN: without a
+// guide.
+template <bool RTN>
 __device__ __forceinline__ void store_words(uint32_t* base, uint32_t idx, uint32_t v) {
-  put<FP4Q_NV_NT_POLICY>(base, idx, v);
+  put<RTN ? FP4Q_RTN_CODE_POLICY : FP4Q_GUIDED_CODE_POLICY>(base, idx, v);
 }
 
 template <int I, int N, typename F>
@@ -1312,7 +1333,7 @@ __global__ __launch_bounds__(256) void nvfp4_guided_units(
         out |= ((sx << 3) | q) << (4 * i);
       }
     }
-    store_words(codes + base, j, out);
+    store_words<RTN>(codes + base, j, out);
     if (DQ) {
       uint32_t o[4];
       static_for<0, 4>([&](auto P) {
