@@ -70,12 +70,16 @@ namespace {
 // gfx950 memory instructions encode them (1 sc0, 2 nt, 16 sc1; -1 none):
 //   FP4Q_NV_DQ_POLICY     the BF16 dequant stream;
 //   FP4Q_NV_NT_POLICY     the non-temporal code and block-scale stores;
-//   FP4Q_NV_PLAIN_POLICY  the other code and block-scale stores.
+//   FP4Q_NV_PLAIN_POLICY  the other code and block-scale stores (those
+//                         beside the dequant stream).
 // nt with sc1 on the dequant stream measured faster than nt alone on MI355X
 // (the headline 42.6 against 43.6 us and 43.5 against 43.8 us on two boxes,
 // the dequant call 23.6 against 23.8 us with distinct codes per call; K0
 // writes of 256 MiB 42.1 against 43.5 us); on the code stores of the
 // routed-token workload it gained nothing, and sc1 without nt was slower.
+// Beside the dequant stream, sc1 on the code and scale stores measured
+// 42.67 against 42.82 us (headline, ten rounds side by side; sc0 with sc1
+// 42.71) and 310.9 against 311.3 us on expert weights.
 #ifndef FP4Q_NV_DQ_POLICY
 #define FP4Q_NV_DQ_POLICY (FP4Q_NV_NT_STORES ? 18 : -1)
 #endif
@@ -83,7 +87,7 @@ namespace {
 #define FP4Q_NV_NT_POLICY (FP4Q_NV_NT_STORES ? 2 : -1)
 #endif
 #ifndef FP4Q_NV_PLAIN_POLICY
-#define FP4Q_NV_PLAIN_POLICY -1
+#define FP4Q_NV_PLAIN_POLICY (FP4Q_NV_NT_STORES ? 16 : -1)
 #endif
 
 // Build-time knob: FP4Q_NV_NT_LOADS = 1 makes the contiguous input copies

@@ -21,7 +21,7 @@ KNOBS = {
                   "FP4Q_GAMAX_DEPTH=2", "FP4Q_GAMAX_GRID=256", "FP4Q_NV_STREAM=1",
                   "FP4Q_NV_STREAM_DEFER=0", "FP4Q_NV_STREAM_GRID=4096", "FP4Q_STANDIN=1",
                   "FP4Q_NV_DQ_POLICY=2", "FP4Q_NV_DQ_POLICY=-1", "FP4Q_NV_NT_POLICY=18",
-                  "FP4Q_NV_PLAIN_POLICY=16", "FP4Q_DQ_POLICY=19", "FP4Q_NV_LOAD_AUX=18",
+                  "FP4Q_NV_PLAIN_POLICY=-1", "FP4Q_DQ_POLICY=19", "FP4Q_NV_LOAD_AUX=18",
                   "FP4Q_GLOBAL_REVERSE=0", "FP4Q_GLOBAL_LOAD_AUX=0", "FP4Q_GAMAX_THREADS=1024",
                   "FP4Q_GAMAX_CHUNKED=0", "FP4Q_NV_FLOAT_MAX=0", "FP4Q_NV_SCALE_NT_POLICY=16",
                   "FP4Q_NV_SCALE_PLAIN_POLICY=16", "FP4Q_GUIDED_CODE_POLICY=16",
