@@ -209,3 +209,27 @@ def test_nvfp4_quantize_global_rejects():
     assert g(ts=P(0x10002)) == MISALIGNED
     assert g(dq=A8) == MISALIGNED
     assert g(rows=0, x=None, codes=None, ts=None, ws=None) == SUCCESS
+
+
+def test_nvfp4_quantize_global_noalloc_rejects():
+    # the same validation as the workspace form, without the workspace
+    # argument; every case returns before any HIP call
+    L = fq.lib()
+    f = L.nvfp4_quantize_global_noalloc
+    f.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int] + [P] * 5
+    f.restype = ctypes.c_int
+    g = lambda **k: f(
+        k.get("x", A16), k.get("rows", 4), k.get("hidden", 64), k.get("fos", 1),
+        k.get("codes", A16), A16, k.get("ts", A16), k.get("dq", A16), None)
+    assert g(hidden=24) == SHAPE
+    assert g(rows=-1) == SHAPE
+    assert g(fos=3) == INVALID
+    assert g(fos=-1) == INVALID
+    assert g(x=None) == NULL
+    assert g(codes=None) == NULL
+    assert g(ts=None) == NULL
+    assert g(x=P(0x10008)) == MISALIGNED
+    assert g(codes=P(0x10004)) == MISALIGNED
+    assert g(ts=P(0x10002)) == MISALIGNED
+    assert g(dq=A8) == MISALIGNED
+    assert g(rows=0, x=None, codes=None, ts=None) == SUCCESS
