@@ -8,10 +8,12 @@ resident in HBM.  value = algorithmic bytes per call / mean call time, in GB
 than the 256 MB last-level cache) so repeated calls cannot be served from
 cache.  Each measurement first spins the GPU up with 0.2 s of untimed
 calls (after host-side work the clocks have dropped and the first tens of
-milliseconds run several % slower), then runs the warm-up calls; the timed
-calls run back to back between two HIP events on the stream the library
-launches on (torch's current stream); a second pass with events around
-every call gives the per-call spread.
+milliseconds run several % slower), then runs the warm-up calls, the last
+three of them queued after a synchronize and ahead of the start event (so
+that the event does not time the host's issue of the first timed call); the
+timed calls run back to back between two HIP events on the stream the
+library launches on (torch's current stream); a second pass with events
+around every call gives the per-call spread.
 
 Also reported on the same JSON line: the roofline of the dominant kernel,
 a CPU baseline (the CPU oracle timed on this host), and under "secondary"
@@ -100,6 +102,7 @@ def guided_bytes(rows, hidden, guide=True, dequant=False):
 # --------------------------------------------------------------- timing --
 
 SPINUP_S = 0.2  # untimed back-to-back calls before the warm-up
+QUEUED_WARMUP = 3  # warm-up calls queued ahead of the start event (time_calls)
 
 
 def rate(ms, nbytes, elements=None):
@@ -129,19 +132,30 @@ def spin_up(fn, sets, seconds=None):
 
 def time_calls(fn, sets, steps, warmup, per_call=False):
     """Spin up, run `warmup` untimed calls, then time `steps` calls (fn(set)
-    round-robin).  Returns (mean ms per call over the `steps` back-to-back
-    calls bracketed by two HIP events on the current stream, per-call ms
-    from a second pass with events around every call, or None)."""
+    round-robin, continuing the warm-up's rotation).  Returns (mean ms per
+    call over the `steps` back-to-back calls bracketed by two HIP events on
+    the current stream, per-call ms from a second pass with events around
+    every call, or None).
+
+    The last QUEUED_WARMUP warm-up calls are queued after the synchronize,
+    ahead of the start event: the GPU then reaches that event with the first
+    timed call already queued behind it.  Recorded on an idle GPU, the start
+    event would also time the host's latency of issuing the first call
+    (about 6 us, +0.31 us per call over 20 calls)."""
     stream = torch.cuda.current_stream()
     spin_up(fn, sets)
-    for i in range(warmup):
-        fn(sets[i % len(sets)])
+    n = len(sets)
+    queued = min(QUEUED_WARMUP, warmup)
+    for i in range(warmup - queued):
+        fn(sets[i % n])
     torch.cuda.synchronize()
+    for i in range(warmup - queued, warmup):
+        fn(sets[i % n])
     wall0 = torch.cuda.Event(enable_timing=True)
     wall1 = torch.cuda.Event(enable_timing=True)
     wall0.record(stream)
     for i in range(steps):
-        fn(sets[i % len(sets)])
+        fn(sets[(warmup + i) % n])
     wall1.record(stream)
     torch.cuda.synchronize()
     mean = wall0.elapsed_time(wall1) / steps
