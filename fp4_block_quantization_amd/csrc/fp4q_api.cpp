@@ -44,9 +44,13 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_scratch_mutex;
 
-hipError_t scratch_on_current_device(void** out) {
+// The array on the device the call's kernels run on: the stream's device
+// (the current device for the NULL stream), which need not be the calling
+// thread's current device.  The first lookup on a device makes that device
+// current for the hipGetSymbolAddress call and then restores the caller's.
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
   int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
@@ -54,8 +58,14 @@ hipError_t scratch_on_current_device(void** out) {
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
     if (p == nullptr) {
+      int cur = -1;
+      e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
       e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
       if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      if (back != hipSuccess) return back;
       g_scratch_ptr[dev].store(p, std::memory_order_release);
     }
   }
@@ -197,7 +207,7 @@ fp4q_status nvfp4_quantize_global_noalloc(const void* x, int64_t rows, int64_t h
   if (fp4q::global_workspace_bytes(rows, hidden) > (int64_t)sizeof(scratch))
     return FP4Q_ERROR_INVALID_SHAPE;
   void* ws = nullptr;
-  if (scratch_on_current_device(&ws) != hipSuccess) return FP4Q_ERROR_LAUNCH;
+  if (scratch_for_stream((hipStream_t)stream, &ws) != hipSuccess) return FP4Q_ERROR_LAUNCH;
   fp4q::NvQuantArgs a{x,     rows,         hidden,  nullptr, 0,
                       four_over_six, codes, block_scales, nullptr, dequant};
   return launched(fp4q::nvfp4_quantize_global_launch(a, tensor_scale, ws, (hipStream_t)stream));

@@ -171,9 +171,11 @@ FP4Q_API fp4q_status nvfp4_quantize_global(const void* x, int64_t rows, int64_t 
  * hipMalloc).  It allocates nothing: the partial maxima live in a fixed
  * 1 KiB array of the library's own (FP4Q_GLOBAL_WORKSPACE_BYTES), one per
  * device, held until the process ends; its address is looked up once per
- * device on the first call there.  The scratch need does not grow with the
- * tensor (at most 512 partial maxima), so no size within the limits of
- * nvfp4_quantize_global is refused for it.  Every call on a device shares
+ * device on the first call there (the stream's device, or the current
+ * device for the NULL stream; that lookup briefly makes the stream's
+ * device current and then restores the caller's).  The scratch need does
+ * not grow with the tensor (at most 512 partial maxima), so no size within
+ * the limits of nvfp4_quantize_global is refused for it.  Every call on a device shares
  * that device's array: calls that overlap on one device (other streams, or
  * other host threads) race and must not be in flight together.  Arguments,
  * outputs and results are those of nvfp4_quantize_global;

@@ -35,14 +35,14 @@ def ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def noalloc(L, x, fos):
+def noalloc(L, x, fos, stream=None):
     rows, hidden = x.shape
     gu = Guards()
     out = gu.nvfp4(rows, hidden)
     ts = gu.empty((1,), torch.float32)
+    stream = torch.cuda.current_stream() if stream is None else stream
     st = L.nvfp4_quantize_global_noalloc(ptr(x), rows, hidden, fos, ptr(out[0]), ptr(out[1]),
-                                         ptr(ts), ptr(out[3]),
-                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                                         ptr(ts), ptr(out[3]), ctypes.c_void_p(stream.cuda_stream))
     assert st == 0, L.fp4q_status_string(st)
     gu.check("noalloc %dx%d" % (rows, hidden))
     return out[0], out[1], ts, out[3]
@@ -68,6 +68,24 @@ def test_noalloc_equals_the_workspace_call_twice(L, fos):
     # the second tensor's scale is its own maximum's, not the first's
     amax = np.abs((small.astype(np.uint32) << 16).view(np.float32)).max()
     assert host(got[2])[0] == np.float32(amax) / np.float32(1536 if fos else 2688)
+
+
+def test_noalloc_on_a_created_stream(L):
+    # a stream other than the NULL stream: the library finds the array on
+    # the stream's device (a created stream at the default priority)
+    x = to_dev(workloads.rows("moe_act", 0, 256))
+    want = fq.nvfp4_quantize_global(x, 1)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = noalloc(L, x, 1, side)
+    side.synchronize()
+    for g, w, what in zip(got, want, ("codes", "scales", "tensor scale", "dequant")):
+        g, w = (bits_of(g), bits_of(w)) if what == "dequant" else (host(g), host(w))
+        if what == "tensor scale":
+            g, w = g[None, :], w[None, :]
+        assert_same(g, w, "side stream " + what)
 
 
 def test_noalloc_rejects_like_the_workspace_call(L):
