@@ -235,6 +235,14 @@ def standin():
     return fq.declare(ctypes.CDLL(_build.STANDIN_PATH))
 
 
+def exactdecision():
+    """The quantizer built to decide every 4/6 block from both exactly
+    computed errors (no certified margin; same results; measurement only)."""
+    if not os.path.exists(_build.EXACTDECISION_PATH):
+        raise RuntimeError("libfp4q_exactdecision.so is not built: run __graft_entry__.build()")
+    return fq.declare(ctypes.CDLL(_build.EXACTDECISION_PATH))
+
+
 def _ok(status, what):
     if status != 0:
         raise RuntimeError("%s returned status %d" % (what, status))
@@ -254,11 +262,13 @@ def rotating_nvfp4_sets(x, n, dequant=True):
     return sets
 
 
-def standin_nvfp4(S, s, offs=None, fos=1):
+def nvfp4_via(S, s, offs=None, fos=1):
+    """nvfp4_quantize of another build of the library (stand-in or exact
+    decision) on a rotating set (x, outputs)."""
     x, (c, sc, ts, dq) = s
     ng = 0 if offs is None else offs.numel() - 1
     _ok(S.nvfp4_quantize(ptr(x), x.shape[0], x.shape[1], ptr(offs), ng, fos, ptr(c), ptr(sc),
-                         ptr(ts), ptr(dq), stream_ptr()), "stand-in nvfp4_quantize")
+                         ptr(ts), ptr(dq), stream_ptr()), "nvfp4_quantize of a measurement build")
 
 
 # ------------------------------------------------------------ CPU baseline --
@@ -404,6 +414,12 @@ R, H, RG, HG = 8192, 7168, 65536, 2048
 def _label(name, grid):
     """Name one dispatch (kernel name, total work-items) of a bench run."""
     standin = "fp4q_standin" in name
+    if "fp4q_exactdecision" in name:
+        if "nvfp4_quantize_split<1, true, 2, false>" in name and grid == R * 256:
+            return "exact-error decision nvfp4_quantize_split<fos,dq> moe_act 8192x7168"
+        if "nvfp4_quantize_split<1, false, 2, false>" in name and grid == RG * 64:
+            return "exact-error decision nvfp4_quantize_split<fos> ragged_routed 65536x2048"
+        return None
     if "k0_copy<1>" in name:
         return COPY_CAL_KEY
     if "k0_copy<0>" in name:
@@ -451,13 +467,15 @@ def _label(name, grid):
         return "nvfp4_quantize_split<fos> ragged_routed 65536x2048"
     if "nvfp4_quantize_split<2, true, 2, false>" in name and grid == R * 256:
         return "nvfp4_quantize_split<fp16-decision,dq> moe_act 8192x7168"
+    if "nvfp4_quantize_split<2, false, 2, false>" in name and grid == RG * 64:
+        return "nvfp4_quantize_split<fp16-decision> ragged_routed 65536x2048"
     if "global_amax_pass" in name:
         return "nvfp4_quantize_global (amax pass) moe_act 8192x7168"
     if "nvfp4_dequantize" in name:
         return "nvfp4_dequantize moe_act 8192x7168"
-    if "nvfp4_guided_units<false>" in name:
+    if "nvfp4_guided_units<false, false>" in name:
         return "nvfp4_quantize_guided moe_act 8192x7168"
-    if "nvfp4_guided_units<true>" in name:
+    if "nvfp4_guided_units<true, false>" in name:
         return "nvfp4_quantize_guided (no guide: nearest) moe_act 8192x7168"
     if "mxfp4_resq_units<false>" in name:
         return "mxfp4_resq_quantize resq_act 8192x7168"
@@ -493,6 +511,8 @@ def algorithmic_rw():
               (ng * 2 + 65 * 8, nvfp4_bytes(RG, HG, dequant=False) - ng * 2),
           "nvfp4_quantize_split<fp16-decision,dq> moe_act 8192x7168":
               (n * 2, nvfp4_bytes(R, H) - n * 2),
+          "nvfp4_quantize_split<fp16-decision> ragged_routed 65536x2048":
+              (ng * 2 + 65 * 8, nvfp4_bytes(RG, HG, dequant=False) - ng * 2),
           "nvfp4_dequantize moe_act 8192x7168": (n // 2 + n // 16 + R * 4, n * 2),
           "nvfp4_quantize_guided moe_act 8192x7168":
               (n * 2 + n // 2 + n // 16 + R * 4, n // 2),
@@ -510,6 +530,10 @@ def algorithmic_rw():
           "stand-in nvfp4_quantize_split<fos> ragged_routed 65536x2048":
               (ng * 2 + 65 * 8, nvfp4_bytes(RG, HG, dequant=False) - ng * 2),
           "stand-in mxfp4_resq_quantize resq_act 8192x7168": (n * 2, mx_bytes(R, H) - n * 2),
+          "exact-error decision nvfp4_quantize_split<fos,dq> moe_act 8192x7168":
+              (n * 2, nvfp4_bytes(R, H) - n * 2),
+          "exact-error decision nvfp4_quantize_split<fos> ragged_routed 65536x2048":
+              (ng * 2 + 65 * 8, nvfp4_bytes(RG, HG, dequant=False) - ng * 2),
           COPY_CAL_KEY: (mib256, mib256), "K0 copy 256 MiB": (mib256, mib256),
           "K0 copy nt sc1 256 MiB": (mib256, mib256),
           "K0 write nt 256 MiB": (0.0, mib256), "K0 write nt sc1 256 MiB": (0.0, mib256)}
@@ -697,7 +721,7 @@ def size_sweep(x, dev):
         t["nvfp4_quantize"], _ = time_calls(
             lambda s: fq.nvfp4_quantize(s[0], True, out=s[1]), sets, steps, steps // 4)
         t["stand-in nvfp4_quantize"], _ = time_calls(
-            lambda s: standin_nvfp4(S, s), sets, steps, steps // 4)
+            lambda s: nvfp4_via(S, s), sets, steps, steps // 4)
         t["nvfp4_dequantize"], _ = time_calls(
             lambda s: fq.nvfp4_dequantize(s[1][0], s[1][1], s[1][2], out=s[1][3]), sets, steps,
             steps // 4)
@@ -772,8 +796,8 @@ def main():
     ap.add_argument("--secondary-steps", type=int, default=None,
                     help="timed calls of every secondary figure (default: per figure)")
     ap.add_argument("--parts",
-                    default="k0,standin,tiny,dequant,resq,resq_dense,trace,global,ragged,"
-                            "weights,fp16",
+                    default="k0,standin,exact,tiny,dequant,resq,resq_dense,trace,global,"
+                            "ragged,weights,fp16",
                     help="secondary measurements to run (comma list)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--sweep", action="store_true",
@@ -895,7 +919,7 @@ def main():
         S = standin()
         ssets = rotating_nvfp4_sets(x, args.sets)
         name = "stand-in nvfp4_quantize moe_act 8192x7168 (4/6 + dequant pattern)"
-        secondary[name] = measure(lambda s: standin_nvfp4(S, s), ssets, nbytes, n_el,
+        secondary[name] = measure(lambda s: nvfp4_via(S, s), ssets, nbytes, n_el,
                                   steps(1000))
         log(name)
         del ssets
@@ -904,7 +928,7 @@ def main():
         bg = nvfp4_bytes(*xg.shape, dequant=False, groups=offs.numel() - 1)
         gsets = rotating_nvfp4_sets(xg, n_sets(bg), dequant=False)
         name = "stand-in nvfp4_quantize ragged_routed 65536x2048 (no dequant pattern)"
-        secondary[name] = measure(lambda s: standin_nvfp4(S, s, offs), gsets, bg, xg.numel(),
+        secondary[name] = measure(lambda s: nvfp4_via(S, s, offs), gsets, bg, xg.numel(),
                                   steps(500))
         log(name)
         del gsets, xg
@@ -921,6 +945,27 @@ def main():
             msets, bm, xr.numel(), steps(500))
         log(name)
         del msets, xr
+        torch.cuda.empty_cache()
+    if "exact" in parts:
+        # the straightforward FP32 4/6 decision (both errors by the
+        # definition for every block), against which the pages measure
+        # their FP16 shortcut: the headline and the ragged call
+        E = exactdecision()
+        esets = rotating_nvfp4_sets(x, args.sets)
+        name = "exact-error decision nvfp4_quantize moe_act 8192x7168 (4/6 + dequant)"
+        secondary[name] = measure(lambda s: nvfp4_via(E, s), esets, nbytes, n_el,
+                                  steps(1000))
+        log(name)
+        del esets
+        xg = workloads.tensor("ragged_routed", dev)
+        offs = torch.from_numpy(workloads.group_offsets()).to(dev)
+        bg = nvfp4_bytes(*xg.shape, dequant=False, groups=offs.numel() - 1)
+        gsets = rotating_nvfp4_sets(xg, n_sets(bg), dequant=False)
+        name = "exact-error decision nvfp4_quantize ragged_routed 65536x2048 (no dequant)"
+        secondary[name] = measure(lambda s: nvfp4_via(E, s, offs), gsets, bg, xg.numel(),
+                                  steps(500))
+        log(name)
+        del gsets, xg
         torch.cuda.empty_cache()
     if "tiny" in parts:
         # C1, launch-bound by construction (2.4 MB a call): reported, not
@@ -1132,6 +1177,16 @@ def main():
                                   n_el, steps(1000))
         log(name)
         del fsets
+        # and on the VALU-bound routed-token call
+        xg = workloads.tensor("ragged_routed", dev)
+        offs = torch.from_numpy(workloads.group_offsets()).to(dev)
+        b = nvfp4_bytes(*xg.shape, dequant=False, groups=offs.numel() - 1)
+        gsets = rotating_nvfp4_sets(xg, n_sets(b), dequant=False)
+        name = "nvfp4_quantize fp16-decision ragged_routed 65536x2048 (no dequant)"
+        secondary[name] = measure(lambda s: fq.nvfp4_quantize(s[0], 2, offsets=offs, out=s[1]),
+                                  gsets, b, xg.numel(), steps(1000))
+        log(name)
+        del gsets, xg
         torch.cuda.empty_cache()
         agree = {}
         for wname in ("tiny_ref", "moe_act", "expert_weights"):

@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(BUILD_DIR, "libfp4q.so")
 # the same sources with the per-block arithmetic compiled out
 # (-DFP4Q_STANDIN=1): memory-pattern stand-ins, for measurement only
 STANDIN_PATH = os.path.join(BUILD_DIR, "libfp4q_standin.so")
+# the same sources deciding every 4/6 block from both exactly computed errors
+# (-DFP4Q_NV_CERTIFY=0, the straightforward FP32 decision): measurement only
+EXACTDECISION_PATH = os.path.join(BUILD_DIR, "libfp4q_exactdecision.so")
 # K0, the HBM probes (copy, read-only, write-only)
 MEMBENCH_PATH = os.path.join(BUILD_DIR, "libfp4q_membench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -65,8 +68,9 @@ def build(verbose: bool = False, extra_flags=(), out_path: str = None, sources=N
 
 
 def build_all(verbose: bool = False):
-    """libfp4q.so, the stand-in build and the K0 probes."""
+    """libfp4q.so, the stand-in and exact-decision builds and the K0 probes."""
     return [build(verbose), build(verbose, ["-DFP4Q_STANDIN=1"], STANDIN_PATH),
+            build(verbose, ["-DFP4Q_NV_CERTIFY=0"], EXACTDECISION_PATH),
             build(verbose, out_path=MEMBENCH_PATH, sources=MEMBENCH_SOURCES)]
 
 

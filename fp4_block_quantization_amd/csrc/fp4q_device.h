@@ -8,11 +8,14 @@
 // division, so every float operation below is one IEEE binary32 operation.
 #pragma once
 
-// The memory-pattern stand-in build (-DFP4Q_STANDIN=1) puts everything in
-// its own namespace, so that its kernels carry names of their own in
+// The memory-pattern stand-in build (-DFP4Q_STANDIN=1) and the
+// exact-error decision build (-DFP4Q_NV_CERTIFY=0) put everything in a
+// namespace of their own, so that their kernels carry names of their own in
 // profiles and cannot be mistaken for the quantizer's.
 #if defined(FP4Q_STANDIN) && FP4Q_STANDIN && !defined(fp4q)
 #define fp4q fp4q_standin
+#elif defined(FP4Q_NV_CERTIFY) && !FP4Q_NV_CERTIFY && !defined(fp4q)
+#define fp4q fp4q_exactdecision
 #endif
 
 #include <hip/hip_runtime.h>

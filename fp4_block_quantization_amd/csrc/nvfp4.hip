@@ -136,6 +136,13 @@ namespace {
 // 56.8 us, 65536 x 7168 with dequant 318.6 -> 316.2 us, 8192 x 7168 with
 // dequant the same).  0: a packed 16-bit integer maximum of the
 // sign-cleared BF16 words, before unpacking.
+// Build-time knob: FP4Q_NV_CERTIFY = 0 decides every block of the exact
+// 4/6 path from both candidates' errors computed by the definition (the
+// straightforward FP32 decision), never from the certified margin below;
+// the results are the same.  For measurement only (libfp4q_exactdecision.so).
+#ifndef FP4Q_NV_CERTIFY
+#define FP4Q_NV_CERTIFY 1
+#endif
 #ifndef FP4Q_NV_FLOAT_MAX
 #define FP4Q_NV_FLOAT_MAX 1
 #endif
@@ -591,13 +598,13 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
   const float2v t6 = tab[eb & 0xFFu];  // {r, D^2} of the 6 candidate
   uint32_t code[2];
   float A6;
-  encode_candidate<FOS == 1>(x, t6.x, code, A6);
+  encode_candidate<FOS == 1 && FP4Q_NV_CERTIFY>(x, t6.x, code, A6);
   uint32_t ebyte = eb & 0xFFu;
   if (FOS) {
     const float2v t4 = tab[eb >> 8];
     uint32_t code4[2];
     float A4;
-    encode_candidate<FOS == 1>(x, t4.x, code4, A4);
+    encode_candidate<FOS == 1 && FP4Q_NV_CERTIFY>(x, t4.x, code4, A4);
     bool four;
     if (FOS == 2) {
       half2v y[8];
@@ -616,7 +623,7 @@ __device__ __forceinline__ void quantize_block_fast(const float (&x)[16], uint32
       // both e nonzero: the 4 candidate's byte is never below the 6
       // candidate's (both round b / (k s) to nearest, monotonically, and
       // b / (6 s) < b / (4 s)), so a nonzero 6 byte is enough
-      if (rs.certify && (eb & 0xFFu) != 0u)
+      if (FP4Q_NV_CERTIFY && rs.certify && (eb & 0xFFu) != 0u)
         decided = certified_four(A6, t6.y, A4, t4.y, four);
       if (__builtin_expect(!decided, 0))
         four = exact_error(x, code4, e4m3_value<1>(eb), rs.s, neg_zero) <

@@ -43,10 +43,12 @@ def test_library_exports_every_declared_call():
     L = fq.lib()
     for n in names:
         assert hasattr(L, n), n
-    # the stand-in build of the same sources exports the same calls
-    S = ctypes.CDLL(_build.STANDIN_PATH)
-    for n in names:
-        assert hasattr(S, n), n
+    # the stand-in and exact-decision builds of the same sources export the
+    # same calls
+    for path in (_build.STANDIN_PATH, _build.EXACTDECISION_PATH):
+        S = ctypes.CDLL(path)
+        for n in names:
+            assert hasattr(S, n), (path, n)
 
 
 def test_membench_library_exports_and_rejects():

@@ -97,9 +97,23 @@ def test_dispatch_labels():
     assert lab("(anonymous namespace)::k0_copy_stream<1>(x)", 1) is None
     assert lab("void (anonymous namespace)::k0_mix<4, 1>(x)", 1) == \
         "K0 mix read 4 KiB, write 4/4 KiB nt 256 MiB"
+    # the exact-decision build, the FP16 decision on routed tokens, and the
+    # guided kernels (two template arguments: nearest or guided, dequant)
+    ex = q.replace("fp4q::", "fp4q_exactdecision::")
+    assert lab(ex % "1, true, 2, false", 8192 * 256).startswith("exact-error decision")
+    assert lab(ex % "1, false, 2, false", 65536 * 64).startswith("exact-error decision")
+    assert lab(q % "2, false, 2, false", 65536 * 64) == \
+        "nvfp4_quantize_split<fp16-decision> ragged_routed 65536x2048"
+    g = "fp4q::(anonymous namespace)::nvfp4_guided_units<%s>(HIP_vector_type<unsigned int, 4u> const*)"
+    assert lab(g % "false, false", 1) == "nvfp4_quantize_guided moe_act 8192x7168"
+    assert lab(g % "true, false", 1) == "nvfp4_quantize_guided (no guide: nearest) moe_act 8192x7168"
     # every labelled kernel has algorithmic bytes
     algo = bench.algorithmic_rw()
     assert bench.HEADLINE_KEY in algo and bench.COPY_CAL_KEY in algo
+    for name in (ex % "1, true, 2, false", q % "2, false, 2, false", g % "false, false",
+                 g % "true, false"):
+        key = lab(name, 8192 * 256 if "true, 2" in name else 65536 * 64)
+        assert key in algo, key
 
 
 def test_host_cpu_description():

@@ -25,7 +25,7 @@ KNOBS = {
                   "FP4Q_GLOBAL_REVERSE=0", "FP4Q_GLOBAL_LOAD_AUX=0", "FP4Q_GAMAX_THREADS=1024",
                   "FP4Q_GAMAX_CHUNKED=0", "FP4Q_NV_FLOAT_MAX=0", "FP4Q_NV_SCALE_NT_POLICY=16",
                   "FP4Q_NV_SCALE_PLAIN_POLICY=16", "FP4Q_GUIDED_CODE_POLICY=16",
-                  "FP4Q_RTN_CODE_POLICY=2"],
+                  "FP4Q_RTN_CODE_POLICY=2", "FP4Q_NV_CERTIFY=0"],
     "mxfp4_resq.hip": ["FP4Q_MX_LDS_STAGE=0", "FP4Q_MX_NT_LOADS=0", "FP4Q_MX_NT_STORES=0",
                        "FP4Q_MX_NT_SMALL=1", "FP4Q_MX_UNITS=1", "FP4Q_MX_UNITS=2",
                        "FP4Q_MX_UNITS=8", "FP4Q_MX_REC_STAGE=0", "FP4Q_MX_REC_NT=0",
