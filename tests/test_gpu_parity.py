@@ -265,6 +265,42 @@ def test_ragged_subrange_leaves_other_rows(H, rows, cut):
         assert (g[:lo] == f).all() and (g[hi:] == f).all(), n
 
 
+@pytest.mark.parametrize("H,rows,offs", [
+    (2048, 100, (-5, 50, 200)),                 # below 0 and past the end: all rows
+    (7168, 40, (30, 10)),                       # decreasing: no row
+    (7168, 40, (12, 25, 1 << 40)),              # far past the end: rows 12..39
+    (32784, 6, (-(1 << 40), 3, 4)),             # the long-row kernel, from far below 0
+])
+def test_ragged_offsets_outside_the_tensor_are_clamped(H, rows, offs):
+    # offsets are not checked on the host; the kernels clamp the range to
+    # [0, rows): the rows inside it are quantized, the others keep their
+    # contents, and nothing is written outside the outputs
+    if H % 2048 == 0:
+        x_bits = np.ascontiguousarray(
+            np.tile(workloads.rows("ragged_routed", 0, rows), (1, H // 2048)))
+    else:
+        e = edge_rows(H, seed=rows)
+        x_bits = np.ascontiguousarray(np.tile(e, (-(-rows // len(e)), 1))[:rows])
+    R = x_bits.shape[0]
+    assert R == rows
+    x = to_dev(x_bits)
+    gu = Guards()
+    out = sentinel_outputs(gu, R, H)
+    fq.nvfp4_quantize(x, True, offsets=torch.tensor(offs, dtype=torch.int64, device="cuda"),
+                      out=out)
+    gu.check("clamped offsets %s" % (offs,))
+    lo, hi = max(offs[0], 0), min(offs[-1], R)
+    got = [host(out[0]), host(out[1]), host(out[2])[:, None], bits_of(out[3])]
+    fills = (0xAB, 0xCD, np.float32(-7.0), 0x3FC0)
+    if hi > lo:
+        want = oracle_nvfp4(x_bits[lo:hi], True)
+        for g, w, n in zip(got, want, ("codes", "scales", "ts", "dq")):
+            w = w if w.ndim > 1 else w[:, None]
+            assert_same(g[lo:hi], w, "clamped %s %s" % (offs, n))
+    for g, f, n in zip(got, fills, ("codes", "scales", "ts", "dq")):
+        assert (g[:lo] == f).all() and (g[max(hi, lo):] == f).all(), n
+
+
 def test_resq_act_full_size():
     check_mx(workloads.rows("resq_act"), label="resq_act")
 
