@@ -10,9 +10,11 @@
  *                       (Rollout-ResQ)
  *
  * Conventions shared by every call
- *   - Every data pointer is a DEVICE pointer on the current HIP device.  The
+ *   - Every data pointer is a DEVICE pointer on the device the call's
+ *     stream belongs to (the current HIP device for the NULL stream).  The
  *     caller allocates and frees all memory; the library allocates nothing
- *     and keeps no state between calls.
+ *     and keeps no state between calls, apart from the fixed per-device
+ *     scratch array of nvfp4_quantize_global_noalloc (below).
  *   - Tensors are row-major and contiguous: [rows, hidden], hidden innermost.
  *     BF16 is passed as 16-bit patterns (void*).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
