@@ -407,6 +407,8 @@ def traffic_record(kernel_key):
 
 # Kernels of the bench run, named by what each dispatch computes.
 HEADLINE_KEY = "nvfp4_quantize_split<fos,dq> moe_act 8192x7168"
+DQ_KEY = "nvfp4_dequantize moe_act 8192x7168"
+DQ_PACKED_KEY = "nvfp4_dequantize moe_act 8192x7168 (one allocation per kind)"
 COPY_CAL_KEY = "K0 copy nt 256 MiB (counter calibration)"
 R, H, RG, HG = 8192, 7168, 65536, 2048
 
@@ -472,7 +474,7 @@ def _label(name, grid):
     if "global_amax_pass" in name:
         return "nvfp4_quantize_global (amax pass) moe_act 8192x7168"
     if "nvfp4_dequantize" in name:
-        return "nvfp4_dequantize moe_act 8192x7168"
+        return DQ_KEY
     if "nvfp4_guided_units<false, false>" in name:
         return "nvfp4_quantize_guided moe_act 8192x7168"
     if "nvfp4_guided_units<true, false>" in name:
@@ -513,7 +515,8 @@ def algorithmic_rw():
               (n * 2, nvfp4_bytes(R, H) - n * 2),
           "nvfp4_quantize_split<fp16-decision> ragged_routed 65536x2048":
               (ng * 2 + 65 * 8, nvfp4_bytes(RG, HG, dequant=False) - ng * 2),
-          "nvfp4_dequantize moe_act 8192x7168": (n // 2 + n // 16 + R * 4, n * 2),
+          DQ_KEY: (n // 2 + n // 16 + R * 4, n * 2),
+          DQ_PACKED_KEY: (n // 2 + n // 16 + R * 4, n * 2),
           "nvfp4_quantize_guided moe_act 8192x7168":
               (n * 2 + n // 2 + n // 16 + R * 4, n // 2),
           "nvfp4_quantize_guided (no guide: nearest) moe_act 8192x7168":
@@ -564,7 +567,16 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
     for r, lab in zip(rows, labels):
         if lab:
             dur.setdefault(lab, []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    # the dequant is timed over two layouts of the same sets, one after the
+    # other: its dispatches split at the longest pause between them
+    if len(dur.get(DQ_KEY, ())) > 1:
+        d = sorted(dur[DQ_KEY])
+        gaps = [b[0] - a[0] for a, b in zip(d, d[1:])]
+        k = int(np.argmax(gaps))
+        if gaps[k] > 500_000:  # ns: the second layout's set-up, not a gap between calls
+            dur[DQ_KEY], dur[DQ_PACKED_KEY] = d[:k + 1], d[k + 1:]
+    dur = {lab: [t for _, t in v] for lab, v in dur.items()}
     stats = glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0]
     srows = list(csv.DictReader(open(stats)))
     algo = algorithmic_rw()
@@ -985,12 +997,26 @@ def main():
         # and outputs per set
         c, s_, ts, _ = fq.nvfp4_quantize(x, True, dequant=False)
         b = dequant_bytes(rows, hidden)
-        dsets = [(c.clone(), s_.clone(), ts.clone(), torch.empty_like(x)) for _ in range(n_sets(b))]
+        nd = n_sets(b)
+        dsets = [(c.clone(), s_.clone(), ts.clone(), torch.empty_like(x)) for _ in range(nd)]
         name = "nvfp4_dequantize moe_act 8192x7168"
         secondary[name] = measure(lambda d: fq.nvfp4_dequantize(d[0], d[1], d[2], out=d[3]),
                                   dsets, b, n_el, steps(400))
+        del dsets
+        torch.cuda.empty_cache()
+        # the same sets with each kind held in one allocation (every set's
+        # codes together, and so on): the same bytes and rotation, but this
+        # call's time depends on where its inputs lie (the other calls'
+        # do not), so both figures are reported
+        C = c.repeat(nd, 1).view(nd, rows, hidden // 2)
+        S = s_.repeat(nd, 1).view(nd, rows, hidden // 16)
+        T = ts.repeat(nd).view(nd, rows)
+        D = torch.empty((nd, rows, hidden), dtype=torch.bfloat16, device=dev)
+        psets = [(C[i], S[i], T[i], D[i]) for i in range(nd)]
+        secondary[name]["one_allocation_per_kind"] = measure(
+            lambda d: fq.nvfp4_dequantize(d[0], d[1], d[2], out=d[3]), psets, b, n_el, steps(400))
         log(name)
-        del dsets, c, s_, ts
+        del psets, C, S, T, D, c, s_, ts
         torch.cuda.empty_cache()
     if "resq" in parts or "resq_dense" in parts:
         xr = workloads.tensor("resq_act", dev)

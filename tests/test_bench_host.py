@@ -122,3 +122,44 @@ def test_host_cpu_description():
     assert isinstance(d["cpu_model"], str)
     assert d["cpuid"] is None or d["cpuid"].startswith("family ")
     assert isinstance(d["vector_extensions"], list)
+
+
+def test_profile_summary_splits_the_dequant_layouts(tmp_path):
+    # a synthetic rocprofv3 output: the copy that calibrates the counters,
+    # then two bursts of dequant dispatches a pause apart (the bench's two
+    # layouts of the same sets); the summary keeps them as two rows
+    import csv
+
+    def write_csv(path, header, rows):
+        path.parent.mkdir(parents=True, exist_ok=True)
+        with open(path, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(header)
+            w.writerows(rows)
+
+    dq = "fp4q::(anonymous namespace)::nvfp4_dequantize_rows(unsigned int const*)"
+    copy = "void (anonymous namespace)::k0_copy<1>(x)"
+    disp = [(copy, 1, 0, 80_000)]
+    t = 1_000_000
+    for i in range(5):                      # separate allocations: 25 us each
+        disp.append((dq, 1, t, t + 25_000)); t += 30_000
+    t += 5_000_000                          # the second layout's set-up
+    for i in range(5):                      # one allocation per kind: 22 us
+        disp.append((dq, 1, t, t + 22_000)); t += 30_000
+    trace = [(k, g, d, a, b) for d, (k, g, a, b) in enumerate(disp)]
+    write_csv(tmp_path / "tr" / "run_kernel_trace.csv",
+              ["Kernel_Name", "Grid_Size", "Dispatch_Id", "Start_Timestamp", "End_Timestamp"], trace)
+    write_csv(tmp_path / "tr" / "run_kernel_stats.csv",
+              ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"], [(dq, 10, 1, 1, 1)])
+    for cname, val in (("FETCH_SIZE", 131072.0), ("WRITE_SIZE", 262144.0)):
+        rows = [(k, g, d, cname, val) for d, (k, g, a, b) in enumerate(disp)]
+        write_csv(tmp_path / cname / "run_counter_collection.csv",
+                  ["Kernel_Name", "Grid_Size", "Dispatch_Id", "Counter_Name", "Counter_Value"], rows)
+    out = tmp_path / "out"
+    bench.summarize_profiles(str(tmp_path / "tr"), str(tmp_path / "FETCH_SIZE"),
+                             str(tmp_path / "WRITE_SIZE"), str(out))
+    text = (out / "kernel_trace_bench_default.md").read_text()
+    row = {ln.split("|")[1].strip(): ln.split("|")[2:4] for ln in text.splitlines()
+           if ln.startswith("| nvfp4_dequantize")}
+    assert row[bench.DQ_KEY][0].strip() == "5" and row[bench.DQ_KEY][1].strip() == "25.00"
+    assert row[bench.DQ_PACKED_KEY][0].strip() == "5" and row[bench.DQ_PACKED_KEY][1].strip() == "22.00"
