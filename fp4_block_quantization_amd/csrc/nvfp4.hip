@@ -129,13 +129,6 @@ namespace {
 #ifndef FP4Q_NV_NB
 #define FP4Q_NV_NB 2
 #endif
-// Build-time knob: how the split kernel takes its block maxima.  1:
-// three-input maxima of the magnitudes of the unpacked FP32 values, which
-// the quantization then reuses (8 fewer VALU instructions per block, 16
-// more live registers; 65536 x 2048 routed rows without dequant 60.4 ->
-// 56.8 us, 65536 x 7168 with dequant 318.6 -> 316.2 us, 8192 x 7168 with
-// dequant the same).  0: a packed 16-bit integer maximum of the
-// sign-cleared BF16 words, before unpacking.
 // Build-time knob: FP4Q_NV_CERTIFY = 0 decides every block of the exact
 // 4/6 path from both candidates' errors computed by the definition (the
 // straightforward FP32 decision), never from the certified margin below;
@@ -143,6 +136,13 @@ namespace {
 #ifndef FP4Q_NV_CERTIFY
 #define FP4Q_NV_CERTIFY 1
 #endif
+// Build-time knob: how the split kernel takes its block maxima.  1:
+// three-input maxima of the magnitudes of the unpacked FP32 values, which
+// the quantization then reuses (8 fewer VALU instructions per block, 16
+// more live registers; 65536 x 2048 routed rows without dequant 60.4 ->
+// 56.8 us, 65536 x 7168 with dequant 318.6 -> 316.2 us, 8192 x 7168 with
+// dequant the same).  0: a packed 16-bit integer maximum of the
+// sign-cleared BF16 words, before unpacking.
 #ifndef FP4Q_NV_FLOAT_MAX
 #define FP4Q_NV_FLOAT_MAX 1
 #endif
